@@ -1,0 +1,384 @@
+"""Plain FP64 CPU oracle for the Muse Spark Open text-decoder attention core.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, tables or
+helpers with the HIP library and does not import it.
+
+What it computes is defined by the NeMo AutoModel API reference pages for the
+``muse_spark`` model package.  Citations name a page and the section on it:
+
+* "layers page" -- ``nemo_automodel.components.models.muse_spark.layers``
+  (sections ``MuseSparkAttention``, ``MuseSparkRMSNorm``,
+  ``MuseSparkRotaryEmbedding``, ``_rms_norm_core``, ``_qk_norm_rope_core``,
+  ``apply_rotary_embedding``, ``_repeat_kv``, ``_output_norm_gate_core``);
+* "model page" -- ``nemo_automodel.components.models.muse_spark.model``
+  (section ``_causal_mask``);
+* "adapter page" -- ``nemo_automodel.components.models.muse_spark.hf_state_dict_adapter``
+  (section ``_permute_rope_rows``).
+
+The method is a composition of exact definitions (no approximation, heuristic
+or iteration), so every function below is that definition written out in
+float64, with each dtype boundary the pages name emulated by an explicit
+round-to-nearest-even.  Flash-style blocking reaches the plain softmax result
+up to rounding order, so attention here is the plain masked softmax.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+RMS over the last dim per (token, head); eps inside the square root; effective
+gain ``f32(gain_center + g)`` applied after normalisation and before the cast;
+RoFormer rotation sign with frequencies ``theta**(-2i/D)``; cos/sin of width
+D/2; window ``W`` = number of visible causal keys including the query itself;
+no attention across packed segments; bf16 boundary on the attention output;
+sigmoid and output norm in full precision with one final cast.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
+forms, library routines or brute force; none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "round_bf16",
+    "round_f32",
+    "rope_inv_freq",
+    "rope_cos_sin",
+    "rms_normalize",
+    "rms_norm",
+    "rope_rotate",
+    "qk_norm_rope",
+    "visible_mask",
+    "attention",
+    "attention_rows",
+    "out_norm_gate",
+    "Segments",
+    "attn_core",
+    "attn_core_rows",
+]
+
+
+# --------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 values of bfloat16 bit patterns (uint16)."""
+    u32 = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to bfloat16, ties to even, in one step.
+
+    bfloat16 keeps 8 significant bits and the binary32 exponent range; below
+    2**-126 the quantum is fixed at 2**-133 (subnormals).  The rounding is done
+    directly from float64 so no double rounding through binary32 occurs.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    fin = np.isfinite(x)
+    xf = x[fin]
+    _, e = np.frexp(xf)                       # xf = m * 2**e, 0.5 <= |m| < 1
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(xf / q) * q                   # np.rint rounds half to even
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, xf), r)
+    out[fin] = r
+    return out
+
+
+def round_f32(x) -> np.ndarray:
+    """Round float64 values to binary32 (numpy's cast rounds to nearest even)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Rotary table -- layers page, MuseSparkRotaryEmbedding ("FP32 adjacent-pair
+# rotary frequencies shared by all text layers"; forward returns cosine/sine
+# shaped [batch, sequence, head_dim / 2]).
+# --------------------------------------------------------------------------
+
+def rope_inv_freq(theta: float, head_dim: int) -> np.ndarray:
+    """FP32 inverse frequencies inv_i = theta**(-2i/D), i < D/2, rounded once."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return round_f32(np.power(np.float64(theta), -2.0 * i / head_dim))
+
+
+def rope_cos_sin(theta: float, head_dim: int, positions) -> tuple[np.ndarray, np.ndarray]:
+    """cos/sin [len(positions), D/2]: FP32 angle p*inv_i, then FP32 cos and sin.
+
+    The angle is the binary32 product of the (exact) position and the FP32
+    frequency; its cosine and sine are evaluated in float64 and rounded once.
+    """
+    p = np.asarray(positions, dtype=np.float64).reshape(-1, 1)
+    ang = round_f32(p * rope_inv_freq(theta, head_dim)[None, :])
+    return round_f32(np.cos(ang)), round_f32(np.sin(ang))
+
+
+# --------------------------------------------------------------------------
+# RMSNorm -- layers page, MuseSparkRMSNorm / effective_weight / _rms_norm_core
+# ("Normalize in FP32, then apply the effective gain before the output cast";
+# eps is "added to the mean squared activation").
+# --------------------------------------------------------------------------
+
+def rms_normalize(x: np.ndarray, eps: float) -> tuple[np.ndarray, np.ndarray]:
+    """Unrounded x / sqrt(mean(x**2) + eps) over the last dim, and that rstd."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(ms + float(round_f32(eps)))
+    return x * rstd, rstd[..., 0]
+
+
+def rms_norm(x: np.ndarray, eps: float, gain=None, gain_center: float = 1.0):
+    """bf16(normalize(x) * w) with w = f32(gain_center + g); no gain when None.
+
+    Returns (bf16-valued float64 array, rstd float64 [...]).
+    """
+    y, rstd = rms_normalize(x, eps)
+    if gain is not None:
+        w = round_f32(np.float64(round_f32(gain_center)) + np.asarray(gain, dtype=np.float64))
+        y = y * w
+    return round_bf16(y), rstd
+
+
+# --------------------------------------------------------------------------
+# RoPE rotation -- layers page, apply_rotary_embedding ("adjacent-pair";
+# the original checkpoint computes the rotation in FP32, upcast=True).
+# --------------------------------------------------------------------------
+
+def rope_rotate(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate each adjacent pair (x_{2i}, x_{2i+1}) by its angle; one bf16 cast.
+
+    ``cos``/``sin`` broadcast against x[..., 0::2].  The rotation is
+    (x0*C - x1*S, x0*S + x1*C), RoFormer's 2-D rotation block.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = round_bf16(x0 * cos - x1 * sin)
+    y[..., 1::2] = round_bf16(x0 * sin + x1 * cos)
+    return y
+
+
+# --------------------------------------------------------------------------
+# Sequences: BSHD rows or packed THD segments (layers page, MuseSparkAttention
+# .forward: cu_seqlens [documents + 1]; model page, position_ids are local).
+# --------------------------------------------------------------------------
+
+class Segments:
+    """Token ranges [start, start+len) that attend only within themselves."""
+
+    def __init__(self, starts, lengths):
+        self.starts = [int(s) for s in starts]
+        self.lengths = [int(n) for n in lengths]
+
+    @classmethod
+    def bshd(cls, batch: int, seqlen: int) -> "Segments":
+        return cls([b * seqlen for b in range(batch)], [seqlen] * batch)
+
+    @classmethod
+    def thd(cls, cu_seqlens) -> "Segments":
+        cu = [int(c) for c in cu_seqlens]
+        return cls(cu[:-1], [cu[i + 1] - cu[i] for i in range(len(cu) - 1)])
+
+    @property
+    def total(self) -> int:
+        return sum(self.lengths)
+
+    def local_positions(self) -> np.ndarray:
+        """Position of each token inside its own sequence/segment (restarting at 0)."""
+        end = max((s + n for s, n in zip(self.starts, self.lengths)), default=0)
+        pos = np.zeros(end, dtype=np.int64)
+        for s, n in zip(self.starts, self.lengths):
+            pos[s:s + n] = np.arange(n)
+        return pos
+
+    def locate(self, token: int) -> tuple[int, int]:
+        """(segment start, segment length) of the segment holding ``token``."""
+        for s, n in zip(self.starts, self.lengths):
+            if s <= token < s + n:
+                return s, n
+        raise IndexError(token)
+
+
+# --------------------------------------------------------------------------
+# Q/K norm + query scale + RoPE -- layers page, _qk_norm_rope_core
+# ("Multiplier applied after the normalized query's dtype cast").
+# --------------------------------------------------------------------------
+
+def qk_norm_rope(q, k, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
+                 query_scale=1.0, use_rope=True, cos=None, sin=None):
+    """Q [N,Hq,D], K [N,Hkv,D] -> (q_hat, k_hat, q_rstd [N,Hq], k_rstd [N,Hkv]).
+
+    ``cos``/``sin`` are the per-token rows [N, D/2] (already indexed by each
+    token's position); they are ignored when ``use_rope`` is false.
+    """
+    q1, q_rstd = rms_norm(q, eps, q_gain, gain_center)
+    k1, k_rstd = rms_norm(k, eps, k_gain, gain_center)
+    q1 = round_bf16(q1 * np.float64(round_f32(query_scale)))
+    if use_rope:
+        c = np.asarray(cos, dtype=np.float64)[:, None, :]
+        s = np.asarray(sin, dtype=np.float64)[:, None, :]
+        q1 = rope_rotate(q1, c, s)
+        k1 = rope_rotate(k1, c, s)
+    return q1, k1, q_rstd, k_rstd
+
+
+# --------------------------------------------------------------------------
+# Attention -- layers page, MuseSparkAttention (scaling = head_dim**-0.5,
+# num_key_value_groups = num_heads // num_key_value_heads), _repeat_kv
+# (KV heads repeated to the query-head count); model page, _causal_mask
+# (window = number of causal key positions visible to each query).
+# --------------------------------------------------------------------------
+
+def visible_mask(qpos: np.ndarray, kpos: np.ndarray, window: int) -> np.ndarray:
+    """Key j visible to query i iff j <= i and, with a window W > 0, j > i - W."""
+    i = np.asarray(qpos)[:, None]
+    j = np.asarray(kpos)[None, :]
+    vis = j <= i
+    if window and window > 0:
+        vis &= j > i - window
+    return vis
+
+
+def _attend_block(qb, kseg, vseg, qpos, window, scaling):
+    """Softmax attention of query rows qb [m,D] over one segment's keys [L,D]."""
+    s = float(scaling) * (qb @ kseg.T)
+    vis = visible_mask(qpos, np.arange(kseg.shape[0]), window)
+    s = np.where(vis, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    e = np.exp(s - mx)
+    z = e.sum(axis=1, keepdims=True)
+    o = (e @ vseg) / z
+    return o, mx[:, 0] + np.log(z[:, 0])
+
+
+def attention(q_hat, k_hat, v, segments: Segments, *, window=0, scaling, row_block=2048):
+    """Exact causal GQA softmax attention.  Returns (bf16(o) [N,Hq,D], lse [N,Hq]).
+
+    Query head h reads key/value head h // (Hq // Hkv).  lse uses the natural
+    log.  Rows outside every segment are left at zero.
+    """
+    q_hat = np.asarray(q_hat, dtype=np.float64)
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, hq, d = q_hat.shape
+    hkv = k_hat.shape[1]
+    groups = hq // hkv
+    o = np.zeros_like(q_hat)
+    lse = np.zeros((n, hq))
+    for s0, length in zip(segments.starts, segments.lengths):
+        for h in range(hq):
+            g = h // groups
+            kseg = k_hat[s0:s0 + length, g]
+            vseg = v[s0:s0 + length, g]
+            for r0 in range(0, length, row_block):
+                r1 = min(length, r0 + row_block)
+                ob, lb = _attend_block(q_hat[s0 + r0:s0 + r1, h], kseg, vseg,
+                                       np.arange(r0, r1), window, scaling)
+                o[s0 + r0:s0 + r1, h] = ob
+                lse[s0 + r0:s0 + r1, h] = lb
+    return round_bf16(o), lse
+
+
+def attention_rows(q_hat_rows, k_hat, v, segments: Segments, rows, *, num_heads, window=0, scaling):
+    """Attention for selected (token, head) rows only.
+
+    ``q_hat_rows`` [len(rows), D] holds the normalised/rotated query of each
+    selected row.  Returns (bf16(o) [len(rows), D], lse [len(rows)]).
+    """
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    groups = num_heads // k_hat.shape[1]
+    o = np.zeros((len(rows), k_hat.shape[2]))
+    lse = np.zeros(len(rows))
+    for r, (t, h) in enumerate(rows):
+        s0, length = segments.locate(int(t))
+        g = int(h) // groups
+        ob, lb = _attend_block(np.asarray(q_hat_rows[r], dtype=np.float64)[None, :],
+                               k_hat[s0:s0 + length, g], v[s0:s0 + length, g],
+                               np.array([int(t) - s0]), window, scaling)
+        o[r] = ob[0]
+        lse[r] = lb[0]
+    return round_bf16(o), lse
+
+
+# --------------------------------------------------------------------------
+# Output norm and gate -- layers page, _output_norm_gate_core (parameter-free
+# output RMSNorm, sigmoid gate with the output's shape, gated output in the
+# original dtype).
+# --------------------------------------------------------------------------
+
+def out_norm_gate(o, gate, eps):
+    """bf16(rmsnorm(o) * sigmoid(gate)), both in full precision; returns (out, rstd)."""
+    y, rstd = rms_normalize(o, eps)
+    g = np.asarray(gate, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    return round_bf16(y * sig), rstd
+
+
+# --------------------------------------------------------------------------
+# The whole core -- layers page, MuseSparkAttention.forward: Q/K norm + RoPE
+# (_qk_norm_rope_core), attention, then _output_norm_gate_core, ending in the
+# tensor fed to o_proj.
+# --------------------------------------------------------------------------
+
+def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling,
+              window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
+              query_scale=1.0, position_ids=None):
+    """Full forward over every row.  Inputs are float64 arrays of bf16 values.
+
+    Returns a dict with q_hat, k_hat, q_rstd, k_rstd, o (bf16 values), lse,
+    o_rstd and out (bf16 values [N,Hq,D]).
+    """
+    d = q.shape[-1]
+    pos = segments.local_positions() if position_ids is None else np.asarray(position_ids)
+    cos, sin = rope_cos_sin(theta, d, pos) if use_rope else (None, None)
+    q_hat, k_hat, q_rstd, k_rstd = qk_norm_rope(
+        q, k, eps=eps, q_gain=q_gain, k_gain=k_gain, gain_center=gain_center,
+        query_scale=query_scale, use_rope=use_rope, cos=cos, sin=sin)
+    o, lse = attention(q_hat, k_hat, v, segments, window=window, scaling=scaling)
+    out, o_rstd = out_norm_gate(o, gate, out_eps)
+    return dict(q_hat=q_hat, k_hat=k_hat, q_rstd=q_rstd, k_rstd=k_rstd, o=o, lse=lse,
+                o_rstd=o_rstd, out=out)
+
+
+def attn_core_rows(q, k, v, gate, segments: Segments, rows, *, theta, eps, out_eps, scaling,
+                   window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
+                   query_scale=1.0, position_ids=None):
+    """The full forward for selected (token, head) rows only (K/V are used whole).
+
+    Returns a dict with q_hat [R,D], k_hat [N,Hkv,D], o [R,D], lse [R],
+    o_rstd [R] and out [R,D] for the R selected rows.
+    """
+    rows = [(int(t), int(h)) for t, h in rows]
+    d = q.shape[-1]
+    pos = segments.local_positions() if position_ids is None else np.asarray(position_ids)
+    tok = np.array([t for t, _ in rows], dtype=np.int64)
+    head = np.array([h for _, h in rows], dtype=np.int64)
+    q_sel = np.asarray(q, dtype=np.float64)[tok, head][:, None, :]       # [R,1,D]
+    if use_rope:
+        kc, ks = rope_cos_sin(theta, d, pos)
+        qc, qs = kc[tok], ks[tok]
+    else:
+        kc = ks = qc = qs = None
+    q_hat = _q_rows(q_sel, eps, q_gain, gain_center, query_scale, use_rope, qc, qs)
+    k1, _ = rms_norm(k, eps, k_gain, gain_center)
+    k_hat = rope_rotate(k1, kc[:, None, :], ks[:, None, :]) if use_rope else k1
+    num_heads = q.shape[1]
+    o, lse = attention_rows(q_hat, k_hat, v, segments, rows, num_heads=num_heads,
+                            window=window, scaling=scaling)
+    g_sel = np.asarray(gate, dtype=np.float64)[tok, head]
+    out, o_rstd = out_norm_gate(o, g_sel, out_eps)
+    return dict(q_hat=q_hat, k_hat=k_hat, o=o, lse=lse, o_rstd=o_rstd, out=out)
+
+
+def _q_rows(q_sel, eps, q_gain, gain_center, query_scale, use_rope, cos, sin):
+    q1, _ = rms_norm(q_sel[:, 0, :], eps, q_gain, gain_center)
+    q1 = round_bf16(q1 * np.float64(round_f32(query_scale)))
+    if use_rope:
+        q1 = rope_rotate(q1, cos, sin)
+    return q1

@@ -1,0 +1,459 @@
+"""Pins of the FP64 oracle against things other than itself.
+
+Each test ties one oracle function to a closed form, a library routine, a
+hand-derived fixture under tests/golden/, or brute force on tiny inputs, so
+that a plausible slip (a dropped term, a wrong sign or index, a transposed
+operand, an off-by-one window) fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- bf16 / f32
+
+def _golden_bf16_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "bf16_rounding.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b = line.split("|")
+            cases.append((eval(a), eval(b)))  # fixture is trusted, repo-owned arithmetic text
+    return cases
+
+
+@pytest.mark.parametrize("x,expected", _golden_bf16_cases())
+def test_round_bf16_hand_cases(x, expected):
+    got = float(O.round_bf16(np.array([x]))[0])
+    assert got == expected or (math.isinf(expected) and got == expected)
+    assert math.copysign(1.0, got) == math.copysign(1.0, expected)
+
+
+def test_round_bf16_matches_torch_cast_on_fp32_inputs():
+    rng = np.random.default_rng(1)
+    mant = rng.standard_normal(200_000).astype(np.float32)
+    expo = rng.integers(-140, 128, 200_000)
+    x = np.ldexp(mant.astype(np.float64), expo).astype(np.float32)   # includes subnormals, inf
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45, 3.4e38, -3.4e38],
+                        dtype=np.float32)
+    x = np.concatenate([x, specials])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_bits_decode():
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0xFF80, 0x0001, 0x0000, 0x8000, 0x3DCD], dtype=np.uint16)
+    got = O.bf16_bits_to_f64(bits)
+    exp = [1.0, -2.0, np.inf, -np.inf, 2.0 ** -133, 0.0, -0.0, 0.10009765625]
+    np.testing.assert_array_equal(got, exp)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got, t)
+
+
+def test_round_f32_ties_to_even():
+    assert O.round_f32(1.0 + 2.0 ** -24) == 1.0
+    assert O.round_f32(1.0 + 2.0 ** -24 + 2.0 ** -50) == 1.0 + 2.0 ** -23
+    assert O.round_f32(1.0 + 3 * 2.0 ** -24) == 1.0 + 2.0 ** -22
+
+
+# ---------------------------------------------------------------- RoPE table
+
+@pytest.mark.parametrize("theta,d", [(1.0e4, 64), (5.0e5, 128), (1.0e4, 128)])
+def test_inv_freq_closed_forms(theta, d):
+    inv = O.rope_inv_freq(theta, d)
+    assert inv.shape == (d // 2,)
+    assert inv[0] == 1.0                                   # theta**0
+    # i = D/4 gives theta**(-1/2) exactly in real arithmetic
+    assert inv[d // 4] == np.float32(1.0 / math.sqrt(theta))
+    assert np.all(np.diff(inv) < 0)
+    # exponent additivity: inv_i * inv_j = inv_{i+j} up to binary32 rounding
+    for i, j in [(1, 2), (3, 5), (7, 9)]:
+        assert abs(inv[i] * inv[j] / inv[i + j] - 1.0) < 3 * 2.0 ** -24
+
+
+def test_inv_freq_theta_1e4_quarter_point():
+    assert O.rope_inv_freq(1.0e4, 64)[16] == np.float32(0.01)
+
+
+def test_rope_table_position_zero_and_pair_zero():
+    pos = np.arange(0, 4096, 37)
+    c, s = O.rope_cos_sin(5.0e5, 128, pos)
+    assert c.shape == (len(pos), 64)
+    np.testing.assert_array_equal(c[0], 1.0)
+    np.testing.assert_array_equal(s[0], 0.0)
+    # pair 0 has inverse frequency 1, so its angle is the position itself
+    for r, p in enumerate(pos):
+        assert c[r, 0] == np.float32(math.cos(p))
+        assert s[r, 0] == np.float32(math.sin(p))
+
+
+def test_rope_table_unit_circle_and_fp32_values():
+    c, s = O.rope_cos_sin(1.0e4, 64, np.arange(0, 32768, 997))
+    assert np.all(np.abs(c * c + s * s - 1.0) < 4 * 2.0 ** -24)
+    np.testing.assert_array_equal(c, c.astype(np.float32).astype(np.float64))
+    np.testing.assert_array_equal(s, s.astype(np.float32).astype(np.float64))
+
+
+def test_rope_table_power_of_two_position_angle_is_exact_product():
+    # for p = 2**k the binary32 product p*inv_i is exact: angle = p * inv_i
+    inv = O.rope_inv_freq(5.0e5, 128)
+    c, s = O.rope_cos_sin(5.0e5, 128, [1024])
+    for i in (0, 5, 31, 63):
+        a = 1024.0 * float(inv[i])
+        assert c[0, i] == np.float32(math.cos(a)) and s[0, i] == np.float32(math.sin(a))
+
+
+def test_rope_table_angle_is_binary32_product_like_an_fp32_module():
+    # An FP32 rotary module forms angle = position(fp32) * inv_freq(fp32) in
+    # binary32 arithmetic; here torch does that product, float64 does cos/sin.
+    inv = torch.from_numpy(O.rope_inv_freq(5.0e5, 128).astype(np.float32))
+    pos = torch.arange(0, 32768, 5, dtype=torch.float32)
+    ang = (pos[:, None] * inv[None, :]).to(torch.float64)
+    c, s = O.rope_cos_sin(5.0e5, 128, pos.numpy())
+    np.testing.assert_array_equal(c, torch.cos(ang).to(torch.float32).double().numpy())
+    np.testing.assert_array_equal(s, torch.sin(ang).to(torch.float32).double().numpy())
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def _bf16(x):
+    return O.round_bf16(np.asarray(x, dtype=np.float64))
+
+
+def test_rms_unit_rms_before_gain():
+    x = _bf16(np.random.default_rng(2).standard_normal((50, 3, 128)) * 3.0)
+    y, rstd = O.rms_normalize(x, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-13)
+    assert rstd.shape == (50, 3)
+
+
+def test_rms_eps_enters_inside_the_root():
+    x = _bf16(np.random.default_rng(3).standard_normal((40, 64)) * 0.01)
+    eps = 1e-4
+    y, rstd = O.rms_normalize(x, eps)
+    m = np.mean(x * x, axis=-1)
+    epsf = float(np.float32(eps))
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), np.sqrt(m / (m + epsf)), rtol=1e-12)
+    np.testing.assert_allclose(rstd, 1.0 / np.sqrt(m + epsf), rtol=1e-14)
+
+
+def test_rms_constant_row_and_zero_row():
+    x = np.full((2, 16), -3.0)
+    x[1] = 0.0
+    y, rstd = O.rms_norm(x, 1e-6)
+    # constant row: output is sign(c) (gain 1), rstd = 1/sqrt(c^2 + eps)
+    np.testing.assert_array_equal(y[0], -1.0)
+    np.testing.assert_array_equal(y[1], 0.0)
+    assert abs(rstd[0] - 1.0 / math.sqrt(9.0 + float(np.float32(1e-6)))) < 1e-15
+
+
+def test_rms_axis_is_last_dim_per_head():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((8, 4, 64))
+    x[:, 1] *= 100.0
+    x[:, 3] *= 0.001
+    y, _ = O.rms_normalize(x, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-12)
+
+
+def test_rms_scale_invariance_eps0():
+    x = _bf16(np.random.default_rng(5).standard_normal((16, 128)))
+    a, _ = O.rms_norm(x, 0.0)
+    b, _ = O.rms_norm(4.0 * x, 0.0)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_gain_zero_centered_semantics():
+    x = _bf16(np.random.default_rng(6).standard_normal((16, 64)))
+    plain, _ = O.rms_norm(x, 1e-6)
+    g0, _ = O.rms_norm(x, 1e-6, gain=np.zeros(64), gain_center=1.0)
+    np.testing.assert_array_equal(plain, g0)                 # g = 0 keeps the effective gain 1
+    g1, _ = O.rms_norm(x, 1e-6, gain=np.ones(64), gain_center=1.0)
+    np.testing.assert_array_equal(g1, 2.0 * plain)           # 1 + 1 = 2: exact doubling
+    # a per-dim gain scales its own column (not rows, not heads)
+    g = np.linspace(-0.5, 0.5, 64)
+    gd, _ = O.rms_norm(x, 1e-6, gain=g, gain_center=1.0)
+    y, _ = O.rms_normalize(x, 1e-6)
+    np.testing.assert_allclose(gd, y * (1.0 + g), rtol=2.0 ** -8, atol=1e-30)
+
+
+# ---------------------------------------------------------------- RoPE rotation
+
+def test_rope_rotation_is_complex_multiplication():
+    rng = np.random.default_rng(7)
+    x = _bf16(rng.standard_normal((32, 64)))
+    ang = rng.uniform(-100, 100, (32, 32))
+    c, s = np.cos(ang), np.sin(ang)
+    y = O.rope_rotate(x, c, s)
+    z = (x[:, 0::2] + 1j * x[:, 1::2]) * (c + 1j * s)      # RoFormer: x * e^{i m theta}
+    np.testing.assert_array_equal(y[:, 0::2], _bf16(z.real))
+    np.testing.assert_array_equal(y[:, 1::2], _bf16(z.imag))
+
+
+def test_rope_adjacent_pair_equals_split_half_after_row_permutation():
+    # adapter page, _permute_rope_rows: adjacent-pair and split-half RoPE differ
+    # by a permutation of head rows.  Split-half uses rotate_half(x) = [-x2, x1].
+    d = 64
+    rng = np.random.default_rng(8)
+    x = _bf16(rng.standard_normal((10, d)))
+    ang = rng.uniform(0, 50, (10, d // 2))
+    c, s = np.cos(ang), np.sin(ang)
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])  # adjacent -> split-half
+    xs = x[:, perm]
+    half = np.concatenate([-xs[:, d // 2:], xs[:, :d // 2]], axis=1)
+    ys = _bf16(xs * np.concatenate([c, c], 1) + half * np.concatenate([s, s], 1))
+    y = O.rope_rotate(x, c, s)
+    np.testing.assert_array_equal(y[:, perm], ys)
+
+
+def test_rope_position_zero_identity_and_norm_preservation():
+    rng = np.random.default_rng(9)
+    x = _bf16(rng.standard_normal((64, 4, 128)))
+    c, s = O.rope_cos_sin(5.0e5, 128, np.zeros(64))
+    np.testing.assert_array_equal(O.rope_rotate(x, c[:, None], s[:, None]), x)
+    c, s = O.rope_cos_sin(5.0e5, 128, np.arange(64) * 251)
+    y = O.rope_rotate(x, c[:, None], s[:, None])
+    n0 = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    n1 = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    assert np.all(np.abs(n1 - n0) <= 2 * 2.0 ** -7 * n0 + 1e-30)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(10)
+    q = _bf16(rng.standard_normal(128))
+    k = _bf16(rng.standard_normal(128))
+
+    def score(m, n):
+        cm, sm = O.rope_cos_sin(1.0e4, 128, [m])
+        cn, sn = O.rope_cos_sin(1.0e4, 128, [n])
+        return float(O.rope_rotate(q, cm[0], sm[0]) @ O.rope_rotate(k, cn[0], sn[0]))
+
+    base = score(7, 3)
+    for m, n in [(104, 100), (1004, 1000), (12, 8)]:
+        assert abs(score(m, n) - base) < 0.05 * (abs(base) + 1.0)
+    assert abs(score(9, 3) - base) > 1e-3     # and it does depend on m - n
+
+
+def test_qk_norm_rope_query_scale_and_gain_routing():
+    rng = np.random.default_rng(11)
+    n, hq, hkv, d = 6, 4, 2, 64
+    q = _bf16(rng.standard_normal((n, hq, d)))
+    k = _bf16(rng.standard_normal((n, hkv, d)))
+    c, s = O.rope_cos_sin(1.0e4, d, np.arange(n))
+    qg = np.full(d, 1.0)       # effective Q gain 2
+    kg = np.full(d, -0.5)      # effective K gain 1/2
+    a = O.qk_norm_rope(q, k, eps=1e-6, cos=c, sin=s)
+    b = O.qk_norm_rope(q, k, eps=1e-6, cos=c, sin=s, q_gain=qg, k_gain=kg, query_scale=2.0)
+    np.testing.assert_array_equal(b[0], 4.0 * a[0])     # gain 2 then scale 2
+    np.testing.assert_array_equal(b[1], 0.5 * a[1])
+    nr = O.qk_norm_rope(q, k, eps=1e-6, use_rope=False)
+    np.testing.assert_array_equal(nr[0], O.rms_norm(q, 1e-6)[0])
+    np.testing.assert_array_equal(nr[1], O.rms_norm(k, 1e-6)[0])
+
+
+# ---------------------------------------------------------------- attention
+
+def _brute_attention(q, k, v, seg_bounds, window, scaling):
+    """Pure-Python softmax attention: query i sees the `window` most recent keys
+    up to and including itself (all earlier keys when window == 0)."""
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    o = np.zeros((n, hq, d))
+    lse = np.zeros((n, hq))
+    for (s0, length) in seg_bounds:
+        for i in range(length):
+            first = 0 if window <= 0 else max(0, i - window + 1)
+            keys = list(range(first, i + 1))
+            for h in range(hq):
+                g = h * hkv // hq
+                sc = [scaling * sum(q[s0 + i, h, t] * k[s0 + j, g, t] for t in range(d)) for j in keys]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                z = sum(w)
+                for t in range(d):
+                    o[s0 + i, h, t] = sum(w[a] * v[s0 + j, g, t] for a, j in enumerate(keys)) / z
+                lse[s0 + i, h] = mx + math.log(z)
+    return o, lse
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1), (4, 2), (4, 1), (5, 1), (8, 8)])
+@pytest.mark.parametrize("window", [0, 1, 2, 5])
+def test_attention_brute_force_bshd(hq, hkv, window):
+    rng = np.random.default_rng(100 + hq * 10 + window)
+    b, sl, d = 2, 9, 4
+    q = _bf16(rng.standard_normal((b * sl, hq, d)))
+    k = _bf16(rng.standard_normal((b * sl, hkv, d)))
+    v = _bf16(rng.standard_normal((b * sl, hkv, d)))
+    o, lse = O.attention(q, k, v, O.Segments.bshd(b, sl), window=window, scaling=0.7)
+    ro, rl = _brute_attention(q, k, v, [(0, sl), (sl, sl)], window, 0.7)
+    np.testing.assert_array_equal(o, _bf16(ro))
+    np.testing.assert_allclose(lse, rl, rtol=1e-13, atol=1e-13)
+
+
+def test_attention_brute_force_thd_with_length_one_segments():
+    rng = np.random.default_rng(12)
+    lens = [1, 5, 1, 7, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    n, hq, hkv, d = cu[-1], 4, 2, 6
+    q = _bf16(rng.standard_normal((n, hq, d)))
+    k = _bf16(rng.standard_normal((n, hkv, d)))
+    v = _bf16(rng.standard_normal((n, hkv, d)))
+    for window in (0, 2):
+        o, lse = O.attention(q, k, v, O.Segments.thd(cu), window=window, scaling=0.5)
+        ro, rl = _brute_attention(q, k, v, list(zip(cu[:-1], lens)), window, 0.5)
+        np.testing.assert_array_equal(o, _bf16(ro))
+        np.testing.assert_allclose(lse, rl, rtol=1e-13, atol=1e-13)
+
+
+def test_attention_golden_tiny():
+    with open(os.path.join(GOLDEN, "attention_tiny.json")) as f:
+        g = json.load(f)
+    o, lse = O.attention(np.array(g["q"]), np.array(g["k"]), np.array(g["v"]),
+                         O.Segments.bshd(1, 2), window=g["window"], scaling=g["scaling"])
+    np.testing.assert_allclose(o, g["expected_o"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, g["expected_lse"], rtol=0, atol=1e-12)
+
+
+def test_attention_window_one_returns_v_and_row_zero_returns_v0():
+    rng = np.random.default_rng(13)
+    n, hq, hkv, d = 40, 8, 2, 16
+    q = _bf16(rng.standard_normal((n, hq, d)))
+    k = _bf16(rng.standard_normal((n, hkv, d)))
+    v = _bf16(rng.standard_normal((n, hkv, d)))
+    o, lse = O.attention(q, k, v, O.Segments.bshd(1, n), window=1, scaling=0.25)
+    rep = np.repeat(v, hq // hkv, axis=1)
+    np.testing.assert_array_equal(o, rep)
+    o2, _ = O.attention(q, k, v, O.Segments.bshd(2, n // 2), window=0, scaling=0.25)
+    np.testing.assert_array_equal(o2[0], rep[0])
+    np.testing.assert_array_equal(o2[n // 2], rep[n // 2])
+
+
+def test_attention_zero_query_gives_prefix_and_window_means():
+    rng = np.random.default_rng(14)
+    n, d = 30, 8
+    q = np.zeros((n, 2, d))
+    k = _bf16(rng.standard_normal((n, 1, d)))
+    v = _bf16(rng.standard_normal((n, 1, d)))
+    o, lse = O.attention(q, k, v, O.Segments.bshd(1, n), window=0, scaling=1.0)
+    csum = np.cumsum(v[:, 0], axis=0)
+    cnt = np.arange(1, n + 1)[:, None]
+    np.testing.assert_array_equal(o[:, 0], _bf16(csum / cnt))
+    np.testing.assert_allclose(lse[:, 1], np.log(np.arange(1, n + 1)), rtol=1e-14)
+    w = 4
+    ow, lw = O.attention(q, k, v, O.Segments.bshd(1, n), window=w, scaling=1.0)
+    for i in range(n):
+        lo = max(0, i - w + 1)
+        np.testing.assert_array_equal(ow[i, 0], _bf16(v[lo:i + 1, 0].mean(axis=0)))
+        assert abs(lw[i, 0] - math.log(i + 1 - lo)) < 1e-14
+
+
+def test_attention_invariants_window_ge_len_gqa_thd_lse():
+    rng = np.random.default_rng(15)
+    lens = [13, 4, 21]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    n, hq, hkv, d = cu[-1], 8, 2, 16
+    q = _bf16(rng.standard_normal((n, hq, d)))
+    k = _bf16(rng.standard_normal((n, hkv, d)))
+    v = _bf16(rng.standard_normal((n, hkv, d)))
+    seg = O.Segments.thd(cu)
+    full, lfull = O.attention(q, k, v, seg, window=0, scaling=0.3)
+    big, _ = O.attention(q, k, v, seg, window=max(lens), scaling=0.3)
+    np.testing.assert_array_equal(full, big)                   # W >= L is full causal
+    rep_k = np.repeat(k, hq // hkv, axis=1)                     # _repeat_kv to query heads
+    rep_v = np.repeat(v, hq // hkv, axis=1)
+    mha, _ = O.attention(q, rep_k, rep_v, seg, window=0, scaling=0.3)
+    np.testing.assert_array_equal(full, mha)                   # GQA == MHA on repeated KV
+    for s0, length in zip(cu[:-1], lens):                      # THD == per-segment BSHD
+        part, lpart = O.attention(q[s0:s0 + length], k[s0:s0 + length], v[s0:s0 + length],
+                                  O.Segments.bshd(1, length), window=0, scaling=0.3)
+        np.testing.assert_array_equal(full[s0:s0 + length], part)
+        np.testing.assert_array_equal(lfull[s0:s0 + length], lpart)
+    # lse = log-sum-exp of the visible scores (library routine)
+    t, h = cu[2] + 9, 5
+    s = 0.3 * (k[cu[2]:t + 1, h // 4] @ q[t, h])
+    assert abs(lfull[t, h] - scipy.special.logsumexp(s)) < 1e-12
+    # head permutation inside a group permutes outputs
+    perm = np.array([1, 0, 3, 2, 5, 4, 7, 6])
+    pm, _ = O.attention(q[:, perm], k, v, seg, window=0, scaling=0.3)
+    np.testing.assert_array_equal(pm, full[:, perm])
+
+
+def test_visible_mask_window_counts_keys_including_self():
+    vis = O.visible_mask(np.arange(10), np.arange(10), 3)
+    np.testing.assert_array_equal(vis.sum(axis=1), [1, 2, 3, 3, 3, 3, 3, 3, 3, 3])
+    assert vis[5, 5] and vis[5, 3] and not vis[5, 2] and not vis[5, 6]
+
+
+# ---------------------------------------------------------------- output norm + gate
+
+def test_out_gate_half_and_symmetry():
+    rng = np.random.default_rng(16)
+    o = _bf16(rng.standard_normal((20, 4, 64)))
+    half, _ = O.out_norm_gate(o, np.zeros_like(o), 1e-6)
+    one, _ = O.out_norm_gate(o, np.full_like(o, 40.0), 1e-6)
+    np.testing.assert_array_equal(half, 0.5 * one)
+    g = rng.standard_normal(o.shape) * 4.0
+    a, _ = O.out_norm_gate(o, g, 0.0)
+    b, _ = O.out_norm_gate(o, -g, 0.0)
+    y, _ = O.rms_normalize(o, 0.0)
+    np.testing.assert_allclose(a + b, y, rtol=0, atol=2 * 2.0 ** -8 * np.abs(y).max())
+
+
+def test_out_gate_sigmoid_matches_library_on_unit_rows():
+    g = _bf16(np.linspace(-30, 30, 128))
+    o = np.full((1, 128), 2.0)               # normalises to exactly 1
+    out, rstd = O.out_norm_gate(o, g[None, :], 0.0)
+    np.testing.assert_array_equal(out[0], _bf16(scipy.special.expit(g)))
+    assert rstd[0] == 0.5
+
+
+def test_out_norm_unit_rms():
+    rng = np.random.default_rng(17)
+    o = _bf16(rng.standard_normal((30, 64)) * 0.05)
+    out, _ = O.out_norm_gate(o, np.full_like(o, 40.0), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(out * out, axis=-1)), 1.0, rtol=2.0 ** -8)
+
+
+# ---------------------------------------------------------------- composition
+
+def test_segments_positions_restart_per_segment():
+    seg = O.Segments.thd([0, 3, 3 + 5, 3 + 5 + 2])
+    np.testing.assert_array_equal(seg.local_positions(), [0, 1, 2, 0, 1, 2, 3, 4, 0, 1])
+    np.testing.assert_array_equal(O.Segments.bshd(2, 3).local_positions(), [0, 1, 2, 0, 1, 2])
+
+
+def test_core_rows_match_full_core():
+    rng = np.random.default_rng(18)
+    lens = [17, 40, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    n, hq, hkv, d = cu[-1], 6, 2, 32
+    q = _bf16(rng.standard_normal((n, hq, d)))
+    k = _bf16(rng.standard_normal((n, hkv, d)))
+    v = _bf16(rng.standard_normal((n, hkv, d)))
+    gate = _bf16(rng.standard_normal((n, hq, d)))
+    qg = _bf16(rng.standard_normal(d) * 0.05)
+    kg = _bf16(rng.standard_normal(d) * 0.05)
+    kw = dict(theta=1.0e4, eps=1e-6, out_eps=1e-6, scaling=d ** -0.5, window=7, q_gain=qg,
+              k_gain=kg)
+    seg = O.Segments.thd(cu)
+    full = O.attn_core(q, k, v, gate, seg, **kw)
+    rows = [(0, 0), (16, 5), (17, 2), (56, 3), (cu[2] + 8, 1), (30, 4)]
+    part = O.attn_core_rows(q, k, v, gate, seg, rows, **kw)
+    for r, (t, h) in enumerate(rows):
+        np.testing.assert_array_equal(part["out"][r], full["out"][t, h])
+        np.testing.assert_array_equal(part["q_hat"][r], full["q_hat"][t, h])
+        assert part["lse"][r] == full["lse"][t, h]
+    np.testing.assert_array_equal(part["k_hat"], full["k_hat"])
