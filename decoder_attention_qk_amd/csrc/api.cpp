@@ -1,0 +1,363 @@
+// C ABI of libmuseattn: argument validation on the host, then kernel launches
+// on the caller's stream.  No allocation, no global state besides the
+// per-thread error message.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "host_util.hpp"
+#include "kernels.hpp"
+#include "muse_attn.h"
+
+namespace muse {
+namespace {
+
+struct Geometry {
+  int64_t n_tokens;
+  int d, hq, hkv, group;
+  bool thd;
+  int nseg;
+  int maxlen;
+};
+
+struct Range {
+  const void *p;
+  int64_t bytes;
+  const char *name;
+};
+
+bool ranges_overlap(const Range &a, const Range &b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+// Each output must not overlap any input or any other output.
+muse_status check_disjoint(const std::vector<Range> &inputs, const std::vector<Range> &outputs) {
+  for (size_t i = 0; i < outputs.size(); ++i) {
+    for (const Range &in : inputs)
+      if (ranges_overlap(outputs[i], in))
+        return set_error(MUSE_ERR_INVALID_ARG, "output %s overlaps input %s", outputs[i].name, in.name);
+    for (size_t j = i + 1; j < outputs.size(); ++j)
+      if (ranges_overlap(outputs[i], outputs[j]))
+        return set_error(MUSE_ERR_INVALID_ARG, "outputs %s and %s overlap", outputs[i].name, outputs[j].name);
+  }
+  return MUSE_OK;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+muse_status check_params(const muse_attn_params *p) {
+  if (!p) return set_error(MUSE_ERR_INVALID_ARG, "params is NULL");
+  if (p->head_dim <= 0 || (p->head_dim & 1))
+    return set_error(MUSE_ERR_INVALID_ARG, "head_dim %d must be positive and even", p->head_dim);
+  if (p->num_heads <= 0 || p->num_key_value_heads <= 0)
+    return set_error(MUSE_ERR_INVALID_ARG, "num_heads %d / num_key_value_heads %d must be positive",
+                     p->num_heads, p->num_key_value_heads);
+  if (p->num_heads % p->num_key_value_heads)
+    return set_error(MUSE_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_key_value_heads %d",
+                     p->num_heads, p->num_key_value_heads);
+  if (!finite(p->scaling) || p->scaling <= 0.0f)
+    return set_error(MUSE_ERR_INVALID_ARG, "scaling must be finite and > 0");
+  if (!finite(p->query_scale)) return set_error(MUSE_ERR_INVALID_ARG, "query_scale must be finite");
+  if (!finite(p->qk_eps) || p->qk_eps < 0.0f || !finite(p->out_eps) || p->out_eps < 0.0f)
+    return set_error(MUSE_ERR_INVALID_ARG, "qk_eps/out_eps must be finite and >= 0");
+  if (!finite(p->gain_center)) return set_error(MUSE_ERR_INVALID_ARG, "gain_center must be finite");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return set_error(MUSE_ERR_UNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", p->head_dim);
+  if (p->use_rope && !p->upcast_rope)
+    return set_error(MUSE_ERR_UNSUPPORTED, "upcast_rope = 0 (bf16-rounded rotation products) is not built");
+  return MUSE_OK;
+}
+
+bool debug_validate() {
+  const char *e = std::getenv("MUSE_DEBUG_VALIDATE");
+  return e && e[0] == '1';
+}
+
+muse_status check_layout(const muse_layout *l, const muse_attn_params *p, hipStream_t stream,
+                         Geometry *g) {
+  if (!l) return set_error(MUSE_ERR_INVALID_ARG, "layout is NULL");
+  g->d = p->head_dim;
+  g->hq = p->num_heads;
+  g->hkv = p->num_key_value_heads;
+  g->group = g->hq / g->hkv;
+  if (l->cu_seqlens) {
+    if (l->num_segments < 1) return set_error(MUSE_ERR_INVALID_ARG, "THD num_segments %d < 1", l->num_segments);
+    if (l->total_tokens < 0 || l->max_seqlen < 0)
+      return set_error(MUSE_ERR_INVALID_ARG, "THD total_tokens/max_seqlen must be >= 0");
+    if (l->max_seqlen > l->total_tokens)
+      return set_error(MUSE_ERR_INVALID_ARG, "max_seqlen %d > total_tokens %d", l->max_seqlen, l->total_tokens);
+    if (l->total_tokens > 0 && l->max_seqlen < 1)
+      return set_error(MUSE_ERR_INVALID_ARG, "max_seqlen must be >= 1 when total_tokens > 0");
+    g->thd = true;
+    g->n_tokens = l->total_tokens;
+    g->nseg = l->num_segments;
+    g->maxlen = l->max_seqlen;
+    if (debug_validate() && l->num_segments < (1 << 26)) {
+      std::vector<int32_t> host((size_t)l->num_segments + 1);
+      if (hipMemcpyAsync(host.data(), l->cu_seqlens, host.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                         stream) != hipSuccess ||
+          hipStreamSynchronize(stream) != hipSuccess)
+        return set_error(MUSE_ERR_DEVICE, "copying cu_seqlens for validation failed");
+      const muse_status s = muse_validate_cu_seqlens(host.data(), l->num_segments, l->total_tokens, l->max_seqlen);
+      if (s != MUSE_OK) return s;
+    }
+  } else {
+    if (l->batch < 0 || l->seqlen < 0)
+      return set_error(MUSE_ERR_INVALID_ARG, "BSHD batch %d / seqlen %d must be >= 0", l->batch, l->seqlen);
+    g->thd = false;
+    g->n_tokens = (int64_t)l->batch * l->seqlen;
+    g->nseg = l->batch;
+    g->maxlen = l->seqlen;
+  }
+  if (g->n_tokens > INT32_MAX / 2)
+    return set_error(MUSE_ERR_UNSUPPORTED, "%lld tokens exceed the 2^30 token limit", (long long)g->n_tokens);
+  return MUSE_OK;
+}
+
+TokenLayout token_layout(const muse_layout *l, const Geometry &g) {
+  TokenLayout t;
+  t.n_tokens = (int32_t)g.n_tokens;
+  t.seqlen = g.thd ? 0 : l->seqlen;
+  t.cu_seqlens = g.thd ? l->cu_seqlens : nullptr;
+  t.num_segments = g.nseg;
+  t.position_ids = l->position_ids;
+  return t;
+}
+
+Range layout_range(const muse_layout *l, const Geometry &g, int which) {
+  if (which == 0) return Range{g.thd ? l->cu_seqlens : nullptr, ((int64_t)g.nseg + 1) * 4, "cu_seqlens"};
+  return Range{l->position_ids, g.n_tokens * 4, "position_ids"};
+}
+
+muse_status check_rope_table(const muse_attn_params *p, const muse_layout *l, const Geometry &g,
+                             const float *cos, const float *sin, int32_t n_pos) {
+  if (!p->use_rope || g.n_tokens == 0) return MUSE_OK;
+  if (!cos || !sin) return set_error(MUSE_ERR_INVALID_ARG, "use_rope needs the cos and sin tables");
+  if (n_pos < 1) return set_error(MUSE_ERR_INVALID_ARG, "n_pos %d < 1", n_pos);
+  if (!l->position_ids && n_pos < g.maxlen)
+    return set_error(MUSE_ERR_INVALID_ARG, "cos/sin table has %d positions, the layout needs %d", n_pos,
+                     g.maxlen);
+  return MUSE_OK;
+}
+
+muse_status device_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return set_error(MUSE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  clear_error();
+  return MUSE_OK;
+}
+
+void attn_shape(int group, int *heads_per_wg, int *tok_blocks, int *head_chunks) {
+  int h = 1;
+  for (int d = group < 8 ? group : 8; d >= 1; --d)
+    if (group % d == 0) { h = d; break; }
+  *heads_per_wg = h;
+  *tok_blocks = h >= 4 ? 1 : 4 / h;
+  *head_chunks = group / h;
+}
+
+AttnArgs attn_args(const muse_attn_params *p, const muse_layout *l, const Geometry &g) {
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.eps = p->qk_eps;
+  a.out_eps = p->out_eps;
+  a.gain_center = p->gain_center;
+  a.query_scale = p->query_scale;
+  a.use_rope = p->use_rope ? 1 : 0;
+  a.scaling = p->scaling;
+  a.scale_log2 = p->scaling * 1.4426950408889634f;
+  a.hq = g.hq;
+  a.hkv = g.hkv;
+  a.group = g.group;
+  attn_shape(g.group, &a.heads_per_wg, &a.tok_blocks, &a.head_chunks);
+  a.window = p->sliding_window > 0 ? p->sliding_window : 0;
+  const int bm = 32 * a.tok_blocks;
+  a.q_blocks = (g.maxlen + bm - 1) / bm;
+  a.lay = token_layout(l, g);
+  return a;
+}
+
+int64_t bf16_bytes(int64_t n, int h, int d) { return n * h * d * 2; }
+
+}  // namespace
+}  // namespace muse
+
+using namespace muse;
+
+extern "C" muse_status muse_rope_cos_sin(float theta, int32_t head_dim, int32_t n_pos, float *cos_out,
+                                         float *sin_out, void *stream) {
+  if (!std::isfinite(theta) || theta <= 0.0f) return set_error(MUSE_ERR_INVALID_ARG, "theta must be finite and > 0");
+  if (head_dim <= 0 || (head_dim & 1)) return set_error(MUSE_ERR_INVALID_ARG, "head_dim %d must be positive and even", head_dim);
+  if (n_pos < 0) return set_error(MUSE_ERR_INVALID_ARG, "n_pos %d < 0", n_pos);
+  if (n_pos == 0) { clear_error(); return MUSE_OK; }
+  if (!cos_out || !sin_out) return set_error(MUSE_ERR_INVALID_ARG, "cos_out/sin_out is NULL");
+  const int64_t bytes = (int64_t)n_pos * (head_dim / 2) * 4;
+  muse_status s = check_disjoint({}, {{cos_out, bytes, "cos_out"}, {sin_out, bytes, "sin_out"}});
+  if (s != MUSE_OK) return s;
+  RopeTableArgs a{theta, head_dim, n_pos, cos_out, sin_out};
+  return device_status(launch_rope_table(a, (hipStream_t)stream), "rope table launch");
+}
+
+extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_layout *l, const void *q,
+                                         const void *k, const float *q_gain, const float *k_gain,
+                                         const float *cos, const float *sin, int32_t n_pos, void *q_out,
+                                         void *k_out, float *q_rstd, float *k_rstd, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  if ((q == nullptr) != (q_out == nullptr)) return set_error(MUSE_ERR_INVALID_ARG, "q and q_out must be given together");
+  if ((k == nullptr) != (k_out == nullptr)) return set_error(MUSE_ERR_INVALID_ARG, "k and k_out must be given together");
+  if (!q && !k) return set_error(MUSE_ERR_INVALID_ARG, "neither q nor k given");
+  if (!q && q_rstd) return set_error(MUSE_ERR_INVALID_ARG, "q_rstd given without q");
+  if (!k && k_rstd) return set_error(MUSE_ERR_INVALID_ARG, "k_rstd given without k");
+  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
+  s = check_disjoint(
+      {{q, bf16_bytes(N, g.hq, g.d), "q"}, {k, bf16_bytes(N, g.hkv, g.d), "k"}, {q_gain, g.d * 4, "q_gain"},
+       {k_gain, g.d * 4, "k_gain"}, {cos, tab, "cos"}, {sin, tab, "sin"}, layout_range(l, g, 0),
+       layout_range(l, g, 1)},
+      {{q_out, bf16_bytes(N, g.hq, g.d), "q_out"}, {k_out, bf16_bytes(N, g.hkv, g.d), "k_out"},
+       {q_rstd, N * g.hq * 4, "q_rstd"}, {k_rstd, N * g.hkv * 4, "k_rstd"}});
+  if (s != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  QkNormArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.q_out = (uint16_t *)q_out;
+  a.k_out = (uint16_t *)k_out;
+  a.q_rstd = q_rstd;
+  a.k_rstd = k_rstd;
+  a.q_gain = q_gain;
+  a.k_gain = k_gain;
+  a.cos_tab = cos;
+  a.sin_tab = sin;
+  a.n_pos = n_pos;
+  a.hq = g.hq;
+  a.hkv = g.hkv;
+  a.q_rows = q ? N * g.hq : 0;
+  a.total_rows = a.q_rows + (k ? N * g.hkv : 0);
+  a.eps = p->qk_eps;
+  a.gain_center = p->gain_center;
+  a.query_scale = p->query_scale;
+  a.use_rope = p->use_rope ? 1 : 0;
+  a.lay = token_layout(l, g);
+  return device_status(launch_qk_norm_rope(g.d, a, (hipStream_t)stream), "qk_norm_rope launch");
+}
+
+extern "C" muse_status muse_gqa_attn_fwd(const muse_attn_params *p, const muse_layout *l, const void *q_hat,
+                                         const void *k_hat, const void *v, void *o, float *lse, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  if (N > 0 && (!q_hat || !k_hat || !v || !o))
+    return set_error(MUSE_ERR_INVALID_ARG, "q_hat, k_hat, v and o are required");
+  s = check_disjoint({{q_hat, bf16_bytes(N, g.hq, g.d), "q_hat"}, {k_hat, bf16_bytes(N, g.hkv, g.d), "k_hat"},
+                      {v, bf16_bytes(N, g.hkv, g.d), "v"}, layout_range(l, g, 0), layout_range(l, g, 1)},
+                     {{o, bf16_bytes(N, g.hq, g.d), "o"}, {lse, N * g.hq * 4, "lse"}});
+  if (s != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  AttnArgs a = attn_args(p, l, g);
+  a.q = (const uint16_t *)q_hat;
+  a.k = (const uint16_t *)k_hat;
+  a.v = (const uint16_t *)v;
+  a.o = (uint16_t *)o;
+  a.lse = lse;
+  return device_status(launch_attn_fwd(g.d, false, a, (hipStream_t)stream), "attention launch");
+}
+
+extern "C" muse_status muse_out_norm_gate(const muse_attn_params *p, const muse_layout *l, const void *o,
+                                          const void *gate, void *out, float *o_rstd, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  if (N > 0 && (!o || !gate || !out)) return set_error(MUSE_ERR_INVALID_ARG, "o, gate and out are required");
+  s = check_disjoint({{o, bf16_bytes(N, g.hq, g.d), "o"}, {gate, bf16_bytes(N, g.hq, g.d), "gate"}},
+                     {{out, bf16_bytes(N, g.hq, g.d), "out"}, {o_rstd, N * g.hq * 4, "o_rstd"}});
+  if (s != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  OutGateArgs a{(const uint16_t *)o, (const uint16_t *)gate, (uint16_t *)out, o_rstd, N * g.hq, p->out_eps};
+  return device_status(launch_out_norm_gate(g.d, a, (hipStream_t)stream), "out_norm_gate launch");
+}
+
+extern "C" muse_status muse_attn_fused_fwd(const muse_attn_params *p, const muse_layout *l, const void *q,
+                                           const void *k_hat, const void *v, const void *gate,
+                                           const float *q_gain, const float *cos, const float *sin,
+                                           int32_t n_pos, void *out, float *lse, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  if (N > 0 && (!q || !k_hat || !v || !gate || !out))
+    return set_error(MUSE_ERR_INVALID_ARG, "q, k_hat, v, gate and out are required");
+  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  if (s != MUSE_OK) return s;
+  const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
+  s = check_disjoint({{q, bf16_bytes(N, g.hq, g.d), "q"}, {k_hat, bf16_bytes(N, g.hkv, g.d), "k_hat"},
+                      {v, bf16_bytes(N, g.hkv, g.d), "v"}, {gate, bf16_bytes(N, g.hq, g.d), "gate"},
+                      {q_gain, g.d * 4, "q_gain"}, {cos, tab, "cos"}, {sin, tab, "sin"},
+                      layout_range(l, g, 0), layout_range(l, g, 1)},
+                     {{out, bf16_bytes(N, g.hq, g.d), "out"}, {lse, N * g.hq * 4, "lse"}});
+  if (s != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  AttnArgs a = attn_args(p, l, g);
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k_hat;
+  a.v = (const uint16_t *)v;
+  a.gate = (const uint16_t *)gate;
+  a.o = (uint16_t *)out;
+  a.lse = lse;
+  a.q_gain = q_gain;
+  a.cos_tab = cos;
+  a.sin_tab = sin;
+  a.n_pos = n_pos;
+  return device_status(launch_attn_fwd(g.d, true, a, (hipStream_t)stream), "fused attention launch");
+}
+
+extern "C" muse_status muse_attn_core_fwd(const muse_attn_params *p, const muse_layout *l, const void *q,
+                                          const void *k, const void *v, const void *gate, const float *q_gain,
+                                          const float *k_gain, const float *cos, const float *sin, int32_t n_pos,
+                                          void *k_hat_out, void *out, float *lse, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  if (N > 0 && (!q || !k || !v || !gate || !k_hat_out || !out))
+    return set_error(MUSE_ERR_INVALID_ARG, "q, k, v, gate, k_hat_out and out are required");
+  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  if (s != MUSE_OK) return s;
+  const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
+  s = check_disjoint(
+      {{q, bf16_bytes(N, g.hq, g.d), "q"}, {k, bf16_bytes(N, g.hkv, g.d), "k"}, {v, bf16_bytes(N, g.hkv, g.d), "v"},
+       {gate, bf16_bytes(N, g.hq, g.d), "gate"}, {q_gain, g.d * 4, "q_gain"}, {k_gain, g.d * 4, "k_gain"},
+       {cos, tab, "cos"}, {sin, tab, "sin"}, layout_range(l, g, 0), layout_range(l, g, 1)},
+      {{k_hat_out, bf16_bytes(N, g.hkv, g.d), "k_hat_out"}, {out, bf16_bytes(N, g.hq, g.d), "out"},
+       {lse, N * g.hq * 4, "lse"}});
+  if (s != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  // keys: norm + gain + RoPE once per key (the K-only pass of the Q/K kernel),
+  // then attention with the query prologue and the norm/gate epilogue fused.
+  s = muse_qk_norm_rope(p, l, nullptr, k, nullptr, k_gain, cos, sin, n_pos, nullptr, k_hat_out, nullptr,
+                        nullptr, stream);
+  if (s != MUSE_OK) return s;
+  return muse_attn_fused_fwd(p, l, q, k_hat_out, v, gate, q_gain, cos, sin, n_pos, out, lse, stream);
+}

@@ -1,0 +1,122 @@
+// Device helpers shared by the libmuseattn kernels (gfx950, wave64).
+//
+// The per-element arithmetic of the Q/K norm + RoPE step and of the output
+// norm + gate step lives here once, so the standalone kernels and the fused
+// attention kernel apply the same operations in the same order and produce
+// identical bits.  Sums of squares use one fixed reduction tree (a per-chunk
+// fma chain, then pairwise sums over chunk indices); every kernel that
+// normalises a row reproduces that tree whatever its lane layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muse {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bfloat16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ float round_bf16(float x) {
+  __bf16 a = (__bf16)x;
+  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, a) << 16);
+}
+
+// 8 bf16 in a uint4 <-> 8 floats.
+__device__ __forceinline__ void unpack8(const uint4 &v, float (&x)[8]) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ uint4 pack8(const float (&y)[8]) {
+  uint4 r;
+  r.x = pack_bf16x2(y[0], y[1]);
+  r.y = pack_bf16x2(y[2], y[3]);
+  r.z = pack_bf16x2(y[4], y[5]);
+  r.w = pack_bf16x2(y[6], y[7]);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Sums of squares.  A row of D values is cut into chunks of CH consecutive
+// elements; each chunk's partial is an fma chain from element 0 upwards; the
+// chunk partials are combined by pairwise sums over chunk indices
+// (c, c^1), then pairs (c>>1, (c>>1)^1), and so on -- the order a butterfly
+// over lanes produces.
+// ---------------------------------------------------------------------------
+template <int CH>
+__device__ __forceinline__ float chunk_sumsq(const float *x) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < CH; ++e) acc = __builtin_fmaf(x[e], x[e], acc);
+  return acc;
+}
+
+// In-register pairwise tree over N chunk partials (N a power of two).
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&p)[N]) {
+#pragma unroll
+  for (int w = 1; w < N; w <<= 1) {
+#pragma unroll
+    for (int c = 0; c < N; c += 2 * w) p[c] = p[c] + p[c + w];
+  }
+  return p[0];
+}
+
+// 1 / sqrt(mean + eps) with correctly rounded sqrt and division.
+__device__ __forceinline__ float rms_rstd(float sumsq, float inv_d, float eps) {
+  return 1.0f / __builtin_sqrtf(__builtin_fmaf(sumsq, inv_d, 0.0f) + eps);
+}
+
+// ---------------------------------------------------------------------------
+// Q/K norm + query scale + RoPE on one chunk of 8 consecutive elements
+// (4 adjacent pairs).  x: inputs; w: effective gains; c, s: cos/sin of the 4
+// pairs (ignored when !rope); qscale applied (with its own bf16 cast) when
+// apply_qscale.  Writes the rotated bf16 values into y.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void qk_chunk(const float (&x)[8], const float (&w)[8], float r,
+                                         bool apply_qscale, float qscale, bool rope,
+                                         const float (&c)[4], const float (&s)[4],
+                                         float (&y)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float t = round_bf16((x[e] * r) * w[e]);
+    if (apply_qscale) t = round_bf16(t * qscale);
+    y[e] = t;
+  }
+  if (rope) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = y[2 * i], b = y[2 * i + 1];
+      y[2 * i] = round_bf16(__builtin_fmaf(a, c[i], -(b * s[i])));
+      y[2 * i + 1] = round_bf16(__builtin_fmaf(a, s[i], b * c[i]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Output norm + gate on one element: bf16((o * r) * sigmoid(g)), sigmoid in
+// FP32 as 1 / (1 + 2^(-g log2 e)).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sigmoidf(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -kLog2e));
+}
+__device__ __forceinline__ float gate_elem(float o, float r, float g) {
+  return (o * r) * sigmoidf(g);
+}
+
+}  // namespace muse

@@ -1,0 +1,108 @@
+// Kernel argument blocks and launchers (internal to libmuseattn).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muse {
+
+// Where each token sits: its row/segment and its RoPE position.
+struct TokenLayout {
+  int32_t n_tokens;              // N
+  int32_t seqlen;                // BSHD row length (cu_seqlens == nullptr)
+  const int32_t *cu_seqlens;     // THD boundaries [num_segments + 1], or nullptr
+  int32_t num_segments;          // THD segments, or BSHD batch
+  const int32_t *position_ids;   // explicit RoPE positions [N], or nullptr
+};
+
+struct RopeTableArgs {
+  float theta;
+  int32_t head_dim;
+  int32_t n_pos;
+  float *cos_out;
+  float *sin_out;
+};
+
+struct QkNormArgs {
+  const uint16_t *q;       // [N, Hq, D] or nullptr
+  const uint16_t *k;       // [N, Hkv, D] or nullptr
+  uint16_t *q_out;
+  uint16_t *k_out;
+  float *q_rstd;           // [N, Hq] or nullptr
+  float *k_rstd;           // [N, Hkv] or nullptr
+  const float *q_gain;     // [D] or nullptr
+  const float *k_gain;     // [D] or nullptr
+  const float *cos_tab;    // [n_pos, D/2]
+  const float *sin_tab;
+  int32_t n_pos;
+  int32_t hq, hkv;
+  int64_t q_rows;          // N * Hq when q is processed, else 0
+  int64_t total_rows;      // q_rows + (k ? N * Hkv : 0)
+  float eps, gain_center, query_scale;
+  int32_t use_rope;
+  TokenLayout lay;
+};
+
+struct OutGateArgs {
+  const uint16_t *o;       // [N, Hq, D]
+  const uint16_t *gate;    // [N, Hq, D]
+  uint16_t *out;           // [N, Hq, D]
+  float *o_rstd;           // [N, Hq] or nullptr
+  int64_t rows;            // N * Hq
+  float eps;
+};
+
+struct AttnArgs {
+  const uint16_t *q;       // fused: raw Q; otherwise normalised, rotated Q
+  const uint16_t *k;       // normalised, rotated K [N, Hkv, D]
+  const uint16_t *v;       // [N, Hkv, D]
+  const uint16_t *gate;    // fused only: [N, Hq, D]
+  uint16_t *o;             // fused: gated output; otherwise attention output
+  float *lse;              // [N, Hq] or nullptr
+  // fused Q prologue
+  const float *q_gain;
+  const float *cos_tab;
+  const float *sin_tab;
+  int32_t n_pos;
+  int32_t use_rope;
+  float eps, out_eps, gain_center, query_scale;
+  // attention
+  float scaling;           // softmax scale
+  float scale_log2;        // scaling * log2(e)
+  int32_t hq, hkv, group;  // group = hq / hkv
+  int32_t heads_per_wg;    // query heads of one kv group handled by one workgroup
+  int32_t head_chunks;     // group / heads_per_wg
+  int32_t tok_blocks;      // 32-token sub-blocks per workgroup (waves = heads_per_wg * tok_blocks)
+  int32_t window;          // <= 0: none
+  int32_t q_blocks;        // ceil(max segment length / (32 * tok_blocks))
+  TokenLayout lay;
+};
+
+hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t stream);
+hipError_t launch_qk_norm_rope(int head_dim, const QkNormArgs &a, hipStream_t stream);
+hipError_t launch_out_norm_gate(int head_dim, const OutGateArgs &a, hipStream_t stream);
+hipError_t launch_attn_fwd(int head_dim, bool fused, const AttnArgs &a, hipStream_t stream);
+
+// Position of token t for RoPE (clamped into the table), and its segment.
+__device__ __forceinline__ int find_segment(const TokenLayout &l, int t) {
+  int lo = 0, hi = l.num_segments;  // invariant: cu[lo] <= t < cu[hi] for a valid layout
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (l.cu_seqlens[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int rope_position(const TokenLayout &l, int t, int n_pos) {
+  int p;
+  if (l.position_ids) {
+    p = l.position_ids[t];
+  } else if (l.cu_seqlens) {
+    p = t - l.cu_seqlens[find_segment(l, t)];
+  } else {
+    p = t % l.seqlen;
+  }
+  return p < 0 ? 0 : (p >= n_pos ? n_pos - 1 : p);
+}
+
+}  // namespace muse

@@ -1,0 +1,32 @@
+// FP32 RoPE cos/sin table (layers page, MuseSparkRotaryEmbedding: FP32
+// adjacent-pair frequencies; cosine/sine of width head_dim / 2).
+//
+// One thread per (position, pair).  The inverse frequency theta^(-2i/D) and
+// the cosine/sine are evaluated in double and rounded once to binary32; the
+// angle itself is the binary32 product of the position and that frequency.
+#include "kernels.hpp"
+
+namespace muse {
+
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
+  const int half = a.head_dim / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.n_pos * half) return;
+  const int p = (int)(idx / half);
+  const int i = (int)(idx % half);
+  const float inv = (float)pow((double)a.theta, -2.0 * (double)i / (double)a.head_dim);
+  const float ang = (float)p * inv;
+  a.cos_out[idx] = (float)cos((double)ang);
+  a.sin_out[idx] = (float)sin((double)ang);
+}
+
+hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t stream) {
+  const int64_t n = (int64_t)a.n_pos * (a.head_dim / 2);
+  if (n == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace muse

@@ -1,0 +1,257 @@
+/*
+ * libmuseattn -- the Muse Spark Open text-decoder attention core on MI355X (gfx950).
+ *
+ * The path runs from post-projection Q/K/V and gate logits to the bf16 tensor
+ * that feeds o_proj:
+ *
+ *   Q/K RMSNorm (FP32 accumulation, zero-centred gain) -> bf16
+ *   -> query_scale -> adjacent-pair RoPE (FP32 frequencies, FP32 rotation) -> bf16
+ *   -> causal GQA softmax attention (BSHD or packed THD, optional sliding window) -> bf16
+ *   -> parameter-free output RMSNorm x sigmoid(gate) -> bf16 [tokens, Hq * D]
+ *
+ * Definitions come from the NeMo AutoModel API reference pages of the
+ * muse_spark package: the "layers" page (MuseSparkAttention, MuseSparkRMSNorm,
+ * MuseSparkRotaryEmbedding, _rms_norm_core, _qk_norm_rope_core,
+ * apply_rotary_embedding, _repeat_kv, _output_norm_gate_core) and the "model"
+ * page (_causal_mask, _validate_thd_documents).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - bf16 tensors are passed as void pointers to bfloat16 bit patterns in
+ *   device memory.  They are token-major and contiguous: Q, gate, O and out
+ *   are [N, Hq, D]; K, V and K-hat are [N, Hkv, D] (token stride H*D, head
+ *   stride D).  BSHD [B, S, H, D] and packed THD [T, H, D] share this layout:
+ *   N = B*S for BSHD and N = T for THD.
+ * - float pointers marked "fp32" are device memory.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
+ *   only enqueues work on that stream and returns without synchronising.
+ * - The caller owns every buffer.  The library allocates no memory, keeps no
+ *   state between calls and is reentrant.  Outputs must not overlap any input
+ *   or other output of the same call (the pages return independent tensors);
+ *   overlapping ranges are rejected with MUSE_ERR_INVALID_ARG.
+ * - Arguments are validated on the host before anything is enqueued.  An
+ *   error leaves every output untouched.  muse_last_error() gives a message.
+ * - Setting MUSE_DEBUG_VALIDATE=1 in the environment makes THD calls copy
+ *   cu_seqlens to the host (synchronising the stream) and check it with
+ *   muse_validate_cu_seqlens; without it, a malformed cu_seqlens gives
+ *   unspecified results but every memory access stays inside the buffers
+ *   implied by the host-visible sizes.
+ */
+#ifndef MUSE_ATTN_H
+#define MUSE_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUSE_OK = 0,
+  MUSE_ERR_INVALID_ARG = 1, /* null pointer, bad size, Hq % Hkv != 0, overlap ... */
+  MUSE_ERR_UNSUPPORTED = 2, /* valid by the pages, not built here (e.g. D not in {64,128}) */
+  MUSE_ERR_DEVICE = 3       /* a HIP call or kernel launch failed */
+} muse_status;
+
+/*
+ * Per-layer attention parameters (layers page, MuseSparkAttention attributes).
+ *
+ * head_dim            D; even.  Kernels exist for D = 64 and D = 128.
+ * num_heads           Hq, query (and gate/output) heads.
+ * num_key_value_heads Hkv; Hq % Hkv == 0.  Query head h reads key/value head
+ *                     h / (Hq / Hkv) (KV repeated to the query-head count,
+ *                     _repeat_kv).
+ * sliding_window      W > 0: query i sees keys j with i - W < j <= i (W keys
+ *                     including itself, model page _causal_mask).  W <= 0: no
+ *                     window (the pages' "or None").
+ * use_rope            non-zero: rotate Q and K (layers page, layer_uses_rope).
+ * upcast_rope         non-zero: FP32 rotation (apply_rotary_embedding upcast=True,
+ *                     the original checkpoint's arithmetic).  Zero (rounding both
+ *                     products to bf16 before adding) returns MUSE_ERR_UNSUPPORTED.
+ * scaling             softmax scale, head_dim ** -0.5 for this model; finite, > 0.
+ * query_scale         multiplier applied after the normalised query's bf16 cast
+ *                     (_qk_norm_rope_core), followed by another bf16 cast.  1.0 is a no-op.
+ * qk_eps, out_eps     RMSNorm stabilisers added to the mean square (finite, >= 0).
+ * gain_center         zero-centred gain offset: effective gain = gain_center + g
+ *                     (MuseSparkRMSNorm gain_center, 1.0 by default).
+ */
+typedef struct {
+  int32_t head_dim;
+  int32_t num_heads;
+  int32_t num_key_value_heads;
+  int32_t sliding_window;
+  int32_t use_rope;
+  int32_t upcast_rope;
+  float scaling;
+  float query_scale;
+  float qk_eps;
+  float out_eps;
+  float gain_center;
+} muse_attn_params;
+
+/*
+ * Token layout (layers page, MuseSparkAttention.forward: qkv_format and
+ * cu_seqlens [documents + 1]; model page, _validate_thd_documents).
+ *
+ * BSHD: cu_seqlens == NULL.  batch >= 0 rows of seqlen >= 0 tokens; each row
+ *       is its own causal sequence; N = batch * seqlen.
+ * THD:  cu_seqlens != NULL: device int32 [num_segments + 1], non-decreasing,
+ *       cu_seqlens[0] == 0, cu_seqlens[num_segments] == total_tokens.  Tokens
+ *       attend only inside their own segment.  max_seqlen (host) must be >= the
+ *       longest segment; it sizes the launch.  batch and seqlen are ignored.
+ * position_ids: optional device int32 [N] RoPE positions (model page, local
+ *       position_ids).  NULL means the implicit positions: the index inside the
+ *       BSHD row, or inside the THD segment (restarting at 0).  Positions must
+ *       lie in [0, n_pos) of the cos/sin table; out-of-range ids are clamped
+ *       into it (memory stays safe, the result is unspecified).  Masking
+ *       always uses the token's index inside its row/segment.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t seqlen;
+  const int32_t *cu_seqlens;
+  int32_t num_segments;
+  int32_t total_tokens;
+  int32_t max_seqlen;
+  const int32_t *position_ids;
+} muse_layout;
+
+/*
+ * FP32 RoPE cos/sin table (layers page, MuseSparkRotaryEmbedding: FP32
+ * adjacent-pair frequencies shared by all text layers; cosine/sine of width
+ * head_dim / 2).
+ *
+ * For position p in [0, n_pos) and pair i in [0, head_dim/2):
+ *   inv_i = float(theta ** (-2 i / head_dim))   (evaluated in double, rounded once)
+ *   a     = float(p) * inv_i                    (binary32 product)
+ *   cos_out[p * head_dim/2 + i] = float(cos(a)), sin_out[...] = float(sin(a))
+ *                                               (cos/sin evaluated in double)
+ * cos_out, sin_out: device fp32 [n_pos, head_dim/2], written.
+ * Errors: INVALID_ARG for theta <= 0 or non-finite, odd or non-positive
+ * head_dim, n_pos < 0, null outputs (when n_pos > 0), overlapping outputs.
+ */
+muse_status muse_rope_cos_sin(float theta, int32_t head_dim, int32_t n_pos, float *cos_out,
+                              float *sin_out, void *stream);
+
+/*
+ * Q/K RMSNorm + gain + bf16 cast + query_scale + adjacent-pair RoPE
+ * (layers page, _qk_norm_rope_core, _rms_norm_core, apply_rotary_embedding).
+ *
+ * For every (token, head) row x of D bf16 values:
+ *   r = 1 / sqrt(mean(x^2) + qk_eps)                   (FP32 accumulation)
+ *   y = bf16(x * r * (gain_center + g))                 (no gain multiply when g is NULL)
+ *   Q only: y = bf16(y * query_scale)
+ *   use_rope: (y0, y1) of each adjacent pair -> bf16(y0 C - y1 S), bf16(y0 S + y1 C)
+ *             in FP32, with C, S = cos/sin[position][pair].
+ *
+ * q       [N, Hq, D] bf16 in;  q_out [N, Hq, D] bf16 out.   Both NULL: skip Q.
+ * k       [N, Hkv, D] bf16 in; k_out [N, Hkv, D] bf16 out.  Both NULL: skip K.
+ * q_gain, k_gain  fp32 [D] raw zero-centred gains, or NULL (parameter-free).
+ *                 The same pointer may be passed for both (one shared qk_norm).
+ * cos, sin        fp32 [n_pos, D/2] table from muse_rope_cos_sin; required
+ *                 when use_rope, ignored otherwise.  Implicit positions need
+ *                 n_pos >= seqlen (BSHD) or >= max_seqlen (THD).
+ * q_rstd, k_rstd  optional fp32 [N, Hq] / [N, Hkv] outputs of r.
+ * Errors: INVALID_ARG (see conventions; also when both q and k are NULL or an
+ * input is given without its output), UNSUPPORTED (D not in {64,128},
+ * upcast_rope == 0), DEVICE.
+ */
+muse_status muse_qk_norm_rope(const muse_attn_params *params, const muse_layout *layout,
+                              const void *q, const void *k, const float *q_gain,
+                              const float *k_gain, const float *cos, const float *sin,
+                              int32_t n_pos, void *q_out, void *k_out, float *q_rstd,
+                              float *k_rstd, void *stream);
+
+/*
+ * Causal GQA softmax attention on normalised, rotated Q/K (layers page,
+ * MuseSparkAttention: scaling = head_dim ** -0.5, GQA groups, sliding_window;
+ * model page, _causal_mask).
+ *
+ * For every query token i (index inside its row/segment) and head h, with
+ * kv = h / (Hq / Hkv) and J(i) the visible keys (j <= i, j > i - W when W > 0,
+ * same row/segment):
+ *   s_j = scaling * <q_hat[i,h], k_hat[j,kv]>   (bf16 products, FP32 accumulation)
+ *   o[i,h] = bf16( sum_j softmax(s)_j v[j,kv] ),  lse[i,h] = ln sum_j exp(s_j)
+ *
+ * q_hat [N, Hq, D], k_hat [N, Hkv, D], v [N, Hkv, D]: bf16 in.
+ * o     [N, Hq, D] bf16 out.  lse: optional fp32 [N, Hq] out (natural log).
+ * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}), DEVICE.
+ */
+muse_status muse_gqa_attn_fwd(const muse_attn_params *params, const muse_layout *layout,
+                              const void *q_hat, const void *k_hat, const void *v, void *o,
+                              float *lse, void *stream);
+
+/*
+ * Parameter-free output RMSNorm times the sigmoid output gate (layers page,
+ * _output_norm_gate_core).
+ *
+ * For every (token, head) row o of D bf16 values and its gate row:
+ *   r = 1 / sqrt(mean(o^2) + out_eps)                   (FP32)
+ *   out = bf16( o * r * 1 / (1 + exp(-gate)) )         (FP32, one final cast)
+ *
+ * o, gate [N, Hq, D] bf16 in; out [N, Hq, D] bf16 out (= [N, Hq*D], o_proj's input).
+ * o_rstd: optional fp32 [N, Hq] out.
+ * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}), DEVICE.
+ */
+muse_status muse_out_norm_gate(const muse_attn_params *params, const muse_layout *layout,
+                               const void *o, const void *gate, void *out, float *o_rstd,
+                               void *stream);
+
+/*
+ * The whole core in one call: muse_qk_norm_rope -> muse_gqa_attn_fwd ->
+ * muse_out_norm_gate, with the query norm/RoPE fused into the attention
+ * kernel's Q load and the output norm and gate applied to the attention
+ * result in registers.  Results equal the three-call chain.
+ *
+ * q, gate [N, Hq, D]; k, v [N, Hkv, D]: bf16 in.  q_gain, k_gain, cos, sin,
+ * n_pos as in muse_qk_norm_rope.
+ * k_hat_out [N, Hkv, D] bf16 out: the normalised, rotated keys (what a KV cache
+ *           keeps).  Required: the attention reads it back.
+ * out       [N, Hq, D] bf16 out.   lse: optional fp32 [N, Hq] out.
+ * Errors: as the three calls above.
+ */
+muse_status muse_attn_core_fwd(const muse_attn_params *params, const muse_layout *layout,
+                               const void *q, const void *k, const void *v, const void *gate,
+                               const float *q_gain, const float *k_gain, const float *cos,
+                               const float *sin, int32_t n_pos, void *k_hat_out, void *out,
+                               float *lse, void *stream);
+
+/*
+ * The attention kernel of muse_attn_core_fwd on its own: the query norm/RoPE
+ * prologue and the output norm/gate epilogue fused, keys already normalised
+ * and rotated (by muse_qk_norm_rope, or held that way in a key cache).
+ * muse_attn_core_fwd is muse_qk_norm_rope on K followed by this call.
+ *
+ * q, gate [N, Hq, D]; k_hat, v [N, Hkv, D]: bf16 in.  q_gain, cos, sin, n_pos
+ * as in muse_qk_norm_rope (Q side).  out [N, Hq, D] bf16 out; lse optional
+ * fp32 [N, Hq] out.
+ * Errors: as muse_gqa_attn_fwd, plus the table rules of muse_qk_norm_rope.
+ */
+muse_status muse_attn_fused_fwd(const muse_attn_params *params, const muse_layout *layout,
+                                const void *q, const void *k_hat, const void *v, const void *gate,
+                                const float *q_gain, const float *cos, const float *sin,
+                                int32_t n_pos, void *out, float *lse, void *stream);
+
+/*
+ * Pure host check of a packed layout (model page, _validate_thd_documents):
+ * cu_seqlens (host int32 [num_segments + 1]) starts at 0, never decreases,
+ * ends at total_tokens, and no segment is longer than max_seqlen.
+ * Returns MUSE_OK or MUSE_ERR_INVALID_ARG.  Touches no GPU.
+ */
+muse_status muse_validate_cu_seqlens(const int32_t *cu_seqlens_host, int32_t num_segments,
+                                     int32_t total_tokens, int32_t max_seqlen);
+
+/* Static name of a status code. */
+const char *muse_status_string(muse_status status);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char *muse_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char *muse_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUSE_ATTN_H */

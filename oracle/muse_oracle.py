@@ -346,38 +346,37 @@ def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling
                 o_rstd=o_rstd, out=out)
 
 
-def attn_core_rows(q, k, v, gate, segments: Segments, rows, *, theta, eps, out_eps, scaling,
-                   window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
+def attn_core_rows(q_rows, k, v, gate_rows, segments: Segments, rows, *, num_heads, theta, eps,
+                   out_eps, scaling, window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
                    query_scale=1.0, position_ids=None):
-    """The full forward for selected (token, head) rows only (K/V are used whole).
+    """The full forward for selected (token, head) rows only.
 
-    Returns a dict with q_hat [R,D], k_hat [N,Hkv,D], o [R,D], lse [R],
-    o_rstd [R] and out [R,D] for the R selected rows.
+    ``q_rows``/``gate_rows`` [R, D] hold the query and gate values of the R
+    selected rows (``num_heads`` query heads in all); K and V [N, Hkv, D] are
+    used whole.  Returns a dict with
+    q_hat [R,D], k_hat [N,Hkv,D], o [R,D], lse [R], o_rstd [R] and out [R,D].
     """
     rows = [(int(t), int(h)) for t, h in rows]
-    d = q.shape[-1]
+    d = k.shape[-1]
     pos = segments.local_positions() if position_ids is None else np.asarray(position_ids)
     tok = np.array([t for t, _ in rows], dtype=np.int64)
-    head = np.array([h for _, h in rows], dtype=np.int64)
-    q_sel = np.asarray(q, dtype=np.float64)[tok, head][:, None, :]       # [R,1,D]
     if use_rope:
         kc, ks = rope_cos_sin(theta, d, pos)
         qc, qs = kc[tok], ks[tok]
     else:
         kc = ks = qc = qs = None
-    q_hat = _q_rows(q_sel, eps, q_gain, gain_center, query_scale, use_rope, qc, qs)
+    q_hat = _q_rows(np.asarray(q_rows, dtype=np.float64), eps, q_gain, gain_center, query_scale,
+                    use_rope, qc, qs)
     k1, _ = rms_norm(k, eps, k_gain, gain_center)
     k_hat = rope_rotate(k1, kc[:, None, :], ks[:, None, :]) if use_rope else k1
-    num_heads = q.shape[1]
     o, lse = attention_rows(q_hat, k_hat, v, segments, rows, num_heads=num_heads,
                             window=window, scaling=scaling)
-    g_sel = np.asarray(gate, dtype=np.float64)[tok, head]
-    out, o_rstd = out_norm_gate(o, g_sel, out_eps)
+    out, o_rstd = out_norm_gate(o, np.asarray(gate_rows, dtype=np.float64), out_eps)
     return dict(q_hat=q_hat, k_hat=k_hat, o=o, lse=lse, o_rstd=o_rstd, out=out)
 
 
 def _q_rows(q_sel, eps, q_gain, gain_center, query_scale, use_rope, cos, sin):
-    q1, _ = rms_norm(q_sel[:, 0, :], eps, q_gain, gain_center)
+    q1, _ = rms_norm(q_sel, eps, q_gain, gain_center)
     q1 = round_bf16(q1 * np.float64(round_f32(query_scale)))
     if use_rope:
         q1 = rope_rotate(q1, cos, sin)

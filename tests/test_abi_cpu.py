@@ -1,0 +1,145 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before enqueuing
+anything.  Every call here fails host validation by construction (fake
+pointers are never dereferenced), so no kernel is launched."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import decoder_attention_qk_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muse_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muse_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(m.symbols) == _declared_functions()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m.library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", m.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (muse_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(_declared_functions()) <= exported
+
+
+def test_status_strings_and_version():
+    assert m.muse_status_string(0) == "MUSE_OK"
+    assert m.muse_status_string(1) == "MUSE_ERR_INVALID_ARG"
+    assert m.muse_status_string(2) == "MUSE_ERR_UNSUPPORTED"
+    assert m.muse_status_string(3) == "MUSE_ERR_DEVICE"
+    assert re.fullmatch(r"\d+\.\d+\.\d+", m.muse_version())
+
+
+@pytest.mark.parametrize("cu,nseg,total,maxlen,ok", [
+    ([0, 3, 5], 2, 5, 3, True),
+    ([0, 0, 4, 4], 3, 4, 4, True),              # empty documents are allowed
+    ([0], 0, 0, 0, False),                      # no segment
+    ([1, 3, 5], 2, 5, 3, False),                # must start at 0
+    ([0, 3, 2], 2, 2, 3, False),                # decreasing
+    ([0, 3, 5], 2, 6, 3, False),                # last != total
+    ([0, 3, 8], 2, 8, 4, False),                # a segment longer than max_seqlen
+])
+def test_validate_cu_seqlens(cu, nseg, total, maxlen, ok):
+    status = m.muse_validate_cu_seqlens(cu, nseg, total, maxlen)
+    assert (status == 0) == ok
+    if not ok:
+        assert status == 1 and m.library().muse_last_error().decode()
+
+
+FAKE = 0x7F0000000000   # a host-side stand-in address; validation never dereferences it
+
+
+def _params(**kw):
+    p = dict(head_dim=128, num_heads=8, num_key_value_heads=2, sliding_window=0, use_rope=1,
+             upcast_rope=1, scaling=128 ** -0.5, query_scale=1.0, qk_eps=1e-6, out_eps=1e-6,
+             gain_center=1.0)
+    p.update(kw)
+    return m.c_params(**p)
+
+
+def _bshd(batch=1, seqlen=16):
+    return m.c_layout(batch, seqlen, None, batch, 0, 0, None)
+
+
+def _attn(p, lay, q=FAKE, k=FAKE + (1 << 24), v=FAKE + (2 << 24), o=FAKE + (3 << 24), lse=None):
+    return m.library().muse_gqa_attn_fwd(ctypes.byref(p) if p is not None else None,
+                                         ctypes.byref(lay) if lay is not None else None,
+                                         q, k, v, o, lse, None)
+
+
+def test_null_params_and_layout():
+    assert _attn(None, _bshd()) == 1
+    assert _attn(_params(), None) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=0), 1), (dict(head_dim=127), 1), (dict(num_heads=0), 1),
+    (dict(num_heads=6, num_key_value_heads=4), 1), (dict(scaling=0.0), 1),
+    (dict(scaling=float("nan")), 1), (dict(qk_eps=-1.0), 1), (dict(out_eps=float("inf")), 1),
+    (dict(query_scale=float("inf")), 1), (dict(gain_center=float("nan")), 1),
+    (dict(head_dim=96), 2), (dict(head_dim=256), 2), (dict(upcast_rope=0), 2),
+])
+def test_bad_params(kw, status):
+    assert _attn(_params(**kw), _bshd()) == status
+    assert m.library().muse_last_error().decode()
+
+
+def test_bad_layouts():
+    assert _attn(_params(), _bshd(-1, 4)) == 1
+    thd = m.c_layout(0, 0, FAKE + (9 << 24), 0, 10, 10, None)       # no segment
+    assert _attn(_params(), thd) == 1
+    thd = m.c_layout(0, 0, FAKE + (9 << 24), 2, 10, 11, None)       # max_seqlen > total
+    assert _attn(_params(), thd) == 1
+    thd = m.c_layout(0, 0, FAKE + (9 << 24), 2, 10, 0, None)        # max_seqlen 0 with tokens
+    assert _attn(_params(), thd) == 1
+
+
+def test_missing_and_overlapping_buffers():
+    assert _attn(_params(), _bshd(), q=None) == 1
+    assert _attn(_params(), _bshd(), o=None) == 1
+    # o overlapping q (same base) and lse overlapping o
+    assert _attn(_params(), _bshd(), o=FAKE) == 1
+    assert "overlaps" in m.library().muse_last_error().decode()
+    assert _attn(_params(), _bshd(), lse=FAKE + (3 << 24) + 64) == 1
+
+
+def test_qk_norm_rope_argument_rules():
+    lib = m.library()
+    p, lay = _params(), _bshd()
+    base = [FAKE, FAKE + (1 << 24), None, None, FAKE + (2 << 24), FAKE + (3 << 24), 16,
+            FAKE + (4 << 24), FAKE + (5 << 24), None, None]
+
+    def call(**over):
+        a = dict(zip(["q", "k", "qg", "kg", "cos", "sin", "npos", "qo", "ko", "qr", "kr"], base))
+        a.update(over)
+        return lib.muse_qk_norm_rope(ctypes.byref(p), ctypes.byref(lay), a["q"], a["k"], a["qg"],
+                                     a["kg"], a["cos"], a["sin"], a["npos"], a["qo"], a["ko"],
+                                     a["qr"], a["kr"], None)
+    assert call(q=None, qo=None, k=None, ko=None) == 1     # nothing to do
+    assert call(qo=None) == 1                              # input without output
+    assert call(cos=None) == 1                             # rope without table
+    assert call(npos=8) == 1                               # table shorter than the row
+    assert call(qo=FAKE + 100) == 1                        # output overlaps input
+
+
+def test_rope_table_argument_rules():
+    lib = m.library()
+    assert lib.muse_rope_cos_sin(0.0, 64, 4, FAKE, FAKE + 4096, None) == 1
+    assert lib.muse_rope_cos_sin(1e4, 63, 4, FAKE, FAKE + 4096, None) == 1
+    assert lib.muse_rope_cos_sin(1e4, 64, -1, FAKE, FAKE + 4096, None) == 1
+    assert lib.muse_rope_cos_sin(1e4, 64, 4, None, FAKE, None) == 1
+    assert lib.muse_rope_cos_sin(1e4, 64, 4, FAKE, FAKE + 64, None) == 1   # overlapping outputs

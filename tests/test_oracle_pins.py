@@ -451,7 +451,9 @@ def test_core_rows_match_full_core():
     seg = O.Segments.thd(cu)
     full = O.attn_core(q, k, v, gate, seg, **kw)
     rows = [(0, 0), (16, 5), (17, 2), (56, 3), (cu[2] + 8, 1), (30, 4)]
-    part = O.attn_core_rows(q, k, v, gate, seg, rows, **kw)
+    tok = [t for t, _ in rows]
+    hd = [h for _, h in rows]
+    part = O.attn_core_rows(q[tok, hd], k, v, gate[tok, hd], seg, rows, num_heads=hq, **kw)
     for r, (t, h) in enumerate(rows):
         np.testing.assert_array_equal(part["out"][r], full["out"][t, h])
         np.testing.assert_array_equal(part["q_hat"][r], full["q_hat"][t, h])

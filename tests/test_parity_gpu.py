@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path (through the C ABI) against the FP64 oracle.
+
+Small cases compare every element and span several tiles, ragged tails,
+windows, packed segments (including empty and length-1 ones) and GQA group
+sizes 1..16.  Stage tests feed the oracle the GPU's own bf16 stage inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decoder_attention_qk_amd as m
+import oracle as O
+import workloads as W
+from gpu_util import (BF16_TOL, EPS, bits_f64, check_bf16, check_fp32, dev_bf16, f64, make_case)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    W.WORKLOADS["bshd_1x128_h4kv1_d64"],
+    W.small_workload("bshd_b2_s200_g4", num_heads=8, num_kv_heads=2, head_dim=128, batch=2, seqlen=200),
+    W.small_workload("bshd_s300_g5_w37", num_heads=5, num_kv_heads=1, head_dim=128, seqlen=300, window=37),
+    W.small_workload("bshd_s130_g1_d64", num_heads=2, num_kv_heads=2, head_dim=64, seqlen=130),
+    W.small_workload("bshd_s257_g8_w64", num_heads=16, num_kv_heads=2, head_dim=128, seqlen=257, window=64),
+    W.small_workload("thd_g3_mixed", num_heads=6, num_kv_heads=2, head_dim=128,
+                     segment_lengths=(1, 77, 0, 300, 64, 65)),
+    W.small_workload("thd_g5_w100", num_heads=40, num_kv_heads=8, head_dim=128,
+                     segment_lengths=(500, 3, 129), window=100, theta=5.0e5),
+    W.small_workload("bshd_norope_d64", num_heads=4, num_kv_heads=4, head_dim=64, seqlen=160,
+                     use_rope=False),
+    W.small_workload("bshd_g16_d64", num_heads=16, num_kv_heads=1, head_dim=64, seqlen=100),
+    W.small_workload("bshd_g12_w1", num_heads=12, num_kv_heads=1, head_dim=128, seqlen=90, window=1),
+    W.small_workload("bshd_g2_s96_w500", num_heads=4, num_kv_heads=2, head_dim=128, seqlen=96, window=500),
+]
+IDS = [w.name for w in SMALL]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.library()
+
+
+def _oracle_full(case):
+    return O.attn_core(bits_f64(case.x["q"]), bits_f64(case.x["k"]), bits_f64(case.x["v"]),
+                       bits_f64(case.x["gate"]), case.segs, **case.oracle_kw())
+
+
+# ---------------------------------------------------------------- RoPE table
+
+@pytest.mark.parametrize("theta,d,n_pos", [(1.0e4, 64, 128), (5.0e5, 128, 4096), (5.0e5, 128, 32768)])
+def test_rope_table(theta, d, n_pos):
+    cos, sin = m.muse_rope_cos_sin(theta, d, n_pos)
+    torch.cuda.synchronize()
+    rc, rs = O.rope_cos_sin(theta, d, np.arange(n_pos))
+    gc, gs = f64(cos), f64(sin)
+    # the same binary32 angle, cos/sin rounded once from double: equal up to
+    # rare double-rounding cases (at most 1 ulp, at most a handful of entries)
+    for g, r in ((gc, rc), (gs, rs)):
+        diff = g != r
+        assert diff.sum() <= max(2, g.size // 1_000_000)
+        if diff.any():
+            ulp = np.spacing(np.abs(r[diff]).astype(np.float32)).astype(np.float64)
+            assert np.all(np.abs(g[diff] - r[diff]) <= ulp)
+
+
+# ---------------------------------------------------------------- stage parity
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_qk_norm_rope_stage(w):
+    case = make_case(w, query_scale=0.75 if w.name == "bshd_b2_s200_g4" else 1.0)
+    q_hat, k_hat, q_rstd, k_rstd = m.muse_qk_norm_rope(
+        case.params, case.layout, case.q, case.k, case.q_gain, case.k_gain, case.cos, case.sin,
+        want_rstd=True)
+    torch.cuda.synchronize()
+    kw = case.oracle_kw()
+    pos = case.segs.local_positions()
+    c = s = None
+    if kw["use_rope"]:
+        c, s = O.rope_cos_sin(w.theta, w.head_dim, pos)
+    rq, rk, rqr, rkr = O.qk_norm_rope(bits_f64(case.x["q"]), bits_f64(case.x["k"]), eps=EPS,
+                                      q_gain=kw["q_gain"], k_gain=kw["k_gain"],
+                                      query_scale=kw["query_scale"], use_rope=kw["use_rope"],
+                                      cos=c, sin=s)
+    sq = check_bf16(f64(q_hat), rq, what="q_hat")
+    sk = check_bf16(f64(k_hat), rk, what="k_hat")
+    assert sq["exact"] > 0.999 and sk["exact"] > 0.999, (sq, sk)
+    check_fp32(f64(q_rstd), rqr, what="q_rstd")
+    check_fp32(f64(k_rstd), rkr, what="k_rstd")
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_attention_stage(w):
+    case = make_case(w)
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, case.layout, case.q, case.k, case.q_gain,
+                                             case.k_gain, case.cos, case.sin)
+    o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs,
+                         window=case.x["window"], scaling=case.scaling)
+    check_bf16(f64(o), ro, what="o")
+    check_fp32(f64(lse), rl, floor=1.0, what="lse")
+
+
+@pytest.mark.parametrize("w", SMALL[:4], ids=IDS[:4])
+def test_out_norm_gate_stage(w):
+    case = make_case(w)
+    o_bits = W.draw_bf16(tuple(case.q.shape), 0.3, seed=1, workload=w.name, layer=0, tensor="o")
+    o = dev_bf16(o_bits)
+    out, rstd = m.muse_out_norm_gate(case.params, case.layout, o, case.gate, want_rstd=True)
+    torch.cuda.synchronize()
+    rout, rr = O.out_norm_gate(bits_f64(o_bits), bits_f64(case.x["gate"]), EPS)
+    st = check_bf16(f64(out), rout, what="out")
+    assert st["exact"] > 0.999, st
+    check_fp32(f64(rstd), rr, what="o_rstd")
+
+
+# ---------------------------------------------------------------- end to end
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_fused_core_matches_oracle_and_unfused_chain(w):
+    case = make_case(w)
+    out, k_hat_f, lse_f = m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v,
+                                               case.gate, case.q_gain, case.k_gain, case.cos,
+                                               case.sin, want_lse=True)
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, case.layout, case.q, case.k, case.q_gain,
+                                             case.k_gain, case.cos, case.sin)
+    o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    out_u, _ = m.muse_out_norm_gate(case.params, case.layout, o, case.gate)
+    torch.cuda.synchronize()
+    ref = _oracle_full(case)
+    check_bf16(f64(out), ref["out"], what="fused out")
+    # lse is an FP32 intermediate: judged on the GPU's own bf16 q_hat/k_hat
+    _, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs,
+                        window=case.x["window"], scaling=case.scaling)
+    check_fp32(f64(lse_f), rl, floor=1.0, what="fused lse")
+    # fused == unfused chain, bit for bit
+    assert torch.equal(k_hat_f.view(torch.int16), k_hat.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), out_u.view(torch.int16))
+    assert torch.equal(lse_f, lse)
+
+
+# ---------------------------------------------------------------- bit-exact invariants
+
+def test_window_one_returns_v_exactly():
+    w = W.small_workload("w1", num_heads=8, num_kv_heads=2, head_dim=128, batch=2, seqlen=150, window=1)
+    case = make_case(w)
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, case.layout, case.q, case.k, case.q_gain,
+                                             case.k_gain, case.cos, case.sin)
+    o, _ = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v)
+    torch.cuda.synchronize()
+    rep = case.v.repeat_interleave(4, dim=1)
+    assert torch.equal(o.view(torch.int16), rep.view(torch.int16))
+
+
+def test_rope_position_zero_is_identity():
+    w = W.small_workload("p0", num_heads=4, num_kv_heads=2, head_dim=128, segment_lengths=(5, 9, 1))
+    case = make_case(w)
+    a = m.muse_qk_norm_rope(case.params, case.layout, case.q, case.k, case.q_gain, case.k_gain,
+                            case.cos, case.sin)
+    p2 = m.AttnParams(**{**case.params.__dict__, "use_rope": False})
+    b = m.muse_qk_norm_rope(p2, case.layout, case.q, case.k, case.q_gain, case.k_gain)
+    torch.cuda.synchronize()
+    for start in (0, 5, 14):            # first token of each segment has position 0
+        assert torch.equal(a[0][start].view(torch.int16), b[0][start].view(torch.int16))
+        assert torch.equal(a[1][start].view(torch.int16), b[1][start].view(torch.int16))
+    assert not torch.equal(a[0][1].view(torch.int16), b[0][1].view(torch.int16))
+
+
+def test_gate_zero_halves_gate_forty():
+    w = SMALL[1]
+    case = make_case(w)
+    o = dev_bf16(W.draw_bf16(tuple(case.q.shape), 1.0, seed=2, workload=w.name, layer=0, tensor="o"))
+    half, _ = m.muse_out_norm_gate(case.params, case.layout, o, torch.zeros_like(case.gate))
+    one, _ = m.muse_out_norm_gate(case.params, case.layout, o, torch.full_like(case.gate, 40.0))
+    torch.cuda.synchronize()
+    assert torch.equal(half.float() * 2, one.float())
+
+
+def test_thd_equals_per_segment_bshd():
+    lens = (70, 1, 129, 64)
+    w = W.small_workload("thd_eq", num_heads=8, num_kv_heads=2, head_dim=128, segment_lengths=lens,
+                         window=50)
+    case = make_case(w)
+    out, _, lse = m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v, case.gate,
+                                       case.q_gain, case.k_gain, case.cos, case.sin, want_lse=True)
+    s0 = 0
+    for n in lens:
+        sl = slice(s0, s0 + n)
+        lay = m.Layout.bshd(1, n)
+        o1, _, l1 = m.muse_attn_core_fwd(case.params, lay, case.q[sl].contiguous(),
+                                         case.k[sl].contiguous(), case.v[sl].contiguous(),
+                                         case.gate[sl].contiguous(), case.q_gain, case.k_gain,
+                                         case.cos, case.sin, want_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), out[sl].view(torch.int16))
+        assert torch.equal(l1, lse[sl])
+        s0 += n
+
+
+def test_explicit_position_ids_match_oracle():
+    w = W.small_workload("posids", num_heads=4, num_kv_heads=1, head_dim=128, batch=2, seqlen=70)
+    case = make_case(w)
+    pos = (np.arange(140) % 70 + 1000).astype(np.int32)
+    pos[75] = 5
+    cos, sin = m.muse_rope_cos_sin(w.theta, 128, 2048)
+    lay = m.Layout.bshd(2, 70, position_ids=torch.from_numpy(pos).cuda())
+    out, _, _ = m.muse_attn_core_fwd(case.params, lay, case.q, case.k, case.v, case.gate,
+                                     case.q_gain, case.k_gain, cos, sin)
+    torch.cuda.synchronize()
+    ref = O.attn_core(bits_f64(case.x["q"]), bits_f64(case.x["k"]), bits_f64(case.x["v"]),
+                      bits_f64(case.x["gate"]), case.segs, position_ids=pos, **case.oracle_kw())
+    check_bf16(f64(out), ref["out"], what="out with position_ids")
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_empty_inputs_are_noops():
+    p = m.AttnParams(head_dim=128, num_heads=4, num_key_value_heads=1)
+    e = torch.empty((0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    ek = torch.empty((0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    lay = m.Layout.bshd(0, 16)
+    cos, sin = m.muse_rope_cos_sin(5e5, 128, 16)
+    out, _, _ = m.muse_attn_core_fwd(p, lay, e, ek, ek, e, None, None, cos, sin)
+    assert out.shape == (0, 4, 128)
+    cu = torch.zeros(3, dtype=torch.int32, device="cuda")
+    out, _, _ = m.muse_attn_core_fwd(p, m.Layout.thd(cu, 0, total_tokens=0), e, ek, ek, e, None,
+                                     None, cos, sin)
+    torch.cuda.synchronize()
+
+
+def test_outputs_stay_inside_their_buffers_and_runs_are_deterministic():
+    w = SMALL[6]
+    case = make_case(w)
+    n, hq, d = case.q.shape
+    guard = 4096
+    big = torch.full((n * hq * d + 2 * guard,), 12345, dtype=torch.int16, device="cuda")
+    lse_big = torch.full((n * hq + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    kbig = torch.full((case.k.numel() + 2 * guard,), -3, dtype=torch.int16, device="cuda")
+    out = big[guard:guard + n * hq * d].view(torch.bfloat16).view(n, hq, d)
+    lse = lse_big[guard:guard + n * hq].view(n, hq)
+    kh = kbig[guard:guard + case.k.numel()].view(torch.bfloat16).view(case.k.shape)
+    m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v, case.gate, case.q_gain,
+                         case.k_gain, case.cos, case.sin, out=out, lse=lse, k_hat_out=kh)
+    torch.cuda.synchronize()
+    assert torch.all(big[:guard] == 12345) and torch.all(big[-guard:] == 12345)
+    assert torch.all(lse_big[:guard] == 7.0) and torch.all(lse_big[-guard:] == 7.0)
+    assert torch.all(kbig[:guard] == -3) and torch.all(kbig[-guard:] == -3)
+    out2, _, lse2 = m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v, case.gate,
+                                         case.q_gain, case.k_gain, case.cos, case.sin, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+
+
+def test_invalid_arguments_raise():
+    case = make_case(SMALL[0])
+    with pytest.raises(m.MuseError):
+        m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v, case.gate,
+                             case.q_gain, case.k_gain, case.cos, case.sin, out=case.q)
+    bad = m.AttnParams(**{**case.params.__dict__, "head_dim": 96})
+    with pytest.raises(m.MuseError) as ei:
+        m.muse_gqa_attn_fwd(bad, case.layout, case.q, case.k, case.v)
+    assert ei.value.status == m.MUSE_ERR_UNSUPPORTED
