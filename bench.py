@@ -116,10 +116,12 @@ class Bench:
 
 
 def measure_stages(b: Bench, iters: int = 5) -> dict:
-    """Unfused stages, each timed alone after a 512 MiB write that evicts the
-    256 MB Infinity Cache, so the HBM-bound kernels are charged HBM traffic."""
+    """Unfused stages, each timed alone after reading a 512 MiB buffer, which
+    refills the 256 MB Infinity Cache with clean unrelated lines, so the
+    HBM-bound kernels are charged HBM traffic (a write-based flush would leave
+    dirty lines for the measured kernel to write back)."""
     torch, m, w = b.torch, b.m, b.w
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=b.dev)
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=b.dev)
     t = b.layers[0]
     cos, sin = (b.cos, b.sin) if t["params"].use_rope else (None, None)
     q_hat, k_hat = torch.empty_like(t["q"]), torch.empty_like(t["k"])
@@ -129,7 +131,7 @@ def measure_stages(b: Bench, iters: int = 5) -> dict:
     def timed(fn):
         ts = []
         for _ in range(iters + 1):
-            flush.zero_()
+            flush.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()

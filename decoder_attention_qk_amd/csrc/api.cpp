@@ -115,8 +115,9 @@ muse_status check_layout(const muse_layout *l, const muse_attn_params *p, hipStr
     g->nseg = l->batch;
     g->maxlen = l->seqlen;
   }
-  if (g->n_tokens > INT32_MAX / 2)
-    return set_error(MUSE_ERR_UNSUPPORTED, "%lld tokens exceed the 2^30 token limit", (long long)g->n_tokens);
+  if (g->n_tokens * (g->hq + g->hkv) > INT32_MAX)
+    return set_error(MUSE_ERR_UNSUPPORTED, "%lld tokens x %d heads exceed the 2^31 row limit",
+                     (long long)g->n_tokens, g->hq + g->hkv);
   return MUSE_OK;
 }
 
@@ -124,6 +125,7 @@ TokenLayout token_layout(const muse_layout *l, const Geometry &g) {
   TokenLayout t;
   t.n_tokens = (int32_t)g.n_tokens;
   t.seqlen = g.thd ? 0 : l->seqlen;
+  t.seqlen_div = FastDiv(g.thd || l->seqlen < 1 ? 1u : (uint32_t)l->seqlen);
   t.cu_seqlens = g.thd ? l->cu_seqlens : nullptr;
   t.num_segments = g.nseg;
   t.position_ids = l->position_ids;
@@ -152,12 +154,16 @@ muse_status device_status(hipError_t e, const char *what) {
   return MUSE_OK;
 }
 
-void attn_shape(int group, int *heads_per_wg, int *tok_blocks, int *head_chunks) {
+// Workgroup shape: a workgroup holds a fixed number of (token, head) query
+// columns; its heads are the largest divisor of the KV group size that fits,
+// and as many whole tokens as the columns allow.
+void attn_shape(int group, int *heads_per_wg, int *tok_per_wg, int *head_chunks) {
+  const int cols = attn_columns_per_workgroup();
   int h = 1;
-  for (int d = group < 8 ? group : 8; d >= 1; --d)
+  for (int d = group < cols ? group : cols; d >= 1; --d)
     if (group % d == 0) { h = d; break; }
   *heads_per_wg = h;
-  *tok_blocks = h >= 4 ? 1 : 4 / h;
+  *tok_per_wg = cols / h;
   *head_chunks = group / h;
 }
 
@@ -171,13 +177,13 @@ AttnArgs attn_args(const muse_attn_params *p, const muse_layout *l, const Geomet
   a.use_rope = p->use_rope ? 1 : 0;
   a.scaling = p->scaling;
   a.scale_log2 = p->scaling * 1.4426950408889634f;
+  a.rescale_slack = kRescaleSlackLog2 / a.scale_log2;
   a.hq = g.hq;
   a.hkv = g.hkv;
   a.group = g.group;
-  attn_shape(g.group, &a.heads_per_wg, &a.tok_blocks, &a.head_chunks);
+  attn_shape(g.group, &a.heads_per_wg, &a.tok_per_wg, &a.head_chunks);
   a.window = p->sliding_window > 0 ? p->sliding_window : 0;
-  const int bm = 32 * a.tok_blocks;
-  a.q_blocks = (g.maxlen + bm - 1) / bm;
+  a.q_blocks = (g.maxlen + a.tok_per_wg - 1) / a.tok_per_wg;
   a.lay = token_layout(l, g);
   return a;
 }
@@ -244,8 +250,10 @@ extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_l
   a.n_pos = n_pos;
   a.hq = g.hq;
   a.hkv = g.hkv;
-  a.q_rows = q ? N * g.hq : 0;
-  a.total_rows = a.q_rows + (k ? N * g.hkv : 0);
+  a.hq_div = FastDiv((uint32_t)g.hq);
+  a.hkv_div = FastDiv((uint32_t)g.hkv);
+  a.q_rows = q ? (int32_t)(N * g.hq) : 0;
+  a.total_rows = a.q_rows + (k ? (int32_t)(N * g.hkv) : 0);
   a.eps = p->qk_eps;
   a.gain_center = p->gain_center;
   a.query_scale = p->query_scale;

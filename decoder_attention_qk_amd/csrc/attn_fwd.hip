@@ -4,25 +4,37 @@
 // Semantics: layers page, MuseSparkAttention (scaling = head_dim^-0.5, KV
 // heads repeated to the query-head count, per-layer sliding window), model
 // page _causal_mask (window = number of visible causal keys including the
-// query), packed documents attend only inside themselves; _qk_norm_rope_core
+// query); packed documents attend only inside themselves; _qk_norm_rope_core
 // and _output_norm_gate_core for the fused prologue/epilogue.
 //
-// Work item: (row/segment, kv head, head chunk, block of 32*TB query tokens).
-// The workgroup holds HPW query heads of one KV group x TB sub-blocks of 32
-// tokens: one wave per (head, sub-block).  K and V tiles of BN = 64 keys are
-// staged once in LDS and read by every wave of the group.
+// Work item: (row/segment, kv head, head chunk, block of query tokens).  A
+// workgroup of NW = 4 waves owns 32*NW query columns; a column is a (token,
+// head) pair of the KV group, token-major, so any group size fills the
+// columns (G = 5 uses 25 tokens x 5 heads + 3 idle columns).  K and V tiles
+// of BN = 64 keys are shared by all columns through LDS.
 //
-// Layout in registers (v_mfma_f32_32x32x16_bf16, 64 lanes): each wave computes
+// Registers (v_mfma_f32_32x32x16_bf16, 64 lanes): each wave computes
 // S^T = K Q^T, so lane l owns query column n = l % 32 and key rows
-// 8*(i/4) + 4*(l/32) + i%4 of each 32-key tile.  The row max therefore needs
-// one cross-lane exchange (lanes l, l^32), the row sum none until the end, and
-// the probabilities P^T land directly in the B-operand layout of
-// O^T += V^T P^T.  V is written to LDS transposed ([d][key]) with keys
-// permuted so each lane's 8 keys of a k-step are one 16-byte read.
+// 8*(i/4) + 4*(l/32) + i%4 of each 32-key tile.  The row max needs one
+// exchange between lanes l and l^32, the row sum none until the end, and P^T
+// lands directly in the B-operand layout of O^T += V^T P^T.
 //
-// Tiles are visited from the diagonal downwards; tiles no query of the
-// workgroup can see are never loaded, tiles every query of a wave sees skip
-// the element mask.
+// LDS: K and V tiles arrive by direct global->LDS DMA (global_load_lds, 16
+// bytes per lane, one contiguous KiB per wave instruction), double-buffered:
+// the DMA of tile j+1 runs while tile j is computed, so no registers stage
+// tiles and one barrier per tile suffices.  V stays row-major; the PV A
+// operand is read with ds_read_b64_tr_b16 (within each 16-lane group, lane r
+// receives element r%4 of the 4-vectors addressed by lanes r/4 + 4j), which
+// hands lane (d, g) keys {4g..4g+3, 8+4g..8+4g+3} of a 16-key step -- the same
+// key order P^T has in the S^T accumulator.  16-byte chunks are XOR-swizzled
+// per row on the DMA source side so both read patterns avoid bank conflicts.
+//
+// Tiles are visited from the diagonal downwards; tiles no column of the
+// workgroup sees are never loaded, tiles every column of a wave sees skip the
+// element mask.  Softmax keeps a lagging reference max that moves only when a
+// tile exceeds it by kRescaleSlackLog2 (log2 units), so the O rescale runs on
+// few tiles; probabilities stay below 2^kRescaleSlackLog2 and the final
+// division by the running sum removes the reference.
 #include <cmath>
 
 #include "device_common.hpp"
@@ -32,34 +44,49 @@ namespace muse {
 
 namespace {
 
-constexpr int BN = 64;         // keys per tile
-constexpr int kMaxWaves = 8;
+constexpr int BN = 64;        // keys per tile
+constexpr int NW = 4;         // waves per workgroup
+constexpr int COLS = 32 * NW; // query columns per workgroup
 
-// Position of key `key` (0..BN-1) inside a transposed V row: within each
-// 16-key step, swap bits 2 and 3 so lane group g's keys {4g..4g+3, 8+4g..8+4g+3}
-// sit contiguously at [8g, 8g+8).
-__device__ __forceinline__ int vt_pos(int key) {
-  const int kl = key & 15;
-  return (key & ~15) | (((kl >> 2) & 1) << 3) | ((kl >> 3) << 2) | (kl & 3);
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <int D>
+struct Tile {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CHUNKS = D / 8;                    // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;       // one K or V tile
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;      // K + V
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;       // double buffered
+  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / NW;
+  static constexpr int ROWS_PER_256B = 256 / ROW_BYTES;
+  // K rows are read 16 rows x one chunk per 16-lane group: spread 16 rows over 16 slots.
+  static __device__ __forceinline__ int swz_k(int row) { return (row / ROWS_PER_256B) % CHUNKS; }
+  // V is read 4 rows x 2 chunks per 16-lane group: shift 2 chunks per row.
+  static __device__ __forceinline__ int swz_v(int row) { return 2 * (row & 3); }
+};
+
+// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
+// (dst must be the same for the whole wave).
+__device__ __forceinline__ void dma16(const void *src, lds_char *dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4 &v, int w) {
-  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+__device__ __forceinline__ void vmem_wait_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
 }
 
 template <int D, bool FUSED>
-__global__ __launch_bounds__(64 * kMaxWaves) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
+  using T = Tile<D>;
   constexpr int KS = D / 16;   // QK^T k-steps
   constexpr int DT = D / 32;   // O^T row tiles
-  constexpr int MT = BN / 32;  // S^T row tiles
   constexpr int KK = BN / 16;  // PV k-steps
-  constexpr int KSTR = D + 8;  // LDS row stride of the K tile (elements)
-  constexpr int VSTR = BN + 8; // LDS row stride of the V^T tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+  constexpr int RB = T::ROW_BYTES;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  lds_char *smem = (lds_char *)smem_raw;
 
   const int tid = threadIdx.x;
-  const int nthreads = blockDim.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int n = lane & 31;
@@ -77,31 +104,35 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_fwd_kernel(AttnArgs a) {
 
   int s0, L;
   if (a.lay.cu_seqlens) {
-    const int T = a.lay.n_tokens;
+    const int T_ = a.lay.n_tokens;
     int c0 = a.lay.cu_seqlens[seg];
     int c1 = a.lay.cu_seqlens[seg + 1];
-    c0 = min(max(c0, 0), T);
-    c1 = min(max(c1, c0), T);
+    c0 = min(max(c0, 0), T_);
+    c1 = min(max(c1, c0), T_);
     s0 = c0;
     L = c1 - c0;
   } else {
     s0 = seg * a.lay.seqlen;
     L = a.lay.seqlen;
   }
-  const int BM = 32 * a.tok_blocks;
-  const int q0 = qb * BM;
+  const int HPW = a.heads_per_wg;
+  const int BMT = a.tok_per_wg;              // tokens per workgroup
+  const int q0 = qb * BMT;
   if (q0 >= L) return;
-  const int q1 = min(q0 + BM, L);
+  const int q1 = min(q0 + BMT, L);
 
-  const int hl = wave / a.tok_blocks;
-  const int tb = wave % a.tok_blocks;
-  const int head = kvh * a.group + hc * a.heads_per_wg + hl;
-  const int q0w = q0 + tb * 32;
-  const int q1w = min(q0w + 32, L);
-  const bool wave_active = q0w < L;
-  const int qpos = q0w + n;
-  const bool qvalid = qpos < L;
-  const int64_t qrow = ((int64_t)(s0 + (qvalid ? qpos : 0)) * a.hq + head) * D;
+  // ---- this lane's column and this wave's token range
+  const int col = wave * 32 + n;
+  const int ct = col / HPW;
+  const int head = kvh * a.group + hc * HPW + (col - ct * HPW);
+  const int qpos = q0 + ct;
+  const bool qvalid = ct < BMT && qpos < L;
+  const int wcol0 = wave * 32;
+  const int wcol1 = min(wcol0 + 31, BMT * HPW - 1);
+  const bool wave_active = wcol0 < BMT * HPW && q0 + wcol0 / HPW < L;
+  const int q0w = q0 + wcol0 / HPW;
+  const int q1w = min(q0 + wcol1 / HPW + 1, q1);
+  const int64_t qrow = ((int64_t)(s0 + (qvalid ? qpos : 0)) * a.hq + (qvalid ? head : 0)) * D;
 
   // ---- Q fragment: B operand of S^T = K Q^T; lane holds d = 16 ks + 8 g + [0, 8)
   bf16x8 qf[KS];
@@ -119,7 +150,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_fwd_kernel(AttnArgs a) {
         unpack8(raw[ks], x[ks]);
         const float own = chunk_sumsq<8>(x[ks]);
         const float other = __shfl_xor(own, 32);
-        all[2 * ks] = g ? other : own;       // chunk index 2 ks + g holds d = 16 ks + 8 g
+        all[2 * ks] = g ? other : own;       // chunk 2 ks + g holds d = 16 ks + 8 g
         all[2 * ks + 1] = g ? own : other;
       }
       const float rstd = rms_rstd(tree_sum(all), 1.0f / (float)D, a.eps);
@@ -151,6 +182,58 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_fwd_kernel(AttnArgs a) {
     }
   }
 
+  // ---- per-lane DMA source offsets (elements) and LDS read addresses (bytes)
+  const int64_t kv_stride = (int64_t)a.hkv * D;
+  const uint16_t *kbase = a.k + ((int64_t)s0 * a.hkv + kvh) * D;
+  const uint16_t *vbase = a.v + ((int64_t)s0 * a.hkv + kvh) * D;
+  int dma_row[T::DMA_PER_WAVE], off_k[T::DMA_PER_WAVE], off_v[T::DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+    const int slot = (wave * T::DMA_PER_WAVE + i) * 64 + lane;
+    const int row = slot / T::CHUNKS;
+    const int pch = slot % T::CHUNKS;
+    dma_row[i] = row;
+    off_k[i] = row * (int)kv_stride + (pch ^ T::swz_k(row)) * 8;
+    off_v[i] = row * (int)kv_stride + (pch ^ T::swz_v(row)) * 8;
+  }
+  int ka[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ka[ks] = n * RB + (((2 * ks + g) ^ T::swz_k(n)) << 4);
+  int va[DT];
+  {
+    const int r = lane & 15, q = (lane >> 4) & 1;
+    const int row = 4 * g + (r >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int ch = dt * 4 + 2 * q + ((r & 3) >> 1);
+      va[dt] = row * RB + ((ch ^ T::swz_v(row)) << 4) + (r & 1) * 8;
+    }
+  }
+
+  auto issue_dma = [&](int kt, int buf) {
+    const int k0 = kt * BN;
+    lds_char *kdst = smem + buf * T::STAGE_BYTES + wave * T::DMA_PER_WAVE * 1024;
+    lds_char *vdst = kdst + T::TILE_BYTES;
+    const uint16_t *kt_base = kbase + (int64_t)k0 * kv_stride;
+    const uint16_t *vt_base = vbase + (int64_t)k0 * kv_stride;
+    if (k0 + BN <= L) {
+#pragma unroll
+      for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+        dma16(kt_base + off_k[i], kdst + i * 1024);
+        dma16(vt_base + off_v[i], vdst + i * 1024);
+      }
+    } else {
+      // ragged last tile: rows past the segment repeat its last row (finite,
+      // masked out of every score, never read outside the buffers)
+#pragma unroll
+      for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+        const int shift = (min(dma_row[i], L - 1 - k0) - dma_row[i]) * (int)kv_stride;
+        dma16(kt_base + off_k[i] + shift, kdst + i * 1024);
+        dma16(vt_base + off_v[i] + shift, vdst + i * 1024);
+      }
+    }
+  };
+
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
@@ -158,86 +241,49 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_fwd_kernel(AttnArgs a) {
   float l_run = 0.0f;
 
   const int W = a.window;
-  const int lo = W > 0 ? max(0, q0 - W + 1) : 0;
-  const int kt_lo = lo / BN;
-  const int kt_hi = (q1 - 1) / BN;
-  const int64_t kv_stride = (int64_t)a.hkv * D;
-  const uint16_t *kbase = a.k + ((int64_t)s0 * a.hkv + kvh) * D;
-  const uint16_t *vbase = a.v + ((int64_t)s0 * a.hkv + kvh) * D;
+  const float c2 = a.scale_log2;
 
-  for (int kt = kt_hi; kt >= kt_lo; --kt) {
+  // called with literal buffer indices so LDS offsets fold into immediates
+  auto compute = [&](int kt, int BUF) __attribute__((always_inline)) {
     const int k0 = kt * BN;
-    __syncthreads();  // every wave is done with the previous tile
-    for (int u = tid; u < BN * (D / 8); u += nthreads) {
-      const int row = u / (D / 8);
-      const int ch = u % (D / 8);
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (k0 + row < L) val = *reinterpret_cast<const uint4 *>(kbase + (int64_t)(k0 + row) * kv_stride + ch * 8);
-      *reinterpret_cast<uint4 *>(&Ks[row * KSTR + ch * 8]) = val;
-    }
-    for (int u = tid; u < (BN / 4) * (D / 8); u += nthreads) {
-      const int qd = u % (BN / 4);
-      const int ch = u / (BN / 4);
-      uint4 r4[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = qd * 4 + rr;
-        r4[rr] = (k0 + key < L) ? *reinterpret_cast<const uint4 *>(vbase + (int64_t)(k0 + key) * kv_stride + ch * 8)
-                                : make_uint4(0, 0, 0, 0);
-      }
-      const int pos = vt_pos(qd * 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const uint32_t wd = word_of(r4[rr], e >> 1);
-          w4[rr] = (e & 1) ? (wd >> 16) : (wd & 0xffffu);
-        }
-        uint2 out;
-        out.x = w4[0] | (w4[1] << 16);
-        out.y = w4[2] | (w4[3] << 16);
-        *reinterpret_cast<uint2 *>(&Vt[(ch * 8 + e) * VSTR + pos]) = out;
-      }
-    }
-    __syncthreads();
-    if (!wave_active) continue;
-    const bool none_visible = (k0 > q1w - 1) || (W > 0 && k0 + BN - 1 <= q0w - W);
-    if (none_visible) continue;
+    const bool none_visible = !wave_active || (k0 > q1w - 1) || (W > 0 && k0 + BN - 1 <= q0w - W);
+    if (none_visible) return;
     const bool all_visible = (k0 + BN - 1 <= q0w) && (W <= 0 || k0 > q1w - 1 - W);
+    const lds_char *Kt = smem + BUF * T::STAGE_BYTES;
+    const lds_char *Vt = Kt + T::TILE_BYTES;
 
-    f32x16 sacc[MT];
+    f32x16 s0v = f32x16{}, s1v = f32x16{};
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      sacc[mt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&Ks[(mt * 32 + n) * KSTR + ks * 16 + g * 8]);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 k0f = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks]);
+      const bf16x8 k1f = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks] + 32 * RB);
+      s0v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[ks], s0v, 0, 0, 0);
+      s1v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[ks], s1v, 0, 0, 0);
     }
     if (!all_visible) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kpos = k0 + mt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          const bool vis = kpos <= qpos && (W <= 0 || kpos > qpos - W);
-          if (!vis) sacc[mt][i] = -INFINITY;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int kp = k0 + (i >> 2) * 8 + g * 4 + (i & 3);
+        if (!(kp <= qpos && (W <= 0 || kp > qpos - W))) s0v[i] = -INFINITY;
+        if (!(kp + 32 <= qpos && (W <= 0 || kp + 32 > qpos - W))) s1v[i] = -INFINITY;
       }
     }
-
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[mt][i]);
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(s0v[i], s1v[i]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * a.scale_log2);
-    const float mc = m_use * a.scale_log2;
+    const bool grow = tmax > m_run + a.rescale_slack;
+    if (__any(grow)) {
+      // other lanes may enter with this lane still at -inf (no visible key
+      // yet): its sum and accumulator are zero, keep them (no -inf - -inf)
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c2;
     float psum = 0.0f;
     bf16x8 pb[KK];
 #pragma unroll
@@ -245,24 +291,46 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_fwd_kernel(AttnArgs a) {
       float pf[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kk >> 1][(kk & 1) * 8 + j], a.scale_log2, -mc));
-        psum += pv;
-        pf[j] = pv;
+        const float sv = (kk < 2) ? s0v[(kk & 1) * 8 + j] : s1v[(kk & 1) * 8 + j];
+        pf[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -mc));
+        psum += pf[j];
       }
       pb[kk] = __builtin_bit_cast(bf16x8, pack8(pf));
     }
-    l_run = __builtin_fmaf(l_run, alpha, psum);
-    m_run = m_new;
+    l_run += psum;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&Vt[(dt * 32 + n) * VSTR + kk * 16 + g * 8]);
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + (16 * kk) * RB));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + (16 * kk + 8) * RB));
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kk], oacc[dt], 0, 0, 0);
       }
     }
+  };
+
+  const int lo = W > 0 ? max(0, q0 - W + 1) : 0;
+  const int kt_lo = lo / BN;
+  const int kt_hi = (q1 - 1) / BN;
+  const int ntiles = kt_hi - kt_lo + 1;
+
+  issue_dma(kt_hi, 0);
+  vmem_wait_all();
+  __syncthreads();
+  for (int it = 0;;) {
+    if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 1);
+    compute(kt_hi - it, 0);
+    vmem_wait_all();
+    __syncthreads();
+    if (++it >= ntiles) break;
+    if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 0);
+    compute(kt_hi - it, 1);
+    vmem_wait_all();
+    __syncthreads();
+    if (++it >= ntiles) break;
   }
 
   if (!wave_active) return;
@@ -326,21 +394,30 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+template <int D, bool FUSED>
+hipError_t launch_one(const AttnArgs &a, dim3 grid, hipStream_t stream) {
+  constexpr int bytes = Tile<D>::LDS_BYTES;
+  // LDS beyond the 64 KiB default needs the kernel's attribute raised once.
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&attn_fwd_kernel<D, FUSED>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, FUSED>), grid, dim3(64 * NW), bytes, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int attn_columns_per_workgroup() { return COLS; }
 
 hipError_t launch_attn_fwd(int head_dim, bool fused, const AttnArgs &a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.q_blocks * a.lay.num_segments * a.hkv * a.head_chunks;
   if (blocks == 0) return hipSuccess;
+  if (a.heads_per_wg < 1 || a.heads_per_wg > COLS || a.tok_per_wg < 1 || a.tok_per_wg * a.heads_per_wg > COLS)
+    return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
-  const dim3 block(64 * a.heads_per_wg * a.tok_blocks);
-  if (head_dim == 128) {
-    if (fused) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, block, 0, stream, a);
-  } else {
-    if (fused) hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, block, 0, stream, a);
-  }
-  return hipGetLastError();
+  if (head_dim == 128)
+    return fused ? launch_one<128, true>(a, grid, stream) : launch_one<128, false>(a, grid, stream);
+  return fused ? launch_one<64, true>(a, grid, stream) : launch_one<64, false>(a, grid, stream);
 }
 
 }  // namespace muse

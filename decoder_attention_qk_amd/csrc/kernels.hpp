@@ -4,12 +4,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace muse {
+
+// Lagging-max slack of the attention softmax, in log2 units: probabilities
+// stay below 2^kRescaleSlackLog2 between rescales.
+constexpr float kRescaleSlackLog2 = 8.0f;
 
 // Where each token sits: its row/segment and its RoPE position.
 struct TokenLayout {
   int32_t n_tokens;              // N
   int32_t seqlen;                // BSHD row length (cu_seqlens == nullptr)
+  FastDiv seqlen_div;            // division by seqlen (BSHD)
   const int32_t *cu_seqlens;     // THD boundaries [num_segments + 1], or nullptr
   int32_t num_segments;          // THD segments, or BSHD batch
   const int32_t *position_ids;   // explicit RoPE positions [N], or nullptr
@@ -36,8 +43,9 @@ struct QkNormArgs {
   const float *sin_tab;
   int32_t n_pos;
   int32_t hq, hkv;
-  int64_t q_rows;          // N * Hq when q is processed, else 0
-  int64_t total_rows;      // q_rows + (k ? N * Hkv : 0)
+  FastDiv hq_div, hkv_div;
+  int32_t q_rows;          // N * Hq when q is processed, else 0
+  int32_t total_rows;      // q_rows + (k ? N * Hkv : 0); < 2^31
   float eps, gain_center, query_scale;
   int32_t use_rope;
   TokenLayout lay;
@@ -69,12 +77,13 @@ struct AttnArgs {
   // attention
   float scaling;           // softmax scale
   float scale_log2;        // scaling * log2(e)
+  float rescale_slack;     // raw-score slack before the running max moves
   int32_t hq, hkv, group;  // group = hq / hkv
   int32_t heads_per_wg;    // query heads of one kv group handled by one workgroup
   int32_t head_chunks;     // group / heads_per_wg
-  int32_t tok_blocks;      // 32-token sub-blocks per workgroup (waves = heads_per_wg * tok_blocks)
+  int32_t tok_per_wg;      // query tokens per workgroup (tok_per_wg * heads_per_wg <= columns)
   int32_t window;          // <= 0: none
-  int32_t q_blocks;        // ceil(max segment length / (32 * tok_blocks))
+  int32_t q_blocks;        // ceil(max segment length / tok_per_wg)
   TokenLayout lay;
 };
 
@@ -82,6 +91,7 @@ hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t stream);
 hipError_t launch_qk_norm_rope(int head_dim, const QkNormArgs &a, hipStream_t stream);
 hipError_t launch_out_norm_gate(int head_dim, const OutGateArgs &a, hipStream_t stream);
 hipError_t launch_attn_fwd(int head_dim, bool fused, const AttnArgs &a, hipStream_t stream);
+int attn_columns_per_workgroup();  // (token, head) query columns one attention workgroup holds
 
 // Position of token t for RoPE (clamped into the table), and its segment.
 __device__ __forceinline__ int find_segment(const TokenLayout &l, int t) {
@@ -100,7 +110,7 @@ __device__ __forceinline__ int rope_position(const TokenLayout &l, int t, int n_
   } else if (l.cu_seqlens) {
     p = t - l.cu_seqlens[find_segment(l, t)];
   } else {
-    p = t % l.seqlen;
+    p = (int)l.seqlen_div.mod((uint32_t)t);
   }
   return p < 0 ? 0 : (p >= n_pos ? n_pos - 1 : p);
 }

@@ -23,24 +23,30 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
   constexpr int RPP = kThreads / LPR;      // rows per pass of the block
   const int c = threadIdx.x % LPR;         // chunk: elements [8c, 8c+8)
   const int rsub = threadIdx.x / LPR;
-  const int64_t base = (int64_t)blockIdx.x * RPP * kRowsInFlight;
+  const int base = blockIdx.x * RPP * kRowsInFlight;
+
+  // effective gains of this lane's 8 columns (fixed for every row it touches)
+  float wq[8], wk[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    wq[e] = a.q_gain ? a.gain_center + a.q_gain[c * 8 + e] : 1.0f;
+    wk[e] = a.k_gain ? a.gain_center + a.k_gain[c * 8 + e] : 1.0f;
+  }
 
   uint4 xin[kRowsInFlight];
-  int64_t rows[kRowsInFlight];
 #pragma unroll
   for (int j = 0; j < kRowsInFlight; ++j) {
-    const int64_t r = base + (int64_t)j * RPP + rsub;
-    rows[j] = r;
+    const int r = base + j * RPP + rsub;
     xin[j] = make_uint4(0, 0, 0, 0);
     if (r < a.total_rows) {
-      const uint16_t *src = r < a.q_rows ? a.q + r * D : a.k + (r - a.q_rows) * D;
+      const uint16_t *src = r < a.q_rows ? a.q + (int64_t)r * D : a.k + (int64_t)(r - a.q_rows) * D;
       xin[j] = *reinterpret_cast<const uint4 *>(src + c * 8);
     }
   }
 
 #pragma unroll
   for (int j = 0; j < kRowsInFlight; ++j) {
-    const int64_t r = rows[j];
+    const int r = base + j * RPP + rsub;
     const bool valid = r < a.total_rows;
     const bool is_q = r < a.q_rows;
     float x[8];
@@ -50,31 +56,23 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
     for (int w = 1; w < LPR; w <<= 1) ss = ss + __shfl_xor(ss, w);
     if (!valid) continue;
     const float rstd = rms_rstd(ss, 1.0f / (float)D, a.eps);
-
-    const float *gain = is_q ? a.q_gain : a.k_gain;
-    float w[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = gain ? a.gain_center + gain[c * 8 + e] : 1.0f;
-
+    const int rr = is_q ? r : r - a.q_rows;            // row inside its own tensor
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
-    int64_t tok;
-    int heads;
-    if (is_q) { tok = r / a.hq; heads = a.hq; } else { tok = (r - a.q_rows) / a.hkv; heads = a.hkv; }
-    (void)heads;
     if (a.use_rope) {
-      const int p = rope_position(a.lay, (int)tok, a.n_pos);
-      const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)p * (D / 2) + c * 4);
-      const float4 sv = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)p * (D / 2) + c * 4);
+      const int tok = (int)(is_q ? a.hq_div.div((uint32_t)rr) : a.hkv_div.div((uint32_t)rr));
+      const int p = rope_position(a.lay, tok, a.n_pos);
+      const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + p * (D / 2) + c * 4);
+      const float4 sv = *reinterpret_cast<const float4 *>(a.sin_tab + p * (D / 2) + c * 4);
       cs[0] = cv.x; cs[1] = cv.y; cs[2] = cv.z; cs[3] = cv.w;
       sn[0] = sv.x; sn[1] = sv.y; sn[2] = sv.z; sn[3] = sv.w;
     }
     float y[8];
-    qk_chunk(x, w, rstd, is_q && a.query_scale != 1.0f, a.query_scale, a.use_rope != 0, cs, sn, y);
-    uint16_t *dst = is_q ? a.q_out + r * D : a.k_out + (r - a.q_rows) * D;
-    *reinterpret_cast<uint4 *>(dst + c * 8) = pack8(y);
+    qk_chunk(x, is_q ? wq : wk, rstd, is_q && a.query_scale != 1.0f, a.query_scale, a.use_rope != 0, cs, sn, y);
+    uint16_t *dst = is_q ? a.q_out : a.k_out;
+    *reinterpret_cast<uint4 *>(dst + (int64_t)rr * D + c * 8) = pack8(y);
     if (c == 0) {
-      if (is_q) { if (a.q_rstd) a.q_rstd[r] = rstd; }
-      else if (a.k_rstd) a.k_rstd[r - a.q_rows] = rstd;
+      float *rs = is_q ? a.q_rstd : a.k_rstd;
+      if (rs) rs[rr] = rstd;
     }
   }
 }
