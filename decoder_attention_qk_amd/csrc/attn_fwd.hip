@@ -19,8 +19,10 @@
 // exchange between lanes l and l^32, the row sum none until the end, and P^T
 // lands directly in the B-operand layout of O^T += V^T P^T.
 //
-// LDS: K and V tiles arrive by direct global->LDS DMA (global_load_lds, 16
-// bytes per lane, one contiguous KiB per wave instruction), double-buffered:
+// LDS: K and V tiles arrive by direct global->LDS DMA (buffer_load ... lds, 16
+// bytes per lane, one contiguous KiB per wave instruction; the buffer
+// resource ends at the segment's last row, so rows past it read as zeros),
+// double-buffered:
 // the DMA of tile j+1 runs while tile j is computed, so no registers stage
 // tiles and one barrier per tile suffices.  V stays row-major; the PV A
 // operand is read with ds_read_b64_tr_b16 (within each 16-lane group, lane r
@@ -62,14 +64,22 @@ struct Tile {
   static constexpr int ROWS_PER_256B = 256 / ROW_BYTES;
   // K rows are read 16 rows x one chunk per 16-lane group: spread 16 rows over 16 slots.
   static __device__ __forceinline__ int swz_k(int row) { return (row / ROWS_PER_256B) % CHUNKS; }
-  // V is read 4 rows x 2 chunks per 16-lane group: shift 2 chunks per row.
-  static __device__ __forceinline__ int swz_v(int row) { return 2 * (row & 3); }
+  // V is read 4 rows x 32 columns per half-wave: give each row its own quarter
+  // of the 256-byte bank window (XOR on 4-chunk groups).
+  static __device__ __forceinline__ int swz_v(int row) {
+    return 4 * ((row / ROWS_PER_256B) & (CHUNKS / 4 - 1));
+  }
 };
 
-// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
-// (dst must be the same for the whole wave).
-__device__ __forceinline__ void dma16(const void *src, lds_char *dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+// Buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane at byte offset voff of the buffer, straight into LDS at
+// dst + 16 * lane (dst must be the same for the whole wave).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, lds_char *dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ void vmem_wait_all() {
@@ -172,9 +182,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
           cs[0] = cv.x; cs[1] = cv.y; cs[2] = cv.z; cs[3] = cv.w;
           sn[0] = sv.x; sn[1] = sv.y; sn[2] = sv.z; sn[3] = sv.w;
         }
-        float y[8];
-        qk_chunk(x[ks], w, rstd, a.query_scale != 1.0f, a.query_scale, a.use_rope != 0, cs, sn, y);
-        qf[ks] = __builtin_bit_cast(bf16x8, pack8(y));
+        qf[ks] = __builtin_bit_cast(bf16x8, qk_chunk(x[ks], w, rstd, a.query_scale != 1.0f, a.query_scale,
+                                                     a.use_rope != 0, cs, sn));
       }
     } else {
 #pragma unroll
@@ -186,15 +195,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   const int64_t kv_stride = (int64_t)a.hkv * D;
   const uint16_t *kbase = a.k + ((int64_t)s0 * a.hkv + kvh) * D;
   const uint16_t *vbase = a.v + ((int64_t)s0 * a.hkv + kvh) * D;
-  int dma_row[T::DMA_PER_WAVE], off_k[T::DMA_PER_WAVE], off_v[T::DMA_PER_WAVE];
+  int off_k[T::DMA_PER_WAVE], off_v[T::DMA_PER_WAVE];   // byte offsets inside a tile's rows
 #pragma unroll
   for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
     const int slot = (wave * T::DMA_PER_WAVE + i) * 64 + lane;
     const int row = slot / T::CHUNKS;
     const int pch = slot % T::CHUNKS;
-    dma_row[i] = row;
-    off_k[i] = row * (int)kv_stride + (pch ^ T::swz_k(row)) * 8;
-    off_v[i] = row * (int)kv_stride + (pch ^ T::swz_v(row)) * 8;
+    off_k[i] = (row * (int)kv_stride + (pch ^ T::swz_k(row)) * 8) * 2;
+    off_v[i] = (row * (int)kv_stride + (pch ^ T::swz_v(row)) * 8) * 2;
   }
   int ka[KS];
 #pragma unroll
@@ -214,23 +222,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     const int k0 = kt * BN;
     lds_char *kdst = smem + buf * T::STAGE_BYTES + wave * T::DMA_PER_WAVE * 1024;
     lds_char *vdst = kdst + T::TILE_BYTES;
-    const uint16_t *kt_base = kbase + (int64_t)k0 * kv_stride;
-    const uint16_t *vt_base = vbase + (int64_t)k0 * kv_stride;
-    if (k0 + BN <= L) {
+    // the tile's rows k0 .. L-1 of this kv head; rows past the segment read as zeros
+    // (zero keys are masked out of every score, zero values add nothing)
+    const int valid_bytes = ((min(L - k0, BN) - 1) * (int)kv_stride + D) * 2;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)k0 * kv_stride, valid_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)k0 * kv_stride, valid_bytes);
 #pragma unroll
-      for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
-        dma16(kt_base + off_k[i], kdst + i * 1024);
-        dma16(vt_base + off_v[i], vdst + i * 1024);
-      }
-    } else {
-      // ragged last tile: rows past the segment repeat its last row (finite,
-      // masked out of every score, never read outside the buffers)
-#pragma unroll
-      for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
-        const int shift = (min(dma_row[i], L - 1 - k0) - dma_row[i]) * (int)kv_stride;
-        dma16(kt_base + off_k[i] + shift, kdst + i * 1024);
-        dma16(vt_base + off_v[i] + shift, vdst + i * 1024);
-      }
+    for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+      dma16(kr, off_k[i], kdst + i * 1024);
+      dma16(vr, off_v[i], vdst + i * 1024);
     }
   };
 
@@ -252,64 +252,83 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     const lds_char *Kt = smem + BUF * T::STAGE_BYTES;
     const lds_char *Vt = Kt + T::TILE_BYTES;
 
-    f32x16 s0v = f32x16{}, s1v = f32x16{};
+    // The tile is processed as two 32-key halves; the lagging reference max
+    // makes a per-half softmax exact.  Order: QK(h0), QK(h1), softmax(h0),
+    // PV(h0), softmax(h1), PV(h1) -- the MFMA chains of one half are
+    // independent of the other half's softmax, which another wave on the SIMD
+    // overlaps.
+    auto qk = [&](int half) __attribute__((always_inline)) {
+      f32x16 acc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 k0f = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks]);
-      const bf16x8 k1f = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks] + 32 * RB);
-      s0v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[ks], s0v, 0, 0, 0);
-      s1v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[ks], s1v, 0, 0, 0);
-    }
-    if (!all_visible) {
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks] + half * 32 * RB);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc, 0, 0, 0);
+      }
+      return acc;
+    };
+    auto softmax = [&](f32x16 &sv, int half, bf16x8 &p0, bf16x8 &p1) __attribute__((always_inline)) {
+      if (!all_visible) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kp = k0 + half * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+          if (!(kp <= qpos && (W <= 0 || kp > qpos - W))) sv[i] = -INFINITY;
+        }
+      }
+      float tmax = fmaxf(sv[0], sv[15]);
+#pragma unroll
+      for (int i = 1; i < 15; i += 2) tmax = fmaxf(tmax, fmaxf(sv[i], sv[i + 1]));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool grow = tmax > m_run + a.rescale_slack;
+      if (__any(grow)) {
+        // other lanes may enter with this lane still at -inf (no visible key
+        // yet): its sum and accumulator are zero, keep them (no -inf - -inf)
+        const float m_new = grow ? tmax : m_run;
+        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c2;
+      float pf[16];
+      float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kp = k0 + (i >> 2) * 8 + g * 4 + (i & 3);
-        if (!(kp <= qpos && (W <= 0 || kp > qpos - W))) s0v[i] = -INFINITY;
-        if (!(kp + 32 <= qpos && (W <= 0 || kp + 32 > qpos - W))) s1v[i] = -INFINITY;
+        pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c2, -mc));
+        psum += pf[i];
       }
-    }
-    float tmax = -INFINITY;
+      l_run += psum;
+      uint4 lo, hi;
+      lo.x = pack_bf16x2(pf[0], pf[1]);   lo.y = pack_bf16x2(pf[2], pf[3]);
+      lo.z = pack_bf16x2(pf[4], pf[5]);   lo.w = pack_bf16x2(pf[6], pf[7]);
+      hi.x = pack_bf16x2(pf[8], pf[9]);   hi.y = pack_bf16x2(pf[10], pf[11]);
+      hi.z = pack_bf16x2(pf[12], pf[13]); hi.w = pack_bf16x2(pf[14], pf[15]);
+      p0 = __builtin_bit_cast(bf16x8, lo);
+      p1 = __builtin_bit_cast(bf16x8, hi);
+    };
+    auto pv = [&](int half, const bf16x8 &p0, const bf16x8 &p1) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(s0v[i], s1v[i]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const bool grow = tmax > m_run + a.rescale_slack;
-    if (__any(grow)) {
-      // other lanes may enter with this lane still at -inf (no visible key
-      // yet): its sum and accumulator are zero, keep them (no -inf - -inf)
-      const float m_new = grow ? tmax : m_run;
-      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      l_run *= alpha;
+      for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      m_run = m_new;
-    }
-    const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c2;
-    float psum = 0.0f;
-    bf16x8 pb[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      float pf[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float sv = (kk < 2) ? s0v[(kk & 1) * 8 + j] : s1v[(kk & 1) * 8 + j];
-        pf[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -mc));
-        psum += pf[j];
+        for (int dt = 0; dt < DT; ++dt) {
+          const int r0 = (half * 32 + 16 * kk) * RB;
+          const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0));
+          const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0 + 8 * RB));
+          const bf16x8 vf = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, kk ? p1 : p0, oacc[dt], 0, 0, 0);
+        }
       }
-      pb[kk] = __builtin_bit_cast(bf16x8, pack8(pf));
-    }
-    l_run += psum;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + (16 * kk) * RB));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + (16 * kk + 8) * RB));
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kk], oacc[dt], 0, 0, 0);
-      }
-    }
+    };
+
+    f32x16 s0v = qk(0);
+    f32x16 s1v = qk(1);
+    bf16x8 pa0, pa1, pb0, pb1;
+    softmax(s0v, 0, pa0, pa1);
+    pv(0, pa0, pa1);
+    softmax(s1v, 1, pb0, pb1);
+    pv(1, pb0, pb1);
   };
 
   const int lo = W > 0 ? max(0, q0 - W + 1) : 0;

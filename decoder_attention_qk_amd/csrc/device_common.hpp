@@ -88,26 +88,24 @@ __device__ __forceinline__ float rms_rstd(float sumsq, float inv_d, float eps) {
 // Q/K norm + query scale + RoPE on one chunk of 8 consecutive elements
 // (4 adjacent pairs).  x: inputs; w: effective gains; c, s: cos/sin of the 4
 // pairs (ignored when !rope); qscale applied (with its own bf16 cast) when
-// apply_qscale.  Writes the rotated bf16 values into y.
+// apply_qscale.  Returns the 8 rotated values as packed bf16.  Each pair is
+// rounded with one packed conversion; the rounded values feed the next step.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void qk_chunk(const float (&x)[8], const float (&w)[8], float r,
-                                         bool apply_qscale, float qscale, bool rope,
-                                         const float (&c)[4], const float (&s)[4],
-                                         float (&y)[8]) {
+__device__ __forceinline__ uint4 qk_chunk(const float (&x)[8], const float (&w)[8], float r,
+                                          bool apply_qscale, float qscale, bool rope,
+                                          const float (&c)[4], const float (&s)[4]) {
+  uint32_t out[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float t = round_bf16((x[e] * r) * w[e]);
-    if (apply_qscale) t = round_bf16(t * qscale);
-    y[e] = t;
-  }
-  if (rope) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = y[2 * i], b = y[2 * i + 1];
-      y[2 * i] = round_bf16(__builtin_fmaf(a, c[i], -(b * s[i])));
-      y[2 * i + 1] = round_bf16(__builtin_fmaf(a, s[i], b * c[i]));
+  for (int i = 0; i < 4; ++i) {
+    uint32_t p = pack_bf16x2((x[2 * i] * r) * w[2 * i], (x[2 * i + 1] * r) * w[2 * i + 1]);
+    if (apply_qscale) p = pack_bf16x2(bf16_lo(p) * qscale, bf16_hi(p) * qscale);
+    if (rope) {
+      const float a = bf16_lo(p), b = bf16_hi(p);
+      p = pack_bf16x2(__builtin_fmaf(a, c[i], -(b * s[i])), __builtin_fmaf(a, s[i], b * c[i]));
     }
+    out[i] = p;
   }
+  return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
 // ---------------------------------------------------------------------------

@@ -66,10 +66,10 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
       cs[0] = cv.x; cs[1] = cv.y; cs[2] = cv.z; cs[3] = cv.w;
       sn[0] = sv.x; sn[1] = sv.y; sn[2] = sv.z; sn[3] = sv.w;
     }
-    float y[8];
-    qk_chunk(x, is_q ? wq : wk, rstd, is_q && a.query_scale != 1.0f, a.query_scale, a.use_rope != 0, cs, sn, y);
+    const uint4 y = qk_chunk(x, is_q ? wq : wk, rstd, is_q && a.query_scale != 1.0f, a.query_scale,
+                             a.use_rope != 0, cs, sn);
     uint16_t *dst = is_q ? a.q_out : a.k_out;
-    *reinterpret_cast<uint4 *>(dst + (int64_t)rr * D + c * 8) = pack8(y);
+    *reinterpret_cast<uint4 *>(dst + (int64_t)rr * D + c * 8) = y;
     if (c == 0) {
       float *rs = is_q ? a.q_rstd : a.k_rstd;
       if (rs) rs[rr] = rstd;
