@@ -28,6 +28,7 @@ struct Range {
   const void *p;
   int64_t bytes;
   const char *name;
+  int align = 16;  // bytes; the kernels move bf16 and fp32 tensors in 16-byte vectors
 };
 
 bool ranges_overlap(const Range &a, const Range &b) {
@@ -36,8 +37,13 @@ bool ranges_overlap(const Range &a, const Range &b) {
   return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
 }
 
-// Each output must not overlap any input or any other output.
+// Every given pointer must be aligned as its range requires, and each output
+// must not overlap any input or any other output.
 muse_status check_disjoint(const std::vector<Range> &inputs, const std::vector<Range> &outputs) {
+  for (const auto *list : {&inputs, &outputs})
+    for (const Range &r : *list)
+      if (r.p && ((uintptr_t)r.p % (uintptr_t)r.align) != 0)
+        return set_error(MUSE_ERR_INVALID_ARG, "%s is not %d-byte aligned", r.name, r.align);
   for (size_t i = 0; i < outputs.size(); ++i) {
     for (const Range &in : inputs)
       if (ranges_overlap(outputs[i], in))
@@ -133,8 +139,8 @@ TokenLayout token_layout(const muse_layout *l, const Geometry &g) {
 }
 
 Range layout_range(const muse_layout *l, const Geometry &g, int which) {
-  if (which == 0) return Range{g.thd ? l->cu_seqlens : nullptr, ((int64_t)g.nseg + 1) * 4, "cu_seqlens"};
-  return Range{l->position_ids, g.n_tokens * 4, "position_ids"};
+  if (which == 0) return Range{g.thd ? l->cu_seqlens : nullptr, ((int64_t)g.nseg + 1) * 4, "cu_seqlens", 4};
+  return Range{l->position_ids, g.n_tokens * 4, "position_ids", 4};
 }
 
 muse_status check_rope_table(const muse_attn_params *p, const muse_layout *l, const Geometry &g,
@@ -232,7 +238,7 @@ extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_l
        {k_gain, g.d * 4, "k_gain"}, {cos, tab, "cos"}, {sin, tab, "sin"}, layout_range(l, g, 0),
        layout_range(l, g, 1)},
       {{q_out, bf16_bytes(N, g.hq, g.d), "q_out"}, {k_out, bf16_bytes(N, g.hkv, g.d), "k_out"},
-       {q_rstd, N * g.hq * 4, "q_rstd"}, {k_rstd, N * g.hkv * 4, "k_rstd"}});
+       {q_rstd, N * g.hq * 4, "q_rstd", 4}, {k_rstd, N * g.hkv * 4, "k_rstd", 4}});
   if (s != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
   QkNormArgs a;
@@ -274,7 +280,7 @@ extern "C" muse_status muse_gqa_attn_fwd(const muse_attn_params *p, const muse_l
     return set_error(MUSE_ERR_INVALID_ARG, "q_hat, k_hat, v and o are required");
   s = check_disjoint({{q_hat, bf16_bytes(N, g.hq, g.d), "q_hat"}, {k_hat, bf16_bytes(N, g.hkv, g.d), "k_hat"},
                       {v, bf16_bytes(N, g.hkv, g.d), "v"}, layout_range(l, g, 0), layout_range(l, g, 1)},
-                     {{o, bf16_bytes(N, g.hq, g.d), "o"}, {lse, N * g.hq * 4, "lse"}});
+                     {{o, bf16_bytes(N, g.hq, g.d), "o"}, {lse, N * g.hq * 4, "lse", 4}});
   if (s != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
   AttnArgs a = attn_args(p, l, g);
@@ -296,7 +302,7 @@ extern "C" muse_status muse_out_norm_gate(const muse_attn_params *p, const muse_
   const int64_t N = g.n_tokens;
   if (N > 0 && (!o || !gate || !out)) return set_error(MUSE_ERR_INVALID_ARG, "o, gate and out are required");
   s = check_disjoint({{o, bf16_bytes(N, g.hq, g.d), "o"}, {gate, bf16_bytes(N, g.hq, g.d), "gate"}},
-                     {{out, bf16_bytes(N, g.hq, g.d), "out"}, {o_rstd, N * g.hq * 4, "o_rstd"}});
+                     {{out, bf16_bytes(N, g.hq, g.d), "out"}, {o_rstd, N * g.hq * 4, "o_rstd", 4}});
   if (s != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
   OutGateArgs a{(const uint16_t *)o, (const uint16_t *)gate, (uint16_t *)out, o_rstd, N * g.hq, p->out_eps};
@@ -322,7 +328,7 @@ extern "C" muse_status muse_attn_fused_fwd(const muse_attn_params *p, const muse
                       {v, bf16_bytes(N, g.hkv, g.d), "v"}, {gate, bf16_bytes(N, g.hq, g.d), "gate"},
                       {q_gain, g.d * 4, "q_gain"}, {cos, tab, "cos"}, {sin, tab, "sin"},
                       layout_range(l, g, 0), layout_range(l, g, 1)},
-                     {{out, bf16_bytes(N, g.hq, g.d), "out"}, {lse, N * g.hq * 4, "lse"}});
+                     {{out, bf16_bytes(N, g.hq, g.d), "out"}, {lse, N * g.hq * 4, "lse", 4}});
   if (s != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
   AttnArgs a = attn_args(p, l, g);
@@ -359,7 +365,7 @@ extern "C" muse_status muse_attn_core_fwd(const muse_attn_params *p, const muse_
        {gate, bf16_bytes(N, g.hq, g.d), "gate"}, {q_gain, g.d * 4, "q_gain"}, {k_gain, g.d * 4, "k_gain"},
        {cos, tab, "cos"}, {sin, tab, "sin"}, layout_range(l, g, 0), layout_range(l, g, 1)},
       {{k_hat_out, bf16_bytes(N, g.hkv, g.d), "k_hat_out"}, {out, bf16_bytes(N, g.hq, g.d), "out"},
-       {lse, N * g.hq * 4, "lse"}});
+       {lse, N * g.hq * 4, "lse", 4}});
   if (s != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
   // keys: norm + gain + RoPE once per key (the K-only pass of the Q/K kernel),

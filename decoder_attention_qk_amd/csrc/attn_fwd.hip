@@ -31,7 +31,9 @@
 // key order P^T has in the S^T accumulator.  16-byte chunks are XOR-swizzled
 // per row on the DMA source side so both read patterns avoid bank conflicts.
 //
-// Tiles are visited from the diagonal downwards; tiles no column of the
+// A workgroup first issues the DMA of its first tile, then loads and
+// normalises its Q fragments and fetches its gate fragments while that DMA is
+// in flight.  Tiles are visited from the diagonal downwards; tiles no column of the
 // workgroup sees are never loaded, tiles every column of a wave sees skip the
 // element mask.  Softmax keeps a lagging reference max that moves only when a
 // tile exceeds it by kRescaleSlackLog2 (log2 units), so the O rescale runs on
@@ -82,6 +84,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, lds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 0);
 }
 
+// x of the lower-half lane and of the upper-half lane of this lane's pair
+// (l, l ^ 32), by one VALU lane swap (no LDS round trip).
+__device__ __forceinline__ void swap32(float x, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void vmem_wait_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
 }
@@ -93,8 +103,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int DT = D / 32;   // O^T row tiles
   constexpr int KK = BN / 16;  // PV k-steps
   constexpr int RB = T::ROW_BYTES;
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  lds_char *smem = (lds_char *)smem_raw;
+  // One array per buffer: distinct objects let the compiler see that the DMA
+  // into one stage never aliases reads of the other, so LDS reads of the
+  // current tile do not wait for the next tile's DMA.
+  __shared__ __attribute__((aligned(16))) char lds_k0[T::TILE_BYTES], lds_v0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_k1[T::TILE_BYTES], lds_v1[T::TILE_BYTES];
+  auto kbuf = [&](int buf) __attribute__((always_inline)) { return (lds_char *)(buf ? lds_k1 : lds_k0); };
+  auto vbuf = [&](int buf) __attribute__((always_inline)) { return (lds_char *)(buf ? lds_v1 : lds_v0); };
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -146,7 +161,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 
   // ---- Q fragment: B operand of S^T = K Q^T; lane holds d = 16 ks + 8 g + [0, 8)
   bf16x8 qf[KS];
-  {
+  // (run after the first K/V tile's DMA is issued, so its latency hides the loads)
+  auto load_q = [&]() __attribute__((always_inline)) {
     uint4 raw[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -159,9 +175,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       for (int ks = 0; ks < KS; ++ks) {
         unpack8(raw[ks], x[ks]);
         const float own = chunk_sumsq<8>(x[ks]);
-        const float other = __shfl_xor(own, 32);
-        all[2 * ks] = g ? other : own;       // chunk 2 ks + g holds d = 16 ks + 8 g
-        all[2 * ks + 1] = g ? own : other;
+        float lo, hi;
+        swap32(own, lo, hi);
+        all[2 * ks] = lo;          // chunk 2 ks + g holds d = 16 ks + 8 g
+        all[2 * ks + 1] = hi;
       }
       const float rstd = rms_rstd(tree_sum(all), 1.0f / (float)D, a.eps);
       int p = 0;
@@ -172,9 +189,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int d0 = ks * 16 + g * 8;
-        float w[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = a.q_gain ? a.gain_center + a.q_gain[d0 + e] : 1.0f;
+        float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+        if (a.q_gain) {
+          const float4 g0 = *reinterpret_cast<const float4 *>(a.q_gain + d0);
+          const float4 g1 = *reinterpret_cast<const float4 *>(a.q_gain + d0 + 4);
+          w[0] = a.gain_center + g0.x; w[1] = a.gain_center + g0.y;
+          w[2] = a.gain_center + g0.z; w[3] = a.gain_center + g0.w;
+          w[4] = a.gain_center + g1.x; w[5] = a.gain_center + g1.y;
+          w[6] = a.gain_center + g1.z; w[7] = a.gain_center + g1.w;
+        }
         float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
         if (a.use_rope) {
           const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)p * (D / 2) + d0 / 2);
@@ -189,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
     }
-  }
+  };
 
   // ---- per-lane DMA source offsets (elements) and LDS read addresses (bytes)
   const int64_t kv_stride = (int64_t)a.hkv * D;
@@ -220,8 +243,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 
   auto issue_dma = [&](int kt, int buf) {
     const int k0 = kt * BN;
-    lds_char *kdst = smem + buf * T::STAGE_BYTES + wave * T::DMA_PER_WAVE * 1024;
-    lds_char *vdst = kdst + T::TILE_BYTES;
+    lds_char *kdst = kbuf(buf) + wave * T::DMA_PER_WAVE * 1024;
+    lds_char *vdst = vbuf(buf) + wave * T::DMA_PER_WAVE * 1024;
     // the tile's rows k0 .. L-1 of this kv head; rows past the segment read as zeros
     // (zero keys are masked out of every score, zero values add nothing)
     const int valid_bytes = ((min(L - k0, BN) - 1) * (int)kv_stride + D) * 2;
@@ -249,21 +272,25 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     const bool none_visible = !wave_active || (k0 > q1w - 1) || (W > 0 && k0 + BN - 1 <= q0w - W);
     if (none_visible) return;
     const bool all_visible = (k0 + BN - 1 <= q0w) && (W <= 0 || k0 > q1w - 1 - W);
-    const lds_char *Kt = smem + BUF * T::STAGE_BYTES;
-    const lds_char *Vt = Kt + T::TILE_BYTES;
+    const lds_char *Kt = kbuf(BUF);
+    const lds_char *Vt = vbuf(BUF);
 
     // The tile is processed as two 32-key halves; the lagging reference max
     // makes a per-half softmax exact.  Order: QK(h0), QK(h1), softmax(h0),
     // PV(h0), softmax(h1), PV(h1) -- the MFMA chains of one half are
     // independent of the other half's softmax, which another wave on the SIMD
     // overlaps.
+    // All K fragments of a half are read before its MFMA chain starts, so
+    // the LDS latency is paid once per half rather than once per k-step.
     auto qk = [&](int half) __attribute__((always_inline)) {
+      bf16x8 kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks] + half * 32 * RB);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 acc = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks] + half * 32 * RB);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc, 0, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc, 0, 0, 0);
       return acc;
     };
     auto softmax = [&](f32x16 &sv, int half, bf16x8 &p0, bf16x8 &p1) __attribute__((always_inline)) {
@@ -277,7 +304,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       float tmax = fmaxf(sv[0], sv[15]);
 #pragma unroll
       for (int i = 1; i < 15; i += 2) tmax = fmaxf(tmax, fmaxf(sv[i], sv[i + 1]));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      {
+        float lo, hi;
+        swap32(tmax, lo, hi);
+        tmax = fmaxf(lo, hi);
+      }
       const bool grow = tmax > m_run + a.rescale_slack;
       if (__any(grow)) {
         // other lanes may enter with this lane still at -inf (no visible key
@@ -337,6 +368,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   const int ntiles = kt_hi - kt_lo + 1;
 
   issue_dma(kt_hi, 0);
+  load_q();
+  // the gate fragments of the epilogue are fetched now (qrow always addresses
+  // a real row), so their latency is long hidden when they are needed
+  uint2 gw[DT][4];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        gw[dt][i4] = *reinterpret_cast<const uint2 *>(a.gate + qrow + dt * 32 + i4 * 8 + g * 4);
+  }
   vmem_wait_all();
   __syncthreads();
   for (int it = 0;;) {
@@ -353,7 +395,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 
   if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  float l_lo, l_hi;
+  swap32(l_run, l_lo, l_hi);
+  const float l_tot = l_lo + l_hi;
   const float inv_l = 1.0f / l_tot;
 
   // O^T element i of tile dt: d = 32 dt + 8 (i/4) + 4 g + i%4, rounded to bf16
@@ -386,8 +430,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const float own = chunk_sumsq<4>(&o[dt][i4 * 4]);
-        const float other = __shfl_xor(own, 32);
-        s1[dt * 4 + i4] = g ? other + own : own + other;
+        float lo, hi;
+        swap32(own, lo, hi);
+        s1[dt * 4 + i4] = lo + hi;
       }
     const float rstd = rms_rstd(tree_sum(s1), 1.0f / (float)D, a.out_eps);
     if (qvalid) {
@@ -396,12 +441,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int64_t off = qrow + dt * 32 + i4 * 8 + g * 4;
-          const uint2 gw = *reinterpret_cast<const uint2 *>(a.gate + off);
+          const uint2 gv = gw[dt][i4];
           uint2 w;
-          w.x = pack_bf16x2(gate_elem(o[dt][i4 * 4 + 0], rstd, bf16_lo(gw.x)),
-                            gate_elem(o[dt][i4 * 4 + 1], rstd, bf16_hi(gw.x)));
-          w.y = pack_bf16x2(gate_elem(o[dt][i4 * 4 + 2], rstd, bf16_lo(gw.y)),
-                            gate_elem(o[dt][i4 * 4 + 3], rstd, bf16_hi(gw.y)));
+          w.x = pack_bf16x2(gate_elem(o[dt][i4 * 4 + 0], rstd, bf16_lo(gv.x)),
+                            gate_elem(o[dt][i4 * 4 + 1], rstd, bf16_hi(gv.x)));
+          w.y = pack_bf16x2(gate_elem(o[dt][i4 * 4 + 2], rstd, bf16_lo(gv.y)),
+                            gate_elem(o[dt][i4 * 4 + 3], rstd, bf16_hi(gv.y)));
           *reinterpret_cast<uint2 *>(a.o + off) = w;
         }
     }
@@ -415,12 +460,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 
 template <int D, bool FUSED>
 hipError_t launch_one(const AttnArgs &a, dim3 grid, hipStream_t stream) {
-  constexpr int bytes = Tile<D>::LDS_BYTES;
-  // LDS beyond the 64 KiB default needs the kernel's attribute raised once.
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&attn_fwd_kernel<D, FUSED>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, FUSED>), grid, dim3(64 * NW), bytes, stream, a);
+  // all LDS is static (Tile<D>::LDS_BYTES), so no dynamic allocation
+  hipLaunchKernelGGL((attn_fwd_kernel<D, FUSED>), grid, dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 

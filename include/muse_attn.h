@@ -23,6 +23,10 @@
  *   stride D).  BSHD [B, S, H, D] and packed THD [T, H, D] share this layout:
  *   N = B*S for BSHD and N = T for THD.
  * - float pointers marked "fp32" are device memory.
+ * - Alignment: bf16 tensors, gains and cos/sin tables must be 16-byte
+ *   aligned (the kernels move them in 16-byte vectors); per-row fp32 outputs
+ *   (rstd, lse) and int32 layout arrays 4-byte aligned.  Misaligned pointers
+ *   are rejected with MUSE_ERR_INVALID_ARG.
  * - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
  *   only enqueues work on that stream and returns without synchronising.
  * - The caller owns every buffer.  The library allocates no memory, keeps no

@@ -117,6 +117,15 @@ def test_missing_and_overlapping_buffers():
     assert _attn(_params(), _bshd(), lse=FAKE + (3 << 24) + 64) == 1
 
 
+def test_misaligned_buffers():
+    # bf16 tensors need 16-byte alignment, per-row fp32 outputs 4-byte
+    assert _attn(_params(), _bshd(), q=FAKE + 2) == 1
+    assert "aligned" in m.library().muse_last_error().decode()
+    assert _attn(_params(), _bshd(), o=FAKE + (3 << 24) + 8) == 1
+    assert _attn(_params(), _bshd(), lse=FAKE + (4 << 24) + 2) == 1
+    assert "aligned" in m.library().muse_last_error().decode()
+
+
 def test_qk_norm_rope_argument_rules():
     lib = m.library()
     p, lay = _params(), _bshd()
