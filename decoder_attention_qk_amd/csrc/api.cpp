@@ -259,7 +259,7 @@ extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_l
   a.hq_div = FastDiv((uint32_t)g.hq);
   a.hkv_div = FastDiv((uint32_t)g.hkv);
   a.q_rows = q ? (int32_t)(N * g.hq) : 0;
-  a.total_rows = a.q_rows + (k ? (int32_t)(N * g.hkv) : 0);
+  a.k_rows = k ? (int32_t)(N * g.hkv) : 0;
   a.eps = p->qk_eps;
   a.gain_center = p->gain_center;
   a.query_scale = p->query_scale;

@@ -44,8 +44,9 @@ struct QkNormArgs {
   int32_t n_pos;
   int32_t hq, hkv;
   FastDiv hq_div, hkv_div;
-  int32_t q_rows;          // N * Hq when q is processed, else 0
-  int32_t total_rows;      // q_rows + (k ? N * Hkv : 0); < 2^31
+  int32_t q_rows;          // N * Hq when q is processed, else 0 (< 2^31)
+  int32_t k_rows;          // N * Hkv when k is processed, else 0 (< 2^31)
+  int32_t q_blocks;        // set by the launcher: blocks given to Q rows (the rest take K rows)
   float eps, gain_center, query_scale;
   int32_t use_rope;
   TokenLayout lay;

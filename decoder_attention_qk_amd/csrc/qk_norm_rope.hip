@@ -4,9 +4,11 @@
 //
 // HBM-bound.  Each (token, head) row of D bf16 values is spread over D/8
 // lanes holding 8 consecutive elements (one 16-byte load); the row's sum of
-// squares is a per-lane fma chain followed by an xor butterfly over those
-// lanes.  Every thread keeps ROWS_IN_FLIGHT rows' loads outstanding before it
-// computes.  Q rows come first (row r = token * Hq + head), then K rows.
+// squares is a per-lane fma chain followed by a DPP reduction over those
+// lanes (no LDS traffic).  Every thread keeps kRowsInFlight rows' loads
+// outstanding before it computes.  The first q_blocks blocks take Q rows
+// (row r = token * Hq + head), the others K rows, so the tensor, its gain and
+// the query scale are uniform per block.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -15,79 +17,137 @@ namespace muse {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsInFlight = 4;
+constexpr int kRowsInFlight = 2;
 
-template <int D>
+// DPP row permutations (within 16-lane rows).
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of the LPR lanes of a row in the shared tree order: pairs of chunks
+// (c, c^1), then pairs of pairs, ...  Each step adds the partner group's
+// partial, so every lane ends with the same bits.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+  v = v + dpp<kDppXor1>(v);
+  v = v + dpp<kDppXor2>(v);
+  if constexpr (LPR >= 8) v = v + dpp<kDppHalfMirror>(v);
+  if constexpr (LPR >= 16) v = v + dpp<kDppMirror>(v);
+  return v;
+}
+
+// ROPE: rotate (use_rope); QS: query_scale != 1 (K rows then take the exact
+// identity scale 1, which leaves their bf16 values unchanged).
+template <int D, bool ROPE, bool QS>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
   constexpr int LPR = D / 8;               // lanes per row
   constexpr int RPP = kThreads / LPR;      // rows per pass of the block
+  static_assert(LPR == 8 || LPR == 16, "row_sum covers 8 or 16 lanes");
   const int c = threadIdx.x % LPR;         // chunk: elements [8c, 8c+8)
   const int rsub = threadIdx.x / LPR;
-  const int base = blockIdx.x * RPP * kRowsInFlight;
 
-  // effective gains of this lane's 8 columns (fixed for every row it touches)
-  float wq[8], wk[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    wq[e] = a.q_gain ? a.gain_center + a.q_gain[c * 8 + e] : 1.0f;
-    wk[e] = a.k_gain ? a.gain_center + a.k_gain[c * 8 + e] : 1.0f;
-  }
+  const bool is_q = (int)blockIdx.x < a.q_blocks;
+  const int blk = is_q ? (int)blockIdx.x : (int)blockIdx.x - a.q_blocks;
+  const int nrows = is_q ? a.q_rows : a.k_rows;
+  const uint16_t *src = is_q ? a.q : a.k;
+  uint16_t *dst = is_q ? a.q_out : a.k_out;
+  float *rs = is_q ? a.q_rstd : a.k_rstd;
+  const float *gain = is_q ? a.q_gain : a.k_gain;
+  const FastDiv hdiv = is_q ? a.hq_div : a.hkv_div;
+  const float qs = is_q ? a.query_scale : 1.0f;
+  const int base = blk * RPP * kRowsInFlight + rsub;
 
   uint4 xin[kRowsInFlight];
 #pragma unroll
   for (int j = 0; j < kRowsInFlight; ++j) {
-    const int r = base + j * RPP + rsub;
-    xin[j] = make_uint4(0, 0, 0, 0);
-    if (r < a.total_rows) {
-      const uint16_t *src = r < a.q_rows ? a.q + (int64_t)r * D : a.k + (int64_t)(r - a.q_rows) * D;
-      xin[j] = *reinterpret_cast<const uint4 *>(src + c * 8);
+    const int r = base + j * RPP;
+    xin[j] = r < nrows ? *reinterpret_cast<const uint4 *>(src + (int64_t)r * D + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+
+  // effective gains of this lane's 8 columns
+  float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+  if (gain) {
+    const float4 g0 = *reinterpret_cast<const float4 *>(gain + c * 8);
+    const float4 g1 = *reinterpret_cast<const float4 *>(gain + c * 8 + 4);
+    w[0] = a.gain_center + g0.x; w[1] = a.gain_center + g0.y;
+    w[2] = a.gain_center + g0.z; w[3] = a.gain_center + g0.w;
+    w[4] = a.gain_center + g1.x; w[5] = a.gain_center + g1.y;
+    w[6] = a.gain_center + g1.z; w[7] = a.gain_center + g1.w;
+  }
+
+  // RoPE positions of this thread's rows (tokens increase with j; a packed
+  // layout walks its segments forward from the first row's)
+  int pos[kRowsInFlight];
+  if constexpr (ROPE) {
+    int seg = -1;
+#pragma unroll
+    for (int j = 0; j < kRowsInFlight; ++j) {
+      const int r = min(base + j * RPP, nrows - 1);
+      const int t = (int)hdiv.div((uint32_t)r);
+      int p;
+      if (a.lay.position_ids) {
+        p = a.lay.position_ids[t];
+      } else if (a.lay.cu_seqlens) {
+        if (seg < 0) seg = find_segment(a.lay, t);
+        while (seg + 1 < a.lay.num_segments && a.lay.cu_seqlens[seg + 1] <= t) ++seg;
+        p = t - a.lay.cu_seqlens[seg];
+      } else {
+        p = (int)a.lay.seqlen_div.mod((uint32_t)t);
+      }
+      pos[j] = p < 0 ? 0 : (p >= a.n_pos ? a.n_pos - 1 : p);
     }
   }
 
 #pragma unroll
   for (int j = 0; j < kRowsInFlight; ++j) {
-    const int r = base + j * RPP + rsub;
-    const bool valid = r < a.total_rows;
-    const bool is_q = r < a.q_rows;
+    const int r = base + j * RPP;
     float x[8];
     unpack8(xin[j], x);
-    float ss = chunk_sumsq<8>(x);
-#pragma unroll
-    for (int w = 1; w < LPR; w <<= 1) ss = ss + __shfl_xor(ss, w);
-    if (!valid) continue;
+    const float ss = row_sum<LPR>(chunk_sumsq<8>(x));
+    if (r >= nrows) continue;
     const float rstd = rms_rstd(ss, 1.0f / (float)D, a.eps);
-    const int rr = is_q ? r : r - a.q_rows;            // row inside its own tensor
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
-    if (a.use_rope) {
-      const int tok = (int)(is_q ? a.hq_div.div((uint32_t)rr) : a.hkv_div.div((uint32_t)rr));
-      const int p = rope_position(a.lay, tok, a.n_pos);
-      const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + p * (D / 2) + c * 4);
-      const float4 sv = *reinterpret_cast<const float4 *>(a.sin_tab + p * (D / 2) + c * 4);
+    if constexpr (ROPE) {
+      const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)pos[j] * (D / 2) + c * 4);
+      const float4 sv = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)pos[j] * (D / 2) + c * 4);
       cs[0] = cv.x; cs[1] = cv.y; cs[2] = cv.z; cs[3] = cv.w;
       sn[0] = sv.x; sn[1] = sv.y; sn[2] = sv.z; sn[3] = sv.w;
     }
-    const uint4 y = qk_chunk(x, is_q ? wq : wk, rstd, is_q && a.query_scale != 1.0f, a.query_scale,
-                             a.use_rope != 0, cs, sn);
-    uint16_t *dst = is_q ? a.q_out : a.k_out;
-    *reinterpret_cast<uint4 *>(dst + (int64_t)rr * D + c * 8) = y;
-    if (c == 0) {
-      float *rs = is_q ? a.q_rstd : a.k_rstd;
-      if (rs) rs[rr] = rstd;
-    }
+    const uint4 y = qk_chunk(x, w, rstd, QS, qs, ROPE, cs, sn);
+    *reinterpret_cast<uint4 *>(dst + (int64_t)r * D + c * 8) = y;
+    if (rs && c == 0) rs[r] = rstd;
+  }
+}
+
+template <int D>
+void launch_d(const QkNormArgs &a, dim3 grid, hipStream_t stream) {
+  const bool qs = a.q_rows > 0 && a.query_scale != 1.0f;
+  if (a.use_rope) {
+    if (qs) hipLaunchKernelGGL((qk_norm_rope_kernel<D, true, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((qk_norm_rope_kernel<D, true, false>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (qs) hipLaunchKernelGGL((qk_norm_rope_kernel<D, false, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((qk_norm_rope_kernel<D, false, false>), grid, dim3(kThreads), 0, stream, a);
   }
 }
 
 }  // namespace
 
-hipError_t launch_qk_norm_rope(int head_dim, const QkNormArgs &a, hipStream_t stream) {
-  if (a.total_rows == 0) return hipSuccess;
+hipError_t launch_qk_norm_rope(int head_dim, const QkNormArgs &args, hipStream_t stream) {
   const int lpr = head_dim / 8;
   const int64_t rows_per_block = (int64_t)(kThreads / lpr) * kRowsInFlight;
-  const int64_t blocks = (a.total_rows + rows_per_block - 1) / rows_per_block;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(qk_norm_rope_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(qk_norm_rope_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  QkNormArgs a = args;
+  a.q_blocks = (int)((a.q_rows + rows_per_block - 1) / rows_per_block);
+  const int64_t blocks = a.q_blocks + (a.k_rows + rows_per_block - 1) / rows_per_block;
+  if (blocks == 0) return hipSuccess;
+  if (head_dim == 128) launch_d<128>(a, dim3((unsigned)blocks), stream);
+  else launch_d<64>(a, dim3((unsigned)blocks), stream);
   return hipGetLastError();
 }
 
