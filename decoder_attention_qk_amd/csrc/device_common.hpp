@@ -79,6 +79,31 @@ __device__ __forceinline__ float tree_sum(float (&p)[N]) {
   return p[0];
 }
 
+// DPP row permutations (within 16-lane rows).
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LPR lanes (8 or 16, aligned) holding one row, in the shared
+// tree order: pairs of chunks (c, c^1), then pairs of pairs, ...  Each step
+// adds the partner group's partial, so every lane ends with the same bits.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+  v = v + dpp<kDppXor1>(v);
+  v = v + dpp<kDppXor2>(v);
+  if constexpr (LPR >= 8) v = v + dpp<kDppHalfMirror>(v);
+  if constexpr (LPR >= 16) v = v + dpp<kDppMirror>(v);
+  return v;
+}
+
+// ROPE: rotate (use_rope); QS: query_scale != 1 (K rows then take the exact
+// identity scale 1, which leaves their bf16 values unchanged).
 // 1 / sqrt(mean + eps) with correctly rounded sqrt and division.
 __device__ __forceinline__ float rms_rstd(float sumsq, float inv_d, float eps) {
   return 1.0f / __builtin_sqrtf(__builtin_fmaf(sumsq, inv_d, 0.0f) + eps);

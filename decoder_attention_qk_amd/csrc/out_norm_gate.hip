@@ -4,8 +4,9 @@
 // HBM-bound: reads O and the gate once, writes out once.  Each row of D
 // values spreads over D/8 lanes of 8 consecutive elements.  The sum of
 // squares treats each lane's 8 elements as two 4-element groups (an fma
-// chain each), adds the pair, then runs an xor butterfly over the row's
-// lanes -- the same tree the fused attention epilogue uses on its own layout.
+// chain each), adds the pair, then reduces over the row's lanes with DPP
+// (row_sum) -- the same tree the fused attention epilogue uses on its own
+// layout.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -41,9 +42,7 @@ __global__ __launch_bounds__(kThreads) void out_norm_gate_kernel(OutGateArgs a) 
     float x[8], g[8];
     unpack8(oin[j], x);
     unpack8(gin[j], g);
-    float ss = chunk_sumsq<4>(x) + chunk_sumsq<4>(x + 4);
-#pragma unroll
-    for (int w = 1; w < LPR; w <<= 1) ss = ss + __shfl_xor(ss, w);
+    const float ss = row_sum<LPR>(chunk_sumsq<4>(x) + chunk_sumsq<4>(x + 4));
     if (r >= a.rows) continue;
     const float rstd = rms_rstd(ss, 1.0f / (float)D, a.eps);
     float y[8];
