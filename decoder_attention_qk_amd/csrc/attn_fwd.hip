@@ -117,15 +117,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  // ---- work item (q blocks in descending order: longest first)
-  const int per_qb = a.lay.num_segments * a.hkv * a.head_chunks;
+  // ---- work item: segment-major, then query blocks in descending order
+  // (longest first), then (kv head, head chunk).  Consecutive workgroups
+  // take consecutive kv heads, so with the round-robin dispatch over the
+  // XCDs each XCD works on one (segment, kv head) pair at a time and its K/V
+  // stays in that XCD's L2.
+  const int per_seg = a.q_blocks * a.hkv * a.head_chunks;
   const int b = blockIdx.x;
-  const int qb = a.q_blocks - 1 - b / per_qb;
-  int rest = b % per_qb;
+  const int seg = b / per_seg;
+  int rest = b % per_seg;
+  const int qb = a.q_blocks - 1 - rest / (a.hkv * a.head_chunks);
+  rest %= a.hkv * a.head_chunks;
   const int hc = rest % a.head_chunks;
-  rest /= a.head_chunks;
-  const int kvh = rest % a.hkv;
-  const int seg = rest / a.hkv;
+  const int kvh = rest / a.head_chunks;
 
   int s0, L;
   if (a.lay.cu_seqlens) {
@@ -169,44 +173,62 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       raw[ks] = qvalid ? *reinterpret_cast<const uint4 *>(a.q + qrow + ks * 16 + g * 8)
                        : make_uint4(0, 0, 0, 0);
     if constexpr (FUSED) {
-      float x[KS][8];
+      // every global load of the prologue is issued before any result is used
+      const bool has_gain = a.q_gain != nullptr, rope = a.use_rope != 0;
+      float4 gv[KS][2];
+      if (has_gain) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          gv[ks][0] = *reinterpret_cast<const float4 *>(a.q_gain + ks * 16 + g * 8);
+          gv[ks][1] = *reinterpret_cast<const float4 *>(a.q_gain + ks * 16 + g * 8 + 4);
+        }
+      }
+      float4 cv[KS], sv[KS];
+      if (rope) {
+        int p = a.lay.position_ids ? a.lay.position_ids[s0 + (qvalid ? qpos : 0)] : (qvalid ? qpos : 0);
+        p = p < 0 ? 0 : (p >= a.n_pos ? a.n_pos - 1 : p);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          cv[ks] = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)p * (D / 2) + ks * 8 + g * 4);
+          sv[ks] = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)p * (D / 2) + ks * 8 + g * 4);
+        }
+      }
       float all[2 * KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        unpack8(raw[ks], x[ks]);
-        const float own = chunk_sumsq<8>(x[ks]);
+        float x[8];
+        unpack8(raw[ks], x);
+        const float own = chunk_sumsq<8>(x);
         float lo, hi;
         swap32(own, lo, hi);
         all[2 * ks] = lo;          // chunk 2 ks + g holds d = 16 ks + 8 g
         all[2 * ks + 1] = hi;
       }
       const float rstd = rms_rstd(tree_sum(all), 1.0f / (float)D, a.eps);
-      int p = 0;
-      if (a.use_rope) {
-        p = a.lay.position_ids ? a.lay.position_ids[s0 + (qvalid ? qpos : 0)] : (qvalid ? qpos : 0);
-        p = p < 0 ? 0 : (p >= a.n_pos ? a.n_pos - 1 : p);
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int d0 = ks * 16 + g * 8;
+      auto chunk = [&](int ks, bool qscale, bool rot) __attribute__((always_inline)) {
         float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-        if (a.q_gain) {
-          const float4 g0 = *reinterpret_cast<const float4 *>(a.q_gain + d0);
-          const float4 g1 = *reinterpret_cast<const float4 *>(a.q_gain + d0 + 4);
-          w[0] = a.gain_center + g0.x; w[1] = a.gain_center + g0.y;
-          w[2] = a.gain_center + g0.z; w[3] = a.gain_center + g0.w;
-          w[4] = a.gain_center + g1.x; w[5] = a.gain_center + g1.y;
-          w[6] = a.gain_center + g1.z; w[7] = a.gain_center + g1.w;
+        if (has_gain) {
+          w[0] = a.gain_center + gv[ks][0].x; w[1] = a.gain_center + gv[ks][0].y;
+          w[2] = a.gain_center + gv[ks][0].z; w[3] = a.gain_center + gv[ks][0].w;
+          w[4] = a.gain_center + gv[ks][1].x; w[5] = a.gain_center + gv[ks][1].y;
+          w[6] = a.gain_center + gv[ks][1].z; w[7] = a.gain_center + gv[ks][1].w;
         }
         float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
-        if (a.use_rope) {
-          const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)p * (D / 2) + d0 / 2);
-          const float4 sv = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)p * (D / 2) + d0 / 2);
-          cs[0] = cv.x; cs[1] = cv.y; cs[2] = cv.z; cs[3] = cv.w;
-          sn[0] = sv.x; sn[1] = sv.y; sn[2] = sv.z; sn[3] = sv.w;
+        if (rot) {
+          cs[0] = cv[ks].x; cs[1] = cv[ks].y; cs[2] = cv[ks].z; cs[3] = cv[ks].w;
+          sn[0] = sv[ks].x; sn[1] = sv[ks].y; sn[2] = sv[ks].z; sn[3] = sv[ks].w;
         }
-        qf[ks] = __builtin_bit_cast(bf16x8, qk_chunk(x[ks], w, rstd, a.query_scale != 1.0f, a.query_scale,
-                                                     a.use_rope != 0, cs, sn));
+        float x[8];
+        unpack8(raw[ks], x);
+        qf[ks] = __builtin_bit_cast(bf16x8, qk_chunk(x, w, rstd, qscale, a.query_scale, rot, cs, sn));
+      };
+      if (rope && a.query_scale == 1.0f) {
+        // the common case with its flags known at compile time (no branches)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) chunk(ks, false, true);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) chunk(ks, a.query_scale != 1.0f, rope);
       }
     } else {
 #pragma unroll
