@@ -173,62 +173,76 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       raw[ks] = qvalid ? *reinterpret_cast<const uint4 *>(a.q + qrow + ks * 16 + g * 8)
                        : make_uint4(0, 0, 0, 0);
     if constexpr (FUSED) {
-      // every global load of the prologue is issued before any result is used
+      // Two phases, each with all of its loads issued before any result is
+      // used: (1) Q and the gains -> normalised bf16 chunks; (2) the cos/sin
+      // rows -> query scale and rotation.  Splitting them keeps the gains and
+      // the table rows from being live at the same time.
       const bool has_gain = a.q_gain != nullptr, rope = a.use_rope != 0;
-      float4 gv[KS][2];
-      if (has_gain) {
+      uint4 nq[KS];
+      {
+        float4 gv[KS][2];
+        if (has_gain) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            gv[ks][0] = *reinterpret_cast<const float4 *>(a.q_gain + ks * 16 + g * 8);
+            gv[ks][1] = *reinterpret_cast<const float4 *>(a.q_gain + ks * 16 + g * 8 + 4);
+          }
+        }
+        float all[2 * KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          gv[ks][0] = *reinterpret_cast<const float4 *>(a.q_gain + ks * 16 + g * 8);
-          gv[ks][1] = *reinterpret_cast<const float4 *>(a.q_gain + ks * 16 + g * 8 + 4);
+          float x[8];
+          unpack8(raw[ks], x);
+          const float own = chunk_sumsq<8>(x);
+          float lo, hi;
+          swap32(own, lo, hi);
+          all[2 * ks] = lo;          // chunk 2 ks + g holds d = 16 ks + 8 g
+          all[2 * ks + 1] = hi;
+        }
+        const float rstd = rms_rstd(tree_sum(all), 1.0f / (float)D, a.eps);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+          if (has_gain) {
+            w[0] = a.gain_center + gv[ks][0].x; w[1] = a.gain_center + gv[ks][0].y;
+            w[2] = a.gain_center + gv[ks][0].z; w[3] = a.gain_center + gv[ks][0].w;
+            w[4] = a.gain_center + gv[ks][1].x; w[5] = a.gain_center + gv[ks][1].y;
+            w[6] = a.gain_center + gv[ks][1].z; w[7] = a.gain_center + gv[ks][1].w;
+          }
+          float x[8];
+          unpack8(raw[ks], x);
+          nq[ks] = norm_chunk(x, w, rstd);
         }
       }
-      float4 cv[KS], sv[KS];
+      __builtin_amdgcn_sched_barrier(0);
       if (rope) {
         int p = a.lay.position_ids ? a.lay.position_ids[s0 + (qvalid ? qpos : 0)] : (qvalid ? qpos : 0);
         p = p < 0 ? 0 : (p >= a.n_pos ? a.n_pos - 1 : p);
+        float4 cv[KS], sv[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           cv[ks] = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)p * (D / 2) + ks * 8 + g * 4);
           sv[ks] = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)p * (D / 2) + ks * 8 + g * 4);
         }
-      }
-      float all[2 * KS];
+        const bool qscale = a.query_scale != 1.0f;
+        auto rot = [&](int ks, bool qs) __attribute__((always_inline)) {
+          const float cs[4] = {cv[ks].x, cv[ks].y, cv[ks].z, cv[ks].w};
+          const float sn[4] = {sv[ks].x, sv[ks].y, sv[ks].z, sv[ks].w};
+          qf[ks] = __builtin_bit_cast(bf16x8, scale_rope_chunk(nq[ks], qs, a.query_scale, true, cs, sn));
+        };
+        if (!qscale) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        float x[8];
-        unpack8(raw[ks], x);
-        const float own = chunk_sumsq<8>(x);
-        float lo, hi;
-        swap32(own, lo, hi);
-        all[2 * ks] = lo;          // chunk 2 ks + g holds d = 16 ks + 8 g
-        all[2 * ks + 1] = hi;
-      }
-      const float rstd = rms_rstd(tree_sum(all), 1.0f / (float)D, a.eps);
-      auto chunk = [&](int ks, bool qscale, bool rot) __attribute__((always_inline)) {
-        float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-        if (has_gain) {
-          w[0] = a.gain_center + gv[ks][0].x; w[1] = a.gain_center + gv[ks][0].y;
-          w[2] = a.gain_center + gv[ks][0].z; w[3] = a.gain_center + gv[ks][0].w;
-          w[4] = a.gain_center + gv[ks][1].x; w[5] = a.gain_center + gv[ks][1].y;
-          w[6] = a.gain_center + gv[ks][1].z; w[7] = a.gain_center + gv[ks][1].w;
-        }
-        float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
-        if (rot) {
-          cs[0] = cv[ks].x; cs[1] = cv[ks].y; cs[2] = cv[ks].z; cs[3] = cv[ks].w;
-          sn[0] = sv[ks].x; sn[1] = sv[ks].y; sn[2] = sv[ks].z; sn[3] = sv[ks].w;
-        }
-        float x[8];
-        unpack8(raw[ks], x);
-        qf[ks] = __builtin_bit_cast(bf16x8, qk_chunk(x, w, rstd, qscale, a.query_scale, rot, cs, sn));
-      };
-      if (rope && a.query_scale == 1.0f) {
-        // the common case with its flags known at compile time (no branches)
+          for (int ks = 0; ks < KS; ++ks) rot(ks, false);
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) chunk(ks, false, true);
+          for (int ks = 0; ks < KS; ++ks) rot(ks, true);
+        }
       } else {
+        const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) chunk(ks, a.query_scale != 1.0f, rope);
+        for (int ks = 0; ks < KS; ++ks)
+          qf[ks] = __builtin_bit_cast(
+              bf16x8, scale_rope_chunk(nq[ks], a.query_scale != 1.0f, a.query_scale, false, one, zero));
       }
     } else {
 #pragma unroll
@@ -315,22 +329,27 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc, 0, 0, 0);
       return acc;
     };
-    auto softmax = [&](f32x16 &sv, int half, bf16x8 &p0, bf16x8 &p1) __attribute__((always_inline)) {
-      if (!all_visible) {
+    auto mask = [&](f32x16 &sv, int half) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kp = k0 + half * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          if (!(kp <= qpos && (W <= 0 || kp > qpos - W))) sv[i] = -INFINITY;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int kp = k0 + half * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+        if (!(kp <= qpos && (W <= 0 || kp > qpos - W))) sv[i] = -INFINITY;
       }
-      float tmax = fmaxf(sv[0], sv[15]);
+    };
+    // row max of both halves (a tree, for short dependency chains), folded
+    // into the lagging reference once per tile
+    auto tile_max = [&](const f32x16 &s0, const f32x16 &s1) __attribute__((always_inline)) {
+      float m8[8];
 #pragma unroll
-      for (int i = 1; i < 15; i += 2) tmax = fmaxf(tmax, fmaxf(sv[i], sv[i + 1]));
-      {
-        float lo, hi;
-        swap32(tmax, lo, hi);
-        tmax = fmaxf(lo, hi);
+      for (int j = 0; j < 4; ++j) {
+        m8[j] = fmaxf(fmaxf(s0[4 * j], s0[4 * j + 1]), fmaxf(s0[4 * j + 2], s0[4 * j + 3]));
+        m8[4 + j] = fmaxf(fmaxf(s1[4 * j], s1[4 * j + 1]), fmaxf(s1[4 * j + 2], s1[4 * j + 3]));
       }
+      float tmax = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                         fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+      float lo, hi;
+      swap32(tmax, lo, hi);
+      tmax = fmaxf(lo, hi);
       const bool grow = tmax > m_run + a.rescale_slack;
       if (__any(grow)) {
         // other lanes may enter with this lane still at -inf (no visible key
@@ -342,15 +361,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
         for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         m_run = m_new;
       }
+    };
+    auto softmax = [&](const f32x16 &sv, bf16x8 &p0, bf16x8 &p1) __attribute__((always_inline)) {
       const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c2;
       float pf[16];
-      float psum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c2, -mc));
-        psum += pf[i];
-      }
-      l_run += psum;
+      for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c2, -mc));
+      float t[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[j] = (pf[4 * j] + pf[4 * j + 1]) + (pf[4 * j + 2] + pf[4 * j + 3]);
+      l_run += (t[0] + t[1]) + (t[2] + t[3]);
       uint4 lo, hi;
       lo.x = pack_bf16x2(pf[0], pf[1]);   lo.y = pack_bf16x2(pf[2], pf[3]);
       lo.z = pack_bf16x2(pf[4], pf[5]);   lo.w = pack_bf16x2(pf[6], pf[7]);
@@ -377,10 +397,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 
     f32x16 s0v = qk(0);
     f32x16 s1v = qk(1);
+    if (!all_visible) {
+      mask(s0v, 0);
+      mask(s1v, 1);
+    }
+    tile_max(s0v, s1v);
     bf16x8 pa0, pa1, pb0, pb1;
-    softmax(s0v, 0, pa0, pa1);
+    softmax(s0v, pa0, pa1);
     pv(0, pa0, pa1);
-    softmax(s1v, 1, pb0, pb1);
+    softmax(s1v, pb0, pb1);
     pv(1, pb0, pb1);
   };
 

@@ -111,18 +111,26 @@ __device__ __forceinline__ float rms_rstd(float sumsq, float inv_d, float eps) {
 
 // ---------------------------------------------------------------------------
 // Q/K norm + query scale + RoPE on one chunk of 8 consecutive elements
-// (4 adjacent pairs).  x: inputs; w: effective gains; c, s: cos/sin of the 4
-// pairs (ignored when !rope); qscale applied (with its own bf16 cast) when
-// apply_qscale.  Returns the 8 rotated values as packed bf16.  Each pair is
-// rounded with one packed conversion; the rounded values feed the next step.
+// (4 adjacent pairs), in two stages so a caller may split them:
+//   norm_chunk:       bf16((x * r) * w) for each pair (one packed conversion)
+//   scale_rope_chunk: optional bf16(. * qscale), then the FP32 rotation of each
+//                     pair by (c, s), rounded to bf16.
+// x: inputs; w: effective gains; c, s: cos/sin of the 4 pairs (ignored when
+// !rope).  Each rounded pair is one packed conversion; the rounded values feed
+// the next step.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint4 qk_chunk(const float (&x)[8], const float (&w)[8], float r,
-                                          bool apply_qscale, float qscale, bool rope,
-                                          const float (&c)[4], const float (&s)[4]) {
+__device__ __forceinline__ uint4 norm_chunk(const float (&x)[8], const float (&w)[8], float r) {
   uint32_t out[4];
 #pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2((x[2 * i] * r) * w[2 * i], (x[2 * i + 1] * r) * w[2 * i + 1]);
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+__device__ __forceinline__ uint4 scale_rope_chunk(const uint4 &v, bool apply_qscale, float qscale, bool rope,
+                                                  const float (&c)[4], const float (&s)[4]) {
+  uint32_t out[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t p = pack_bf16x2((x[2 * i] * r) * w[2 * i], (x[2 * i + 1] * r) * w[2 * i + 1]);
+    uint32_t p = out[i];
     if (apply_qscale) p = pack_bf16x2(bf16_lo(p) * qscale, bf16_hi(p) * qscale);
     if (rope) {
       const float a = bf16_lo(p), b = bf16_hi(p);
@@ -131,6 +139,11 @@ __device__ __forceinline__ uint4 qk_chunk(const float (&x)[8], const float (&w)[
     out[i] = p;
   }
   return make_uint4(out[0], out[1], out[2], out[3]);
+}
+__device__ __forceinline__ uint4 qk_chunk(const float (&x)[8], const float (&w)[8], float r,
+                                          bool apply_qscale, float qscale, bool rope,
+                                          const float (&c)[4], const float (&s)[4]) {
+  return scale_rope_chunk(norm_chunk(x, w, r), apply_qscale, qscale, rope, c, s);
 }
 
 // ---------------------------------------------------------------------------
