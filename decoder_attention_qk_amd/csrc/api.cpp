@@ -75,8 +75,6 @@ muse_status check_params(const muse_attn_params *p) {
   if (!finite(p->gain_center)) return set_error(MUSE_ERR_INVALID_ARG, "gain_center must be finite");
   if (p->head_dim != 64 && p->head_dim != 128)
     return set_error(MUSE_ERR_UNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", p->head_dim);
-  if (p->use_rope && !p->upcast_rope)
-    return set_error(MUSE_ERR_UNSUPPORTED, "upcast_rope = 0 (bf16-rounded rotation products) is not built");
   return MUSE_OK;
 }
 
@@ -181,6 +179,7 @@ AttnArgs attn_args(const muse_attn_params *p, const muse_layout *l, const Geomet
   a.gain_center = p->gain_center;
   a.query_scale = p->query_scale;
   a.use_rope = p->use_rope ? 1 : 0;
+  a.rope_v2 = p->upcast_rope ? 0 : 1;
   a.scaling = p->scaling;
   a.scale_log2 = p->scaling * 1.4426950408889634f;
   a.rescale_slack = kRescaleSlackLog2 / a.scale_log2;
@@ -264,6 +263,7 @@ extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_l
   a.gain_center = p->gain_center;
   a.query_scale = p->query_scale;
   a.use_rope = p->use_rope ? 1 : 0;
+  a.rope_v2 = p->upcast_rope ? 0 : 1;
   a.lay = token_layout(l, g);
   return device_status(launch_qk_norm_rope(g.d, a, (hipStream_t)stream), "qk_norm_rope launch");
 }

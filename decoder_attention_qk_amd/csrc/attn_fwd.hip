@@ -224,18 +224,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
           cv[ks] = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)p * (D / 2) + ks * 8 + g * 4);
           sv[ks] = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)p * (D / 2) + ks * 8 + g * 4);
         }
-        const bool qscale = a.query_scale != 1.0f;
-        auto rot = [&](int ks, bool qs) __attribute__((always_inline)) {
+        const bool qscale = a.query_scale != 1.0f, v2 = a.rope_v2 != 0;
+        auto rot = [&](int ks, bool qs, bool rv2) __attribute__((always_inline)) {
           const float cs[4] = {cv[ks].x, cv[ks].y, cv[ks].z, cv[ks].w};
           const float sn[4] = {sv[ks].x, sv[ks].y, sv[ks].z, sv[ks].w};
-          qf[ks] = __builtin_bit_cast(bf16x8, scale_rope_chunk(nq[ks], qs, a.query_scale, true, cs, sn));
+          qf[ks] = __builtin_bit_cast(bf16x8, scale_rope_chunk(nq[ks], qs, a.query_scale, true, cs, sn, rv2));
         };
-        if (!qscale) {
+        if (!qscale && !v2) {
+          // the common case with its flags known at compile time (no branches)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) rot(ks, false);
+          for (int ks = 0; ks < KS; ++ks) rot(ks, false, false);
         } else {
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) rot(ks, true);
+          for (int ks = 0; ks < KS; ++ks) rot(ks, qscale, v2);
         }
       } else {
         const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {0.f, 0.f, 0.f, 0.f};

@@ -102,8 +102,6 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-// ROPE: rotate (use_rope); QS: query_scale != 1 (K rows then take the exact
-// identity scale 1, which leaves their bf16 values unchanged).
 // 1 / sqrt(mean + eps) with correctly rounded sqrt and division.
 __device__ __forceinline__ float rms_rstd(float sumsq, float inv_d, float eps) {
   return 1.0f / __builtin_sqrtf(__builtin_fmaf(sumsq, inv_d, 0.0f) + eps);
@@ -125,16 +123,32 @@ __device__ __forceinline__ uint4 norm_chunk(const float (&x)[8], const float (&w
   for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2((x[2 * i] * r) * w[2 * i], (x[2 * i + 1] * r) * w[2 * i + 1]);
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
+// The Q/K-dtype rotation of one packed pair (apply_rotary_embedding with
+// upcast=False): C and S cast to bf16, each product rounded to bf16, then the
+// difference / sum rounded to bf16 -- each a bf16 operation evaluated in FP32
+// and rounded once.  (Products of two bf16 values are exact in FP32.)
+__device__ __forceinline__ uint32_t rope_pair_v2(uint32_t p, float c, float s) {
+  const float a = bf16_lo(p), b = bf16_hi(p);
+  const float cb = round_bf16(c), sb = round_bf16(s);
+  const float y0 = round_bf16(round_bf16(a * cb) - round_bf16(b * sb));
+  const float y1 = round_bf16(round_bf16(a * sb) + round_bf16(b * cb));
+  return pack_bf16x2(y0, y1);   // exact: both already bf16 values
+}
+// rope_v2 selects the Q/K-dtype rotation above instead of the FP32 one.
 __device__ __forceinline__ uint4 scale_rope_chunk(const uint4 &v, bool apply_qscale, float qscale, bool rope,
-                                                  const float (&c)[4], const float (&s)[4]) {
+                                                  const float (&c)[4], const float (&s)[4], bool rope_v2 = false) {
   uint32_t out[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t p = out[i];
     if (apply_qscale) p = pack_bf16x2(bf16_lo(p) * qscale, bf16_hi(p) * qscale);
     if (rope) {
-      const float a = bf16_lo(p), b = bf16_hi(p);
-      p = pack_bf16x2(__builtin_fmaf(a, c[i], -(b * s[i])), __builtin_fmaf(a, s[i], b * c[i]));
+      if (rope_v2) {
+        p = rope_pair_v2(p, c[i], s[i]);
+      } else {
+        const float a = bf16_lo(p), b = bf16_hi(p);
+        p = pack_bf16x2(__builtin_fmaf(a, c[i], -(b * s[i])), __builtin_fmaf(a, s[i], b * c[i]));
+      }
     }
     out[i] = p;
   }
@@ -142,8 +156,8 @@ __device__ __forceinline__ uint4 scale_rope_chunk(const uint4 &v, bool apply_qsc
 }
 __device__ __forceinline__ uint4 qk_chunk(const float (&x)[8], const float (&w)[8], float r,
                                           bool apply_qscale, float qscale, bool rope,
-                                          const float (&c)[4], const float (&s)[4]) {
-  return scale_rope_chunk(norm_chunk(x, w, r), apply_qscale, qscale, rope, c, s);
+                                          const float (&c)[4], const float (&s)[4], bool rope_v2 = false) {
+  return scale_rope_chunk(norm_chunk(x, w, r), apply_qscale, qscale, rope, c, s, rope_v2);
 }
 
 // ---------------------------------------------------------------------------

@@ -49,6 +49,7 @@ struct QkNormArgs {
   int32_t q_blocks;        // set by the launcher: blocks given to Q rows (the rest take K rows)
   float eps, gain_center, query_scale;
   int32_t use_rope;
+  int32_t rope_v2;         // rotation in the Q/K dtype (upcast_rope == 0)
   TokenLayout lay;
 };
 
@@ -74,6 +75,7 @@ struct AttnArgs {
   const float *sin_tab;
   int32_t n_pos;
   int32_t use_rope;
+  int32_t rope_v2;         // rotation in the Q/K dtype (upcast_rope == 0)
   float eps, out_eps, gain_center, query_scale;
   // attention
   float scaling;           // softmax scale

@@ -19,7 +19,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsInFlight = 2;
 
-template <int D, bool ROPE, bool QS>
+// ROPE: 0 no rotation, 1 FP32 rotation (upcast_rope), 2 rotation in the Q/K
+// dtype; QS: query_scale != 1 (K rows then take the exact identity scale 1,
+// which leaves their bf16 values unchanged).
+template <int D, int ROPE, bool QS>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
   constexpr int LPR = D / 8;               // lanes per row
   constexpr int RPP = kThreads / LPR;      // rows per pass of the block
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
   // RoPE positions of this thread's rows (tokens increase with j; a packed
   // layout walks its segments forward from the first row's)
   int pos[kRowsInFlight];
-  if constexpr (ROPE) {
+  if constexpr (ROPE != 0) {
     int seg = -1;
 #pragma unroll
     for (int j = 0; j < kRowsInFlight; ++j) {
@@ -88,28 +91,31 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
     if (r >= nrows) continue;
     const float rstd = rms_rstd(ss, 1.0f / (float)D, a.eps);
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (ROPE) {
+    if constexpr (ROPE != 0) {
       const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)pos[j] * (D / 2) + c * 4);
       const float4 sv = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)pos[j] * (D / 2) + c * 4);
       cs[0] = cv.x; cs[1] = cv.y; cs[2] = cv.z; cs[3] = cv.w;
       sn[0] = sv.x; sn[1] = sv.y; sn[2] = sv.z; sn[3] = sv.w;
     }
-    const uint4 y = qk_chunk(x, w, rstd, QS, qs, ROPE, cs, sn);
+    const uint4 y = qk_chunk(x, w, rstd, QS, qs, ROPE != 0, cs, sn, ROPE == 2);
     *reinterpret_cast<uint4 *>(dst + (int64_t)r * D + c * 8) = y;
     if (rs && c == 0) rs[r] = rstd;
   }
 }
 
+template <int D, int ROPE>
+void launch_r(const QkNormArgs &a, dim3 grid, hipStream_t stream) {
+  if (a.q_rows > 0 && a.query_scale != 1.0f)
+    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, true>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, false>), grid, dim3(kThreads), 0, stream, a);
+}
+
 template <int D>
 void launch_d(const QkNormArgs &a, dim3 grid, hipStream_t stream) {
-  const bool qs = a.q_rows > 0 && a.query_scale != 1.0f;
-  if (a.use_rope) {
-    if (qs) hipLaunchKernelGGL((qk_norm_rope_kernel<D, true, true>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((qk_norm_rope_kernel<D, true, false>), grid, dim3(kThreads), 0, stream, a);
-  } else {
-    if (qs) hipLaunchKernelGGL((qk_norm_rope_kernel<D, false, true>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((qk_norm_rope_kernel<D, false, false>), grid, dim3(kThreads), 0, stream, a);
-  }
+  if (!a.use_rope) launch_r<D, 0>(a, grid, stream);
+  else if (a.rope_v2) launch_r<D, 2>(a, grid, stream);
+  else launch_r<D, 1>(a, grid, stream);
 }
 
 }  // namespace

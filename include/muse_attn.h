@@ -70,8 +70,10 @@ typedef enum {
  *                     window (the pages' "or None").
  * use_rope            non-zero: rotate Q and K (layers page, layer_uses_rope).
  * upcast_rope         non-zero: FP32 rotation (apply_rotary_embedding upcast=True,
- *                     the original checkpoint's arithmetic).  Zero (rounding both
- *                     products to bf16 before adding) returns MUSE_ERR_UNSUPPORTED.
+ *                     the original checkpoint's arithmetic).  Zero: rotation in the
+ *                     Q/K dtype (upcast=False, the HF release, which rounds both
+ *                     products before adding them): C and S cast to bf16, each
+ *                     product rounded to bf16, then the bf16 difference / sum.
  * scaling             softmax scale, head_dim ** -0.5 for this model; finite, > 0.
  * query_scale         multiplier applied after the normalised query's bf16 cast
  *                     (_qk_norm_rope_core), followed by another bf16 cast.  1.0 is a no-op.
@@ -157,8 +159,7 @@ muse_status muse_rope_cos_sin(float theta, int32_t head_dim, int32_t n_pos, floa
  *                 n_pos >= seqlen (BSHD) or >= max_seqlen (THD).
  * q_rstd, k_rstd  optional fp32 [N, Hq] / [N, Hkv] outputs of r.
  * Errors: INVALID_ARG (see conventions; also when both q and k are NULL or an
- * input is given without its output), UNSUPPORTED (D not in {64,128},
- * upcast_rope == 0), DEVICE.
+ * input is given without its output), UNSUPPORTED (D not in {64,128}), DEVICE.
  */
 muse_status muse_qk_norm_rope(const muse_attn_params *params, const muse_layout *layout,
                               const void *q, const void *k, const float *q_gain,

@@ -147,18 +147,30 @@ def rms_norm(x: np.ndarray, eps: float, gain=None, gain_center: float = 1.0):
 # the original checkpoint computes the rotation in FP32, upcast=True).
 # --------------------------------------------------------------------------
 
-def rope_rotate(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
-    """Rotate each adjacent pair (x_{2i}, x_{2i+1}) by its angle; one bf16 cast.
+def rope_rotate(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, upcast: bool = True) -> np.ndarray:
+    """Rotate each adjacent pair (x_{2i}, x_{2i+1}) by its angle.
 
     ``cos``/``sin`` broadcast against x[..., 0::2].  The rotation is
     (x0*C - x1*S, x0*S + x1*C), RoFormer's 2-D rotation block.
+
+    upcast=True (the original checkpoint, layers page apply_rotary_embedding):
+    the rotation in full precision, one bf16 cast.  upcast=False (the HF
+    release, same section: both products rounded in the Q/K dtype before they
+    are added): C and S cast to bf16, each product rounded to bf16, then the
+    bf16 sum or difference -- every step a bf16 operation.
     """
     x = np.asarray(x, dtype=np.float64)
     x0 = x[..., 0::2]
     x1 = x[..., 1::2]
     y = np.empty_like(x)
-    y[..., 0::2] = round_bf16(x0 * cos - x1 * sin)
-    y[..., 1::2] = round_bf16(x0 * sin + x1 * cos)
+    if upcast:
+        y[..., 0::2] = round_bf16(x0 * cos - x1 * sin)
+        y[..., 1::2] = round_bf16(x0 * sin + x1 * cos)
+    else:
+        c = round_bf16(np.asarray(cos, dtype=np.float64))
+        s = round_bf16(np.asarray(sin, dtype=np.float64))
+        y[..., 0::2] = round_bf16(round_bf16(x0 * c) - round_bf16(x1 * s))
+        y[..., 1::2] = round_bf16(round_bf16(x0 * s) + round_bf16(x1 * c))
     return y
 
 
@@ -209,7 +221,7 @@ class Segments:
 # --------------------------------------------------------------------------
 
 def qk_norm_rope(q, k, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
-                 query_scale=1.0, use_rope=True, cos=None, sin=None):
+                 query_scale=1.0, use_rope=True, cos=None, sin=None, upcast_rope=True):
     """Q [N,Hq,D], K [N,Hkv,D] -> (q_hat, k_hat, q_rstd [N,Hq], k_rstd [N,Hkv]).
 
     ``cos``/``sin`` are the per-token rows [N, D/2] (already indexed by each
@@ -221,8 +233,8 @@ def qk_norm_rope(q, k, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
     if use_rope:
         c = np.asarray(cos, dtype=np.float64)[:, None, :]
         s = np.asarray(sin, dtype=np.float64)[:, None, :]
-        q1 = rope_rotate(q1, c, s)
-        k1 = rope_rotate(k1, c, s)
+        q1 = rope_rotate(q1, c, s, upcast_rope)
+        k1 = rope_rotate(k1, c, s, upcast_rope)
     return q1, k1, q_rstd, k_rstd
 
 
@@ -328,7 +340,7 @@ def out_norm_gate(o, gate, eps):
 
 def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling,
               window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
-              query_scale=1.0, position_ids=None):
+              query_scale=1.0, position_ids=None, upcast_rope=True):
     """Full forward over every row.  Inputs are float64 arrays of bf16 values.
 
     Returns a dict with q_hat, k_hat, q_rstd, k_rstd, o (bf16 values), lse,
@@ -339,7 +351,7 @@ def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling
     cos, sin = rope_cos_sin(theta, d, pos) if use_rope else (None, None)
     q_hat, k_hat, q_rstd, k_rstd = qk_norm_rope(
         q, k, eps=eps, q_gain=q_gain, k_gain=k_gain, gain_center=gain_center,
-        query_scale=query_scale, use_rope=use_rope, cos=cos, sin=sin)
+        query_scale=query_scale, use_rope=use_rope, cos=cos, sin=sin, upcast_rope=upcast_rope)
     o, lse = attention(q_hat, k_hat, v, segments, window=window, scaling=scaling)
     out, o_rstd = out_norm_gate(o, gate, out_eps)
     return dict(q_hat=q_hat, k_hat=k_hat, q_rstd=q_rstd, k_rstd=k_rstd, o=o, lse=lse,
@@ -348,7 +360,7 @@ def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling
 
 def attn_core_rows(q_rows, k, v, gate_rows, segments: Segments, rows, *, num_heads, theta, eps,
                    out_eps, scaling, window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
-                   query_scale=1.0, position_ids=None):
+                   query_scale=1.0, position_ids=None, upcast_rope=True):
     """The full forward for selected (token, head) rows only.
 
     ``q_rows``/``gate_rows`` [R, D] hold the query and gate values of the R
@@ -366,18 +378,18 @@ def attn_core_rows(q_rows, k, v, gate_rows, segments: Segments, rows, *, num_hea
     else:
         kc = ks = qc = qs = None
     q_hat = _q_rows(np.asarray(q_rows, dtype=np.float64), eps, q_gain, gain_center, query_scale,
-                    use_rope, qc, qs)
+                    use_rope, qc, qs, upcast_rope)
     k1, _ = rms_norm(k, eps, k_gain, gain_center)
-    k_hat = rope_rotate(k1, kc[:, None, :], ks[:, None, :]) if use_rope else k1
+    k_hat = rope_rotate(k1, kc[:, None, :], ks[:, None, :], upcast_rope) if use_rope else k1
     o, lse = attention_rows(q_hat, k_hat, v, segments, rows, num_heads=num_heads,
                             window=window, scaling=scaling)
     out, o_rstd = out_norm_gate(o, np.asarray(gate_rows, dtype=np.float64), out_eps)
     return dict(q_hat=q_hat, k_hat=k_hat, o=o, lse=lse, o_rstd=o_rstd, out=out)
 
 
-def _q_rows(q_sel, eps, q_gain, gain_center, query_scale, use_rope, cos, sin):
+def _q_rows(q_sel, eps, q_gain, gain_center, query_scale, use_rope, cos, sin, upcast_rope=True):
     q1, _ = rms_norm(q_sel, eps, q_gain, gain_center)
     q1 = round_bf16(q1 * np.float64(round_f32(query_scale)))
     if use_rope:
-        q1 = rope_rotate(q1, cos, sin)
+        q1 = rope_rotate(q1, cos, sin, upcast_rope)
     return q1

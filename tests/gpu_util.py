@@ -93,14 +93,17 @@ class Case:
                     scaling=self.scaling, window=self.x["window"], use_rope=self.x["use_rope"],
                     q_gain=self.x["q_gain"].astype(np.float64),
                     k_gain=self.x["k_gain"].astype(np.float64),
-                    query_scale=self.params.query_scale, gain_center=self.params.gain_center)
+                    query_scale=self.params.query_scale, gain_center=self.params.gain_center,
+                    upcast_rope=bool(self.params.upcast_rope))
 
 
-def make_case(w: W.Workload, layer: int = 0, *, query_scale: float = 1.0, device="cuda") -> Case:
+def make_case(w: W.Workload, layer: int = 0, *, query_scale: float = 1.0, upcast_rope: bool = True,
+              device="cuda") -> Case:
     x = W.make_layer_inputs(w, layer)
     params = m.AttnParams(head_dim=w.head_dim, num_heads=w.num_heads,
                           num_key_value_heads=w.num_kv_heads, sliding_window=x["window"],
-                          use_rope=x["use_rope"], scaling=float(np.float32(w.head_dim ** -0.5)),
+                          use_rope=x["use_rope"], upcast_rope=upcast_rope,
+                          scaling=float(np.float32(w.head_dim ** -0.5)),
                           query_scale=query_scale, qk_eps=EPS, out_eps=EPS)
     if w.is_thd:
         cu = torch.from_numpy(x["cu_seqlens"]).to(device)

@@ -203,6 +203,36 @@ def test_rope_rotation_is_complex_multiplication():
     np.testing.assert_array_equal(y[:, 1::2], _bf16(z.imag))
 
 
+def test_rope_v2_is_bf16_arithmetic_of_torch():
+    # layers page, apply_rotary_embedding (upcast=False, the HF release): both
+    # products rounded in the Q/K dtype before they are added.  PyTorch's own
+    # bf16 tensor arithmetic (each op rounded to bf16) is the reference.
+    rng = np.random.default_rng(17)
+    x = _bf16(rng.standard_normal((64, 64)) * 3.0)
+    ang = rng.uniform(-300, 300, (64, 32))
+    c, s = np.cos(ang), np.sin(ang)
+    y = O.rope_rotate(x, c, s, upcast=False)
+    tb = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16)
+    x0, x1, tc, ts = tb(x[:, 0::2]), tb(x[:, 1::2]), tb(c), tb(s)
+    np.testing.assert_array_equal(y[:, 0::2], (x0 * tc - x1 * ts).double().numpy())
+    np.testing.assert_array_equal(y[:, 1::2], (x0 * ts + x1 * tc).double().numpy())
+
+
+def test_rope_v2_identity_at_position_zero_and_close_to_fp32_rotation():
+    rng = np.random.default_rng(18)
+    x = _bf16(rng.standard_normal((64, 4, 128)))
+    c, s = O.rope_cos_sin(5.0e5, 128, np.zeros(64))
+    np.testing.assert_array_equal(O.rope_rotate(x, c[:, None], s[:, None], upcast=False), x)
+    c, s = O.rope_cos_sin(5.0e5, 128, np.arange(64) * 97)
+    y1 = O.rope_rotate(x, c[:, None], s[:, None])
+    y2 = O.rope_rotate(x, c[:, None], s[:, None], upcast=False)
+    # the v2 path rounds C, S, both products and the sum: a few bf16 ulps of the pair norm
+    nrm = np.sqrt(x[..., 0::2] ** 2 + x[..., 1::2] ** 2)
+    for j in (0, 1):
+        assert np.all(np.abs(y2[..., j::2] - y1[..., j::2]) <= 4 * 2.0 ** -8 * nrm + 1e-30)
+    assert np.mean(y2 != y1) > 0.05      # and it is a different rounding, not the FP32 path
+
+
 def test_rope_adjacent_pair_equals_split_half_after_row_permutation():
     # adapter page, _permute_rope_rows: adjacent-pair and split-half RoPE differ
     # by a permutation of head rows.  Split-half uses rotate_half(x) = [-x2, x1].

@@ -82,7 +82,7 @@ def test_qk_norm_rope_stage(w):
     rq, rk, rqr, rkr = O.qk_norm_rope(bits_f64(case.x["q"]), bits_f64(case.x["k"]), eps=EPS,
                                       q_gain=kw["q_gain"], k_gain=kw["k_gain"],
                                       query_scale=kw["query_scale"], use_rope=kw["use_rope"],
-                                      cos=c, sin=s)
+                                      cos=c, sin=s, upcast_rope=kw["upcast_rope"])
     sq = check_bf16(f64(q_hat), rq, what="q_hat")
     sk = check_bf16(f64(k_hat), rk, what="k_hat")
     assert sq["exact"] > 0.999 and sk["exact"] > 0.999, (sq, sk)
@@ -136,6 +136,53 @@ def test_fused_core_matches_oracle_and_unfused_chain(w):
                         window=case.x["window"], scaling=case.scaling)
     check_fp32(f64(lse_f), rl, floor=1.0, what="fused lse")
     # fused == unfused chain, bit for bit
+    assert torch.equal(k_hat_f.view(torch.int16), k_hat.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), out_u.view(torch.int16))
+    assert torch.equal(lse_f, lse)
+
+
+# ---------------------------------------------------------------- v2 RoPE (upcast_rope = 0)
+
+V2 = [SMALL[1], SMALL[2], SMALL[5], SMALL[6], SMALL[8]]
+V2_IDS = [w.name for w in V2]
+
+
+@pytest.mark.parametrize("w", V2, ids=V2_IDS)
+def test_qk_norm_rope_stage_v2_rotation(w):
+    # rotation in the Q/K dtype: C, S, both products and the sum rounded to bf16
+    case = make_case(w, upcast_rope=False, query_scale=0.75 if w.name == "bshd_b2_s200_g4" else 1.0)
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, case.layout, case.q, case.k, case.q_gain,
+                                             case.k_gain, case.cos, case.sin)
+    torch.cuda.synchronize()
+    kw = case.oracle_kw()
+    c, s = O.rope_cos_sin(w.theta, w.head_dim, case.segs.local_positions())
+    rq, rk, _, _ = O.qk_norm_rope(bits_f64(case.x["q"]), bits_f64(case.x["k"]), eps=EPS,
+                                  q_gain=kw["q_gain"], k_gain=kw["k_gain"],
+                                  query_scale=kw["query_scale"], use_rope=True, cos=c, sin=s,
+                                  upcast_rope=False)
+    sq = check_bf16(f64(q_hat), rq, what="q_hat v2")
+    sk = check_bf16(f64(k_hat), rk, what="k_hat v2")
+    assert sq["exact"] > 0.999 and sk["exact"] > 0.999, (sq, sk)
+    # and it is not the FP32 rotation
+    rq1, _, _, _ = O.qk_norm_rope(bits_f64(case.x["q"]), bits_f64(case.x["k"]), eps=EPS,
+                                  q_gain=kw["q_gain"], k_gain=kw["k_gain"],
+                                  query_scale=kw["query_scale"], use_rope=True, cos=c, sin=s)
+    assert np.mean(f64(q_hat) != rq1) > 0.01
+
+
+@pytest.mark.parametrize("w", V2, ids=V2_IDS)
+def test_fused_core_v2_rotation(w):
+    case = make_case(w, upcast_rope=False, query_scale=0.75 if w.name == "thd_g3_mixed" else 1.0)
+    out, k_hat_f, lse_f = m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v,
+                                               case.gate, case.q_gain, case.k_gain, case.cos,
+                                               case.sin, want_lse=True)
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, case.layout, case.q, case.k, case.q_gain,
+                                             case.k_gain, case.cos, case.sin)
+    o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    out_u, _ = m.muse_out_norm_gate(case.params, case.layout, o, case.gate)
+    torch.cuda.synchronize()
+    ref = _oracle_full(case)
+    check_bf16(f64(out), ref["out"], what="fused out v2")
     assert torch.equal(k_hat_f.view(torch.int16), k_hat.view(torch.int16))
     assert torch.equal(out.view(torch.int16), out_u.view(torch.int16))
     assert torch.equal(lse_f, lse)
