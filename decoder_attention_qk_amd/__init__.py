@@ -47,7 +47,7 @@ class c_params(ctypes.Structure):
                 ("use_rope", ctypes.c_int32), ("upcast_rope", ctypes.c_int32),
                 ("scaling", ctypes.c_float), ("query_scale", ctypes.c_float),
                 ("qk_eps", ctypes.c_float), ("out_eps", ctypes.c_float),
-                ("gain_center", ctypes.c_float)]
+                ("gain_center", ctypes.c_float), ("bidirectional", ctypes.c_int32)]
 
 
 class c_layout(ctypes.Structure):
@@ -129,13 +129,14 @@ class AttnParams:
     qk_eps: float = 1e-6
     out_eps: float = 1e-6
     gain_center: float = 1.0
+    bidirectional: bool = False           # packed bidirectional attention (no causal order)
 
     def to_c(self) -> c_params:
         scale = self.head_dim ** -0.5 if self.scaling is None else self.scaling
         return c_params(self.head_dim, self.num_heads, self.num_key_value_heads,
                         int(self.sliding_window or 0), int(bool(self.use_rope)),
                         int(bool(self.upcast_rope)), scale, self.query_scale, self.qk_eps,
-                        self.out_eps, self.gain_center)
+                        self.out_eps, self.gain_center, int(bool(self.bidirectional)))
 
 
 @dataclasses.dataclass

@@ -73,6 +73,8 @@ muse_status check_params(const muse_attn_params *p) {
   if (!finite(p->qk_eps) || p->qk_eps < 0.0f || !finite(p->out_eps) || p->out_eps < 0.0f)
     return set_error(MUSE_ERR_INVALID_ARG, "qk_eps/out_eps must be finite and >= 0");
   if (!finite(p->gain_center)) return set_error(MUSE_ERR_INVALID_ARG, "gain_center must be finite");
+  if (p->bidirectional && p->sliding_window > 0)
+    return set_error(MUSE_ERR_INVALID_ARG, "a sliding window applies to causal attention only");
   if (p->head_dim != 64 && p->head_dim != 128)
     return set_error(MUSE_ERR_UNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", p->head_dim);
   return MUSE_OK;
@@ -188,6 +190,7 @@ AttnArgs attn_args(const muse_attn_params *p, const muse_layout *l, const Geomet
   a.group = g.group;
   attn_shape(g.group, &a.heads_per_wg, &a.tok_per_wg, &a.head_chunks);
   a.window = p->sliding_window > 0 ? p->sliding_window : 0;
+  a.bidirectional = p->bidirectional ? 1 : 0;
   a.q_blocks = (g.maxlen + a.tok_per_wg - 1) / a.tok_per_wg;
   a.lay = token_layout(l, g);
   return a;

@@ -301,14 +301,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   float l_run = 0.0f;
 
   const int W = a.window;
+  const bool bidir = a.bidirectional != 0;
   const float c2 = a.scale_log2;
 
   // called with literal buffer indices so LDS offsets fold into immediates
   auto compute = [&](int kt, int BUF) __attribute__((always_inline)) {
     const int k0 = kt * BN;
-    const bool none_visible = !wave_active || (k0 > q1w - 1) || (W > 0 && k0 + BN - 1 <= q0w - W);
+    // bidirectional: every key of the segment (the last tile may end past it)
+    const bool none_visible = !wave_active || (!bidir && ((k0 > q1w - 1) || (W > 0 && k0 + BN - 1 <= q0w - W)));
     if (none_visible) return;
-    const bool all_visible = (k0 + BN - 1 <= q0w) && (W <= 0 || k0 > q1w - 1 - W);
+    const bool all_visible = bidir ? k0 + BN <= L : (k0 + BN - 1 <= q0w) && (W <= 0 || k0 > q1w - 1 - W);
     const lds_char *Kt = kbuf(BUF);
     const lds_char *Vt = vbuf(BUF);
 
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kp = k0 + half * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        if (!(kp <= qpos && (W <= 0 || kp > qpos - W))) sv[i] = -INFINITY;
+        if (!(bidir ? kp < L : kp <= qpos && (W <= 0 || kp > qpos - W))) sv[i] = -INFINITY;
       }
     };
     // row max of both halves (a tree, for short dependency chains), folded
@@ -410,9 +412,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     pv(1, pb0, pb1);
   };
 
-  const int lo = W > 0 ? max(0, q0 - W + 1) : 0;
+  const int lo = W > 0 && !bidir ? max(0, q0 - W + 1) : 0;
   const int kt_lo = lo / BN;
-  const int kt_hi = (q1 - 1) / BN;
+  const int kt_hi = ((bidir ? L : q1) - 1) / BN;
   const int ntiles = kt_hi - kt_lo + 1;
 
   issue_dma(kt_hi, 0);

@@ -86,6 +86,7 @@ struct AttnArgs {
   int32_t head_chunks;     // group / heads_per_wg
   int32_t tok_per_wg;      // query tokens per workgroup (tok_per_wg * heads_per_wg <= columns)
   int32_t window;          // <= 0: none
+  int32_t bidirectional;   // every key of the segment is visible (no causal order, no window)
   int32_t q_blocks;        // ceil(max segment length / tok_per_wg)
   TokenLayout lay;
 };

@@ -80,6 +80,11 @@ typedef enum {
  * qk_eps, out_eps     RMSNorm stabilisers added to the mean square (finite, >= 0).
  * gain_center         zero-centred gain offset: effective gain = gain_center + g
  *                     (MuseSparkRMSNorm gain_center, 1.0 by default).
+ * bidirectional       non-zero: every key of the query's own row/segment is
+ *                     visible, no causal order (vision page,
+ *                     MuseSparkVisionAttention: packed bidirectional attention);
+ *                     requires sliding_window <= 0.  Zero (the default of a
+ *                     zero-initialised struct): causal.
  */
 typedef struct {
   int32_t head_dim;
@@ -93,6 +98,7 @@ typedef struct {
   float qk_eps;
   float out_eps;
   float gain_center;
+  int32_t bidirectional;
 } muse_attn_params;
 
 /*

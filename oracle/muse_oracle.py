@@ -15,7 +15,9 @@ What it computes is defined by the NeMo AutoModel API reference pages for the
 * "model page" -- ``nemo_automodel.components.models.muse_spark.model``
   (section ``_causal_mask``);
 * "adapter page" -- ``nemo_automodel.components.models.muse_spark.hf_state_dict_adapter``
-  (section ``_permute_rope_rows``).
+  (section ``_permute_rope_rows``);
+* "vision page" -- ``nemo_automodel.components.models.muse_spark.vision``
+  (section ``MuseSparkVisionAttention``: packed bidirectional attention).
 
 The method is a composition of exact definitions (no approximation, heuristic
 or iteration), so every function below is that definition written out in
@@ -28,7 +30,8 @@ RMS over the last dim per (token, head); eps inside the square root; effective
 gain ``f32(gain_center + g)`` applied after normalisation and before the cast;
 RoFormer rotation sign with frequencies ``theta**(-2i/D)``; cos/sin of width
 D/2; window ``W`` = number of visible causal keys including the query itself;
-no attention across packed segments; bf16 boundary on the attention output;
+no attention across packed segments (bidirectional mode: every key of the
+query's own segment, no window); bf16 boundary on the attention output;
 sigmoid and output norm in full precision with one final cast.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
@@ -245,20 +248,26 @@ def qk_norm_rope(q, k, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
 # (window = number of causal key positions visible to each query).
 # --------------------------------------------------------------------------
 
-def visible_mask(qpos: np.ndarray, kpos: np.ndarray, window: int) -> np.ndarray:
-    """Key j visible to query i iff j <= i and, with a window W > 0, j > i - W."""
+def visible_mask(qpos: np.ndarray, kpos: np.ndarray, window: int, causal: bool = True) -> np.ndarray:
+    """Key j visible to query i iff j <= i and, with a window W > 0, j > i - W.
+
+    causal=False is the packed bidirectional attention of the vision tower
+    (vision page, MuseSparkVisionAttention): every key of the segment is
+    visible (no window)."""
     i = np.asarray(qpos)[:, None]
     j = np.asarray(kpos)[None, :]
+    if not causal:
+        return np.ones((i.shape[0], j.shape[1]), dtype=bool)
     vis = j <= i
     if window and window > 0:
         vis &= j > i - window
     return vis
 
 
-def _attend_block(qb, kseg, vseg, qpos, window, scaling):
+def _attend_block(qb, kseg, vseg, qpos, window, scaling, causal=True):
     """Softmax attention of query rows qb [m,D] over one segment's keys [L,D]."""
     s = float(scaling) * (qb @ kseg.T)
-    vis = visible_mask(qpos, np.arange(kseg.shape[0]), window)
+    vis = visible_mask(qpos, np.arange(kseg.shape[0]), window, causal)
     s = np.where(vis, s, -np.inf)
     mx = s.max(axis=1, keepdims=True)
     e = np.exp(s - mx)
@@ -267,8 +276,9 @@ def _attend_block(qb, kseg, vseg, qpos, window, scaling):
     return o, mx[:, 0] + np.log(z[:, 0])
 
 
-def attention(q_hat, k_hat, v, segments: Segments, *, window=0, scaling, row_block=2048):
-    """Exact causal GQA softmax attention.  Returns (bf16(o) [N,Hq,D], lse [N,Hq]).
+def attention(q_hat, k_hat, v, segments: Segments, *, window=0, scaling, row_block=2048, causal=True):
+    """Exact causal (or, causal=False, bidirectional) GQA softmax attention.
+    Returns (bf16(o) [N,Hq,D], lse [N,Hq]).
 
     Query head h reads key/value head h // (Hq // Hkv).  lse uses the natural
     log.  Rows outside every segment are left at zero.
@@ -289,13 +299,14 @@ def attention(q_hat, k_hat, v, segments: Segments, *, window=0, scaling, row_blo
             for r0 in range(0, length, row_block):
                 r1 = min(length, r0 + row_block)
                 ob, lb = _attend_block(q_hat[s0 + r0:s0 + r1, h], kseg, vseg,
-                                       np.arange(r0, r1), window, scaling)
+                                       np.arange(r0, r1), window, scaling, causal)
                 o[s0 + r0:s0 + r1, h] = ob
                 lse[s0 + r0:s0 + r1, h] = lb
     return round_bf16(o), lse
 
 
-def attention_rows(q_hat_rows, k_hat, v, segments: Segments, rows, *, num_heads, window=0, scaling):
+def attention_rows(q_hat_rows, k_hat, v, segments: Segments, rows, *, num_heads, window=0, scaling,
+                   causal=True):
     """Attention for selected (token, head) rows only.
 
     ``q_hat_rows`` [len(rows), D] holds the normalised/rotated query of each
@@ -311,7 +322,7 @@ def attention_rows(q_hat_rows, k_hat, v, segments: Segments, rows, *, num_heads,
         g = int(h) // groups
         ob, lb = _attend_block(np.asarray(q_hat_rows[r], dtype=np.float64)[None, :],
                                k_hat[s0:s0 + length, g], v[s0:s0 + length, g],
-                               np.array([int(t) - s0]), window, scaling)
+                               np.array([int(t) - s0]), window, scaling, causal)
         o[r] = ob[0]
         lse[r] = lb[0]
     return round_bf16(o), lse
@@ -340,7 +351,7 @@ def out_norm_gate(o, gate, eps):
 
 def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling,
               window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
-              query_scale=1.0, position_ids=None, upcast_rope=True):
+              query_scale=1.0, position_ids=None, upcast_rope=True, causal=True):
     """Full forward over every row.  Inputs are float64 arrays of bf16 values.
 
     Returns a dict with q_hat, k_hat, q_rstd, k_rstd, o (bf16 values), lse,
@@ -352,7 +363,7 @@ def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling
     q_hat, k_hat, q_rstd, k_rstd = qk_norm_rope(
         q, k, eps=eps, q_gain=q_gain, k_gain=k_gain, gain_center=gain_center,
         query_scale=query_scale, use_rope=use_rope, cos=cos, sin=sin, upcast_rope=upcast_rope)
-    o, lse = attention(q_hat, k_hat, v, segments, window=window, scaling=scaling)
+    o, lse = attention(q_hat, k_hat, v, segments, window=window, scaling=scaling, causal=causal)
     out, o_rstd = out_norm_gate(o, gate, out_eps)
     return dict(q_hat=q_hat, k_hat=k_hat, q_rstd=q_rstd, k_rstd=k_rstd, o=o, lse=lse,
                 o_rstd=o_rstd, out=out)
@@ -360,7 +371,7 @@ def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling
 
 def attn_core_rows(q_rows, k, v, gate_rows, segments: Segments, rows, *, num_heads, theta, eps,
                    out_eps, scaling, window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
-                   query_scale=1.0, position_ids=None, upcast_rope=True):
+                   query_scale=1.0, position_ids=None, upcast_rope=True, causal=True):
     """The full forward for selected (token, head) rows only.
 
     ``q_rows``/``gate_rows`` [R, D] hold the query and gate values of the R
@@ -382,7 +393,7 @@ def attn_core_rows(q_rows, k, v, gate_rows, segments: Segments, rows, *, num_hea
     k1, _ = rms_norm(k, eps, k_gain, gain_center)
     k_hat = rope_rotate(k1, kc[:, None, :], ks[:, None, :], upcast_rope) if use_rope else k1
     o, lse = attention_rows(q_hat, k_hat, v, segments, rows, num_heads=num_heads,
-                            window=window, scaling=scaling)
+                            window=window, scaling=scaling, causal=causal)
     out, o_rstd = out_norm_gate(o, np.asarray(gate_rows, dtype=np.float64), out_eps)
     return dict(q_hat=q_hat, k_hat=k_hat, o=o, lse=lse, o_rstd=o_rstd, out=out)
 

@@ -94,15 +94,15 @@ class Case:
                     q_gain=self.x["q_gain"].astype(np.float64),
                     k_gain=self.x["k_gain"].astype(np.float64),
                     query_scale=self.params.query_scale, gain_center=self.params.gain_center,
-                    upcast_rope=bool(self.params.upcast_rope))
+                    upcast_rope=bool(self.params.upcast_rope), causal=not self.params.bidirectional)
 
 
 def make_case(w: W.Workload, layer: int = 0, *, query_scale: float = 1.0, upcast_rope: bool = True,
-              device="cuda") -> Case:
+              bidirectional: bool = False, device="cuda") -> Case:
     x = W.make_layer_inputs(w, layer)
     params = m.AttnParams(head_dim=w.head_dim, num_heads=w.num_heads,
                           num_key_value_heads=w.num_kv_heads, sliding_window=x["window"],
-                          use_rope=x["use_rope"], upcast_rope=upcast_rope,
+                          use_rope=x["use_rope"], upcast_rope=upcast_rope, bidirectional=bidirectional,
                           scaling=float(np.float32(w.head_dim ** -0.5)),
                           query_scale=query_scale, qk_eps=EPS, out_eps=EPS)
     if w.is_thd:

@@ -91,6 +91,7 @@ def test_null_params_and_layout():
     (dict(num_heads=6, num_key_value_heads=4), 1), (dict(scaling=0.0), 1),
     (dict(scaling=float("nan")), 1), (dict(qk_eps=-1.0), 1), (dict(out_eps=float("inf")), 1),
     (dict(query_scale=float("inf")), 1), (dict(gain_center=float("nan")), 1),
+    (dict(bidirectional=1, sliding_window=8), 1),
     (dict(head_dim=96), 2), (dict(head_dim=256), 2),
 ])
 def test_bad_params(kw, status):

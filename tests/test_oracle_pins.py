@@ -296,9 +296,10 @@ def test_qk_norm_rope_query_scale_and_gain_routing():
 
 # ---------------------------------------------------------------- attention
 
-def _brute_attention(q, k, v, seg_bounds, window, scaling):
+def _brute_attention(q, k, v, seg_bounds, window, scaling, causal=True):
     """Pure-Python softmax attention: query i sees the `window` most recent keys
-    up to and including itself (all earlier keys when window == 0)."""
+    up to and including itself (all earlier keys when window == 0), or, when
+    not causal, every key of its segment."""
     n, hq, d = q.shape
     hkv = k.shape[1]
     o = np.zeros((n, hq, d))
@@ -306,7 +307,7 @@ def _brute_attention(q, k, v, seg_bounds, window, scaling):
     for (s0, length) in seg_bounds:
         for i in range(length):
             first = 0 if window <= 0 else max(0, i - window + 1)
-            keys = list(range(first, i + 1))
+            keys = list(range(first, i + 1)) if causal else list(range(length))
             for h in range(hq):
                 g = h * hkv // hq
                 sc = [scaling * sum(q[s0 + i, h, t] * k[s0 + j, g, t] for t in range(d)) for j in keys]
@@ -346,6 +347,42 @@ def test_attention_brute_force_thd_with_length_one_segments():
         ro, rl = _brute_attention(q, k, v, list(zip(cu[:-1], lens)), window, 0.5)
         np.testing.assert_array_equal(o, _bf16(ro))
         np.testing.assert_allclose(lse, rl, rtol=1e-13, atol=1e-13)
+
+
+def test_bidirectional_attention_brute_force_thd():
+    # vision page, MuseSparkVisionAttention: packed bidirectional attention
+    rng = np.random.default_rng(21)
+    lens = [1, 6, 2, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    n, hq, hkv, d = cu[-1], 4, 2, 5
+    q = _bf16(rng.standard_normal((n, hq, d)))
+    k = _bf16(rng.standard_normal((n, hkv, d)))
+    v = _bf16(rng.standard_normal((n, hkv, d)))
+    o, lse = O.attention(q, k, v, O.Segments.thd(cu), scaling=0.6, causal=False)
+    ro, rl = _brute_attention(q, k, v, list(zip(cu[:-1], lens)), 0, 0.6, causal=False)
+    np.testing.assert_array_equal(o, _bf16(ro))
+    np.testing.assert_allclose(lse, rl, rtol=1e-13, atol=1e-13)
+
+
+def test_bidirectional_attention_invariants():
+    rng = np.random.default_rng(22)
+    sl, hq, d = 12, 2, 8
+    q = _bf16(rng.standard_normal((sl, hq, d)))
+    k = _bf16(rng.standard_normal((sl, 1, d)))
+    v = _bf16(rng.standard_normal((sl, 1, d)))
+    segs = O.Segments.bshd(1, sl)
+    o, lse = O.attention(q, k, v, segs, scaling=0.5, causal=False)
+    # permuting the tokens of a segment permutes the outputs (no order anywhere)
+    perm = rng.permutation(sl)
+    op, lp = O.attention(q[perm], k[perm], v[perm], segs, scaling=0.5, causal=False)
+    np.testing.assert_array_equal(op, o[perm])
+    np.testing.assert_allclose(lp, lse[perm], rtol=1e-13)
+    # the last query of a segment sees every key in both modes
+    oc, lc = O.attention(q, k, v, segs, scaling=0.5)
+    np.testing.assert_array_equal(oc[-1], o[-1])
+    # zero queries: uniform weights over the whole segment -> the mean of V
+    oz, _ = O.attention(np.zeros_like(q), k, v, segs, scaling=0.5, causal=False)
+    np.testing.assert_array_equal(oz[:, 0], np.broadcast_to(_bf16(v[:, 0].mean(axis=0)), (sl, d)))
 
 
 def test_attention_golden_tiny():

@@ -188,6 +188,45 @@ def test_fused_core_v2_rotation(w):
     assert torch.equal(lse_f, lse)
 
 
+# ---------------------------------------------------------------- bidirectional (packed, no causal order)
+
+BIDIR = [SMALL[0], SMALL[1], SMALL[3], SMALL[5], SMALL[8],
+         W.small_workload("thd_bidir_g4", num_heads=8, num_kv_heads=2, head_dim=128,
+                          segment_lengths=(64, 1, 129, 200, 0, 65))]
+BIDIR_IDS = [w.name for w in BIDIR]
+
+
+@pytest.mark.parametrize("w", BIDIR, ids=BIDIR_IDS)
+def test_bidirectional_attention_stage(w):
+    case = make_case(w, bidirectional=True)
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, case.layout, case.q, case.k, case.q_gain,
+                                             case.k_gain, case.cos, case.sin)
+    o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs,
+                         scaling=case.scaling, causal=False)
+    check_bf16(f64(o), ro, what="o bidirectional")
+    check_fp32(f64(lse), rl, floor=1.0, what="lse bidirectional")
+    # and it is not the causal result (the first row of a segment sees every key)
+    rc, _ = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs, scaling=case.scaling)
+    assert np.mean(f64(o) != rc) > 0.5
+
+
+@pytest.mark.parametrize("w", BIDIR, ids=BIDIR_IDS)
+def test_bidirectional_fused_core(w):
+    case = make_case(w, bidirectional=True)
+    out, _, lse_f = m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v, case.gate,
+                                         case.q_gain, case.k_gain, case.cos, case.sin, want_lse=True)
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, case.layout, case.q, case.k, case.q_gain,
+                                             case.k_gain, case.cos, case.sin)
+    o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    out_u, _ = m.muse_out_norm_gate(case.params, case.layout, o, case.gate)
+    torch.cuda.synchronize()
+    check_bf16(f64(out), _oracle_full(case)["out"], what="fused out bidirectional")
+    assert torch.equal(out.view(torch.int16), out_u.view(torch.int16))
+    assert torch.equal(lse_f, lse)
+
+
 # ---------------------------------------------------------------- bit-exact invariants
 
 def test_window_one_returns_v_exactly():
