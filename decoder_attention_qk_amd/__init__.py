@@ -17,9 +17,9 @@ import os
 
 __all__ = [
     "MuseError", "AttnParams", "Layout", "library", "library_path", "symbols",
-    "muse_rope_cos_sin", "muse_qk_norm_rope", "muse_gqa_attn_fwd", "muse_out_norm_gate",
-    "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_validate_cu_seqlens", "muse_status_string",
-    "muse_version",
+    "muse_rope_cos_sin", "muse_rope_cos_sin_2d", "muse_qk_norm_rope", "muse_gqa_attn_fwd",
+    "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_validate_cu_seqlens",
+    "muse_status_string", "muse_version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,7 @@ MUSE_OK, MUSE_ERR_INVALID_ARG, MUSE_ERR_UNSUPPORTED, MUSE_ERR_DEVICE = 0, 1, 2, 
 
 # Every symbol include/muse_attn.h declares.
 symbols = (
-    "muse_rope_cos_sin", "muse_qk_norm_rope", "muse_gqa_attn_fwd", "muse_out_norm_gate",
+    "muse_rope_cos_sin", "muse_rope_cos_sin_2d", "muse_qk_norm_rope", "muse_gqa_attn_fwd", "muse_out_norm_gate",
     "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_validate_cu_seqlens", "muse_status_string",
     "muse_last_error", "muse_version",
 )
@@ -47,20 +47,22 @@ class c_params(ctypes.Structure):
                 ("use_rope", ctypes.c_int32), ("upcast_rope", ctypes.c_int32),
                 ("scaling", ctypes.c_float), ("query_scale", ctypes.c_float),
                 ("qk_eps", ctypes.c_float), ("out_eps", ctypes.c_float),
-                ("gain_center", ctypes.c_float), ("bidirectional", ctypes.c_int32)]
+                ("gain_center", ctypes.c_float), ("bidirectional", ctypes.c_int32),
+                ("skip_qk_norm", ctypes.c_int32)]
 
 
 class c_layout(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("cu_seqlens", ctypes.c_void_p), ("num_segments", ctypes.c_int32),
                 ("total_tokens", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
-                ("position_ids", ctypes.c_void_p)]
+                ("position_ids", ctypes.c_void_p), ("attention_mask", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _SIGS = {
     "muse_rope_cos_sin": [ctypes.c_float, _I32, _I32, _P, _P, _P],
+    "muse_rope_cos_sin_2d": [ctypes.c_float, _I32, _I32, _I32, _P, _P, _P],
     "muse_qk_norm_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P],
     "muse_gqa_attn_fwd": [_P, _P, _P, _P, _P, _P, _P, _P],
     "muse_out_norm_gate": [_P, _P, _P, _P, _P, _P, _P],
@@ -130,13 +132,15 @@ class AttnParams:
     out_eps: float = 1e-6
     gain_center: float = 1.0
     bidirectional: bool = False           # packed bidirectional attention (no causal order)
+    skip_qk_norm: bool = False            # muse_qk_norm_rope: scale/rotate only (vision attention)
 
     def to_c(self) -> c_params:
         scale = self.head_dim ** -0.5 if self.scaling is None else self.scaling
         return c_params(self.head_dim, self.num_heads, self.num_key_value_heads,
                         int(self.sliding_window or 0), int(bool(self.use_rope)),
                         int(bool(self.upcast_rope)), scale, self.query_scale, self.qk_eps,
-                        self.out_eps, self.gain_center, int(bool(self.bidirectional)))
+                        self.out_eps, self.gain_center, int(bool(self.bidirectional)),
+                        int(bool(self.skip_qk_norm)))
 
 
 @dataclasses.dataclass
@@ -149,10 +153,11 @@ class Layout:
     max_seqlen: int = 0
     position_ids: object = None           # optional torch.int32 device tensor [N]
     total_tokens: int | None = None       # THD: cu_seqlens[-1] (read from the device if None)
+    attention_mask: object = None         # optional BSHD token validity [batch, seqlen] (bool/uint8)
 
     @classmethod
-    def bshd(cls, batch: int, seqlen: int, position_ids=None) -> "Layout":
-        return cls(batch=batch, seqlen=seqlen, position_ids=position_ids)
+    def bshd(cls, batch: int, seqlen: int, position_ids=None, attention_mask=None) -> "Layout":
+        return cls(batch=batch, seqlen=seqlen, position_ids=position_ids, attention_mask=attention_mask)
 
     @classmethod
     def thd(cls, cu_seqlens, max_seqlen: int, position_ids=None, total_tokens=None) -> "Layout":
@@ -170,9 +175,11 @@ class Layout:
             _expect(self.cu_seqlens, "cu_seqlens", "int32")
             nseg = self.cu_seqlens.numel() - 1
             return c_layout(0, 0, self.cu_seqlens.data_ptr(), nseg, self._total, self.max_seqlen,
-                            _ptr(self.position_ids, "position_ids", "int32"))
+                            _ptr(self.position_ids, "position_ids", "int32"),
+                            _ptr(self.attention_mask, "attention_mask", "mask"))
         return c_layout(self.batch, self.seqlen, None, self.batch, 0, 0,
-                        _ptr(self.position_ids, "position_ids", "int32"))
+                        _ptr(self.position_ids, "position_ids", "int32"),
+                        _ptr(self.attention_mask, "attention_mask", "mask"))
 
     @property
     def _total(self) -> int:
@@ -185,9 +192,10 @@ class Layout:
 
 def _expect(t, name, dtype):
     import torch
-    want = {"bf16": torch.bfloat16, "fp32": torch.float32, "int32": torch.int32}[dtype]
-    if t.dtype != want:
-        raise TypeError(f"{name}: expected {want}, got {t.dtype}")
+    want = {"bf16": (torch.bfloat16,), "fp32": (torch.float32,), "int32": (torch.int32,),
+            "mask": (torch.bool, torch.uint8)}[dtype]
+    if t.dtype not in want:
+        raise TypeError(f"{name}: expected {' or '.join(map(str, want))}, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name}: expected a GPU tensor")
     if not t.is_contiguous():
@@ -224,6 +232,22 @@ def muse_rope_cos_sin(theta, head_dim, n_pos, cos_out=None, sin_out=None, *, dev
     _check(library().muse_rope_cos_sin(float(theta), int(head_dim), int(n_pos),
                                        _ptr(cos_out, "cos_out", "fp32"),
                                        _ptr(sin_out, "sin_out", "fp32"), _stream(stream)))
+    return cos_out, sin_out
+
+
+def muse_rope_cos_sin_2d(theta, head_dim, grid_h, grid_w, cos_out=None, sin_out=None, *, device=None,
+                         stream=None):
+    """FP32 2-D cos/sin table [grid_h*grid_w, head_dim/2] of a row-major patch grid."""
+    import torch
+    dev = device if device is not None else (cos_out.device if cos_out is not None else "cuda")
+    n = int(grid_h) * int(grid_w)
+    if cos_out is None:
+        cos_out = torch.empty((n, head_dim // 2), dtype=torch.float32, device=dev)
+    if sin_out is None:
+        sin_out = torch.empty((n, head_dim // 2), dtype=torch.float32, device=dev)
+    _check(library().muse_rope_cos_sin_2d(float(theta), int(head_dim), int(grid_h), int(grid_w),
+                                          _ptr(cos_out, "cos_out", "fp32"),
+                                          _ptr(sin_out, "sin_out", "fp32"), _stream(stream)))
     return cos_out, sin_out
 
 

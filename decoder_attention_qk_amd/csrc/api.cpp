@@ -100,6 +100,8 @@ muse_status check_layout(const muse_layout *l, const muse_attn_params *p, hipStr
       return set_error(MUSE_ERR_INVALID_ARG, "max_seqlen %d > total_tokens %d", l->max_seqlen, l->total_tokens);
     if (l->total_tokens > 0 && l->max_seqlen < 1)
       return set_error(MUSE_ERR_INVALID_ARG, "max_seqlen must be >= 1 when total_tokens > 0");
+    if (l->attention_mask)
+      return set_error(MUSE_ERR_INVALID_ARG, "attention_mask is for BSHD; packed THD carries no padding");
     g->thd = true;
     g->n_tokens = l->total_tokens;
     g->nseg = l->num_segments;
@@ -140,6 +142,7 @@ TokenLayout token_layout(const muse_layout *l, const Geometry &g) {
 
 Range layout_range(const muse_layout *l, const Geometry &g, int which) {
   if (which == 0) return Range{g.thd ? l->cu_seqlens : nullptr, ((int64_t)g.nseg + 1) * 4, "cu_seqlens", 4};
+  if (which == 2) return Range{l->attention_mask, g.n_tokens, "attention_mask", 1};
   return Range{l->position_ids, g.n_tokens * 4, "position_ids", 4};
 }
 
@@ -191,6 +194,7 @@ AttnArgs attn_args(const muse_attn_params *p, const muse_layout *l, const Geomet
   attn_shape(g.group, &a.heads_per_wg, &a.tok_per_wg, &a.head_chunks);
   a.window = p->sliding_window > 0 ? p->sliding_window : 0;
   a.bidirectional = p->bidirectional ? 1 : 0;
+  a.key_valid = g.thd ? nullptr : l->attention_mask;
   a.q_blocks = (g.maxlen + a.tok_per_wg - 1) / a.tok_per_wg;
   a.lay = token_layout(l, g);
   return a;
@@ -213,8 +217,25 @@ extern "C" muse_status muse_rope_cos_sin(float theta, int32_t head_dim, int32_t 
   const int64_t bytes = (int64_t)n_pos * (head_dim / 2) * 4;
   muse_status s = check_disjoint({}, {{cos_out, bytes, "cos_out"}, {sin_out, bytes, "sin_out"}});
   if (s != MUSE_OK) return s;
-  RopeTableArgs a{theta, head_dim, n_pos, cos_out, sin_out};
+  RopeTableArgs a{theta, head_dim, n_pos, cos_out, sin_out, 0};
   return device_status(launch_rope_table(a, (hipStream_t)stream), "rope table launch");
+}
+
+extern "C" muse_status muse_rope_cos_sin_2d(float theta, int32_t head_dim, int32_t grid_h, int32_t grid_w,
+                                            float *cos_out, float *sin_out, void *stream) {
+  if (!std::isfinite(theta) || theta <= 0.0f) return set_error(MUSE_ERR_INVALID_ARG, "theta must be finite and > 0");
+  if (head_dim <= 0 || (head_dim & 3))
+    return set_error(MUSE_ERR_INVALID_ARG, "head_dim %d must be a positive multiple of 4", head_dim);
+  if (grid_h < 0 || grid_w < 0) return set_error(MUSE_ERR_INVALID_ARG, "grid %d x %d is negative", grid_h, grid_w);
+  const int64_t n_pos = (int64_t)grid_h * grid_w;
+  if (n_pos > INT32_MAX) return set_error(MUSE_ERR_INVALID_ARG, "grid %d x %d exceeds 2^31 - 1 patches", grid_h, grid_w);
+  if (n_pos == 0) { clear_error(); return MUSE_OK; }
+  if (!cos_out || !sin_out) return set_error(MUSE_ERR_INVALID_ARG, "cos_out/sin_out is NULL");
+  const int64_t bytes = n_pos * (head_dim / 2) * 4;
+  muse_status s = check_disjoint({}, {{cos_out, bytes, "cos_out"}, {sin_out, bytes, "sin_out"}});
+  if (s != MUSE_OK) return s;
+  RopeTableArgs a{theta, head_dim, (int32_t)n_pos, cos_out, sin_out, grid_w};
+  return device_status(launch_rope_table(a, (hipStream_t)stream), "2-D rope table launch");
 }
 
 extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_layout *l, const void *q,
@@ -231,6 +252,8 @@ extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_l
   if (!q && !k) return set_error(MUSE_ERR_INVALID_ARG, "neither q nor k given");
   if (!q && q_rstd) return set_error(MUSE_ERR_INVALID_ARG, "q_rstd given without q");
   if (!k && k_rstd) return set_error(MUSE_ERR_INVALID_ARG, "k_rstd given without k");
+  if (p->skip_qk_norm && (q_gain || k_gain || q_rstd || k_rstd))
+    return set_error(MUSE_ERR_INVALID_ARG, "skip_qk_norm takes no gains and no rstd outputs");
   s = check_rope_table(p, l, g, cos, sin, n_pos);
   if (s != MUSE_OK) return s;
   const int64_t N = g.n_tokens;
@@ -267,6 +290,7 @@ extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_l
   a.query_scale = p->query_scale;
   a.use_rope = p->use_rope ? 1 : 0;
   a.rope_v2 = p->upcast_rope ? 0 : 1;
+  a.skip_norm = p->skip_qk_norm ? 1 : 0;
   a.lay = token_layout(l, g);
   return device_status(launch_qk_norm_rope(g.d, a, (hipStream_t)stream), "qk_norm_rope launch");
 }
@@ -282,7 +306,8 @@ extern "C" muse_status muse_gqa_attn_fwd(const muse_attn_params *p, const muse_l
   if (N > 0 && (!q_hat || !k_hat || !v || !o))
     return set_error(MUSE_ERR_INVALID_ARG, "q_hat, k_hat, v and o are required");
   s = check_disjoint({{q_hat, bf16_bytes(N, g.hq, g.d), "q_hat"}, {k_hat, bf16_bytes(N, g.hkv, g.d), "k_hat"},
-                      {v, bf16_bytes(N, g.hkv, g.d), "v"}, layout_range(l, g, 0), layout_range(l, g, 1)},
+                      {v, bf16_bytes(N, g.hkv, g.d), "v"}, layout_range(l, g, 0), layout_range(l, g, 1),
+                      layout_range(l, g, 2)},
                      {{o, bf16_bytes(N, g.hq, g.d), "o"}, {lse, N * g.hq * 4, "lse", 4}});
   if (s != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
@@ -318,6 +343,7 @@ extern "C" muse_status muse_attn_fused_fwd(const muse_attn_params *p, const muse
                                            int32_t n_pos, void *out, float *lse, void *stream) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
+  if (p->skip_qk_norm) return set_error(MUSE_ERR_UNSUPPORTED, "the fused core normalises Q; skip_qk_norm is for muse_qk_norm_rope");
   Geometry g;
   s = check_layout(l, p, (hipStream_t)stream, &g);
   if (s != MUSE_OK) return s;
@@ -330,7 +356,7 @@ extern "C" muse_status muse_attn_fused_fwd(const muse_attn_params *p, const muse
   s = check_disjoint({{q, bf16_bytes(N, g.hq, g.d), "q"}, {k_hat, bf16_bytes(N, g.hkv, g.d), "k_hat"},
                       {v, bf16_bytes(N, g.hkv, g.d), "v"}, {gate, bf16_bytes(N, g.hq, g.d), "gate"},
                       {q_gain, g.d * 4, "q_gain"}, {cos, tab, "cos"}, {sin, tab, "sin"},
-                      layout_range(l, g, 0), layout_range(l, g, 1)},
+                      layout_range(l, g, 0), layout_range(l, g, 1), layout_range(l, g, 2)},
                      {{out, bf16_bytes(N, g.hq, g.d), "out"}, {lse, N * g.hq * 4, "lse", 4}});
   if (s != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
@@ -354,6 +380,7 @@ extern "C" muse_status muse_attn_core_fwd(const muse_attn_params *p, const muse_
                                           void *k_hat_out, void *out, float *lse, void *stream) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
+  if (p->skip_qk_norm) return set_error(MUSE_ERR_UNSUPPORTED, "the fused core normalises Q/K; skip_qk_norm is for muse_qk_norm_rope");
   Geometry g;
   s = check_layout(l, p, (hipStream_t)stream, &g);
   if (s != MUSE_OK) return s;
@@ -366,7 +393,8 @@ extern "C" muse_status muse_attn_core_fwd(const muse_attn_params *p, const muse_
   s = check_disjoint(
       {{q, bf16_bytes(N, g.hq, g.d), "q"}, {k, bf16_bytes(N, g.hkv, g.d), "k"}, {v, bf16_bytes(N, g.hkv, g.d), "v"},
        {gate, bf16_bytes(N, g.hq, g.d), "gate"}, {q_gain, g.d * 4, "q_gain"}, {k_gain, g.d * 4, "k_gain"},
-       {cos, tab, "cos"}, {sin, tab, "sin"}, layout_range(l, g, 0), layout_range(l, g, 1)},
+       {cos, tab, "cos"}, {sin, tab, "sin"}, layout_range(l, g, 0), layout_range(l, g, 1),
+       layout_range(l, g, 2)},
       {{k_hat_out, bf16_bytes(N, g.hkv, g.d), "k_hat_out"}, {out, bf16_bytes(N, g.hq, g.d), "out"},
        {lse, N * g.hq * 4, "lse", 4}});
   if (s != MUSE_OK) return s;

@@ -38,7 +38,11 @@
 // element mask.  Softmax keeps a lagging reference max that moves only when a
 // tile exceeds it by kRescaleSlackLog2 (log2 units), so the O rescale runs on
 // few tiles; probabilities stay below 2^kRescaleSlackLog2 and the final
-// division by the running sum removes the reference.
+// division by the running sum removes the reference.  Bidirectional mode
+// (vision page, MuseSparkVisionAttention) sees every key of the segment;
+// padded keys of a BSHD batch (model page, MuseSparkTextModel.forward
+// attention_mask) are masked per tile, and a query left with no key gives
+// the zero row.
 #include <cmath>
 
 #include "device_common.hpp"
@@ -96,7 +100,9 @@ __device__ __forceinline__ void vmem_wait_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
 }
 
-template <int D, bool FUSED>
+// PAD: keys may be padding (a.key_valid given); a separate instantiation so
+// the unpadded kernel carries none of its registers.
+template <int D, bool FUSED, bool PAD>
 __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   using T = Tile<D>;
   constexpr int KS = D / 16;   // QK^T k-steps
@@ -278,8 +284,21 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     }
   }
 
+  // Padded keys (BSHD attention_mask): each lane fetches the validity byte of
+  // one key of the tile together with the tile's DMA, so it has arrived by
+  // the barrier before the tile is computed; after that barrier a ballot
+  // turns the 64 bytes into a wave-uniform key mask (scalar registers), and
+  // the byte register is free for the next tile's fetch.
+  const uint8_t *kvalid = a.key_valid + s0;   // read only when PAD
+  int vbyte = 1;
+  uint64_t kmask = ~0ull;   // bit j: key k0 + j of the current tile is not padding
+  auto take_mask = [&]() __attribute__((always_inline)) {
+    if constexpr (PAD) kmask = __ballot(vbyte != 0);
+  };
+
   auto issue_dma = [&](int kt, int buf) {
     const int k0 = kt * BN;
+    if constexpr (PAD) vbyte = k0 + lane < L ? (int)kvalid[k0 + lane] : 0;
     lds_char *kdst = kbuf(buf) + wave * T::DMA_PER_WAVE * 1024;
     lds_char *vdst = vbuf(buf) + wave * T::DMA_PER_WAVE * 1024;
     // the tile's rows k0 .. L-1 of this kv head; rows past the segment read as zeros
@@ -311,6 +330,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     const bool none_visible = !wave_active || (!bidir && ((k0 > q1w - 1) || (W > 0 && k0 + BN - 1 <= q0w - W)));
     if (none_visible) return;
     const bool all_visible = bidir ? k0 + BN <= L : (k0 + BN - 1 <= q0w) && (W <= 0 || k0 > q1w - 1 - W);
+    const bool padded = PAD && kmask != ~0ull;
     const lds_char *Kt = kbuf(BUF);
     const lds_char *Vt = vbuf(BUF);
 
@@ -333,10 +353,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       return acc;
     };
     auto mask = [&](f32x16 &sv, int half) __attribute__((always_inline)) {
+      // this lane's keys of the half as bits at compile-time positions
+      // (8 (i/4) + i%4) of one 32-bit word
+      const uint32_t kbits = (uint32_t)(kmask >> (half * 32 + g * 4));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kp = k0 + half * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        if (!(bidir ? kp < L : kp <= qpos && (W <= 0 || kp > qpos - W))) sv[i] = -INFINITY;
+        bool vis = bidir ? kp < L : kp <= qpos && (W <= 0 || kp > qpos - W);
+        if (padded) vis = vis && ((kbits >> ((i >> 2) * 8 + (i & 3))) & 1u);
+        if (!vis) sv[i] = -INFINITY;
       }
     };
     // row max of both halves (a tree, for short dependency chains), folded
@@ -400,7 +425,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 
     f32x16 s0v = qk(0);
     f32x16 s1v = qk(1);
-    if (!all_visible) {
+    if (!all_visible || padded) {
       mask(s0v, 0);
       mask(s1v, 1);
     }
@@ -432,11 +457,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   vmem_wait_all();
   __syncthreads();
   for (int it = 0;;) {
+    take_mask();
     if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 1);
     compute(kt_hi - it, 0);
     vmem_wait_all();
     __syncthreads();
     if (++it >= ntiles) break;
+    take_mask();
     if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 0);
     compute(kt_hi - it, 1);
     vmem_wait_all();
@@ -448,7 +475,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   float l_lo, l_hi;
   swap32(l_run, l_lo, l_hi);
   const float l_tot = l_lo + l_hi;
-  const float inv_l = 1.0f / l_tot;
+  // a query whose every key is padding has l = 0: the zero row (lse = -inf)
+  const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 
   // O^T element i of tile dt: d = 32 dt + 8 (i/4) + 4 g + i%4, rounded to bf16
   // (the attention output's dtype boundary).
@@ -511,7 +539,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 template <int D, bool FUSED>
 hipError_t launch_one(const AttnArgs &a, dim3 grid, hipStream_t stream) {
   // all LDS is static (Tile<D>::LDS_BYTES), so no dynamic allocation
-  hipLaunchKernelGGL((attn_fwd_kernel<D, FUSED>), grid, dim3(64 * NW), 0, stream, a);
+  if (a.key_valid)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, FUSED, true>), grid, dim3(64 * NW), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, FUSED, false>), grid, dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ struct RopeTableArgs {
   int32_t n_pos;
   float *cos_out;
   float *sin_out;
+  int32_t grid_w;          // > 0: 2-D table of a row-major grid of n_pos / grid_w rows
 };
 
 struct QkNormArgs {
@@ -50,6 +51,7 @@ struct QkNormArgs {
   float eps, gain_center, query_scale;
   int32_t use_rope;
   int32_t rope_v2;         // rotation in the Q/K dtype (upcast_rope == 0)
+  int32_t skip_norm;       // scale/rotate only: no RMSNorm, no gain
   TokenLayout lay;
 };
 
@@ -87,6 +89,7 @@ struct AttnArgs {
   int32_t tok_per_wg;      // query tokens per workgroup (tok_per_wg * heads_per_wg <= columns)
   int32_t window;          // <= 0: none
   int32_t bidirectional;   // every key of the segment is visible (no causal order, no window)
+  const uint8_t *key_valid;  // BSHD [batch, seqlen] token validity (0 = padded key) or nullptr
   int32_t q_blocks;        // ceil(max segment length / tok_per_wg)
   TokenLayout lay;
 };

@@ -1,6 +1,7 @@
 // Q/K RMSNorm + zero-centred gain + bf16 cast + query_scale + adjacent-pair
 // RoPE (layers page, _qk_norm_rope_core, _rms_norm_core,
-// apply_rotary_embedding with upcast=True).
+// apply_rotary_embedding); without the norm, the rotation of the vision
+// attention (vision page, _apply_vision_rope).
 //
 // HBM-bound.  Each (token, head) row of D bf16 values is spread over D/8
 // lanes holding 8 consecutive elements (one 16-byte load); the row's sum of
@@ -21,8 +22,9 @@ constexpr int kRowsInFlight = 2;
 
 // ROPE: 0 no rotation, 1 FP32 rotation (upcast_rope), 2 rotation in the Q/K
 // dtype; QS: query_scale != 1 (K rows then take the exact identity scale 1,
-// which leaves their bf16 values unchanged).
-template <int D, int ROPE, bool QS>
+// which leaves their bf16 values unchanged); NORM: false skips the RMSNorm
+// and gain (the vision attention rotates un-normalised Q/K).
+template <int D, int ROPE, bool QS, bool NORM>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
   constexpr int LPR = D / 8;               // lanes per row
   constexpr int RPP = kThreads / LPR;      // rows per pass of the block
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
 
   // effective gains of this lane's 8 columns
   float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-  if (gain) {
+  if (NORM && gain) {
     const float4 g0 = *reinterpret_cast<const float4 *>(gain + c * 8);
     const float4 g1 = *reinterpret_cast<const float4 *>(gain + c * 8 + 4);
     w[0] = a.gain_center + g0.x; w[1] = a.gain_center + g0.y;
@@ -85,11 +87,14 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
 #pragma unroll
   for (int j = 0; j < kRowsInFlight; ++j) {
     const int r = base + j * RPP;
-    float x[8];
-    unpack8(xin[j], x);
-    const float ss = row_sum<LPR>(chunk_sumsq<8>(x));
+    float rstd = 1.0f;
+    if constexpr (NORM) {
+      float x[8];
+      unpack8(xin[j], x);
+      const float ss = row_sum<LPR>(chunk_sumsq<8>(x));   // every lane takes part
+      rstd = rms_rstd(ss, 1.0f / (float)D, a.eps);
+    }
     if (r >= nrows) continue;
-    const float rstd = rms_rstd(ss, 1.0f / (float)D, a.eps);
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (ROPE != 0) {
       const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)pos[j] * (D / 2) + c * 4);
@@ -97,25 +102,38 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
       cs[0] = cv.x; cs[1] = cv.y; cs[2] = cv.z; cs[3] = cv.w;
       sn[0] = sv.x; sn[1] = sv.y; sn[2] = sv.z; sn[3] = sv.w;
     }
-    const uint4 y = qk_chunk(x, w, rstd, QS, qs, ROPE != 0, cs, sn, ROPE == 2);
+    uint4 y;
+    if constexpr (NORM) {
+      float x[8];
+      unpack8(xin[j], x);
+      y = qk_chunk(x, w, rstd, QS, qs, ROPE != 0, cs, sn, ROPE == 2);
+    } else {
+      y = scale_rope_chunk(xin[j], QS, qs, ROPE != 0, cs, sn, ROPE == 2);
+    }
     *reinterpret_cast<uint4 *>(dst + (int64_t)r * D + c * 8) = y;
-    if (rs && c == 0) rs[r] = rstd;
+    if (NORM && rs && c == 0) rs[r] = rstd;
   }
 }
 
-template <int D, int ROPE>
+template <int D, int ROPE, bool NORM>
 void launch_r(const QkNormArgs &a, dim3 grid, hipStream_t stream) {
   if (a.q_rows > 0 && a.query_scale != 1.0f)
-    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, true>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, true, NORM>), grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, false>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, false, NORM>), grid, dim3(kThreads), 0, stream, a);
+}
+
+template <int D, bool NORM>
+void launch_n(const QkNormArgs &a, dim3 grid, hipStream_t stream) {
+  if (!a.use_rope) launch_r<D, 0, NORM>(a, grid, stream);
+  else if (a.rope_v2) launch_r<D, 2, NORM>(a, grid, stream);
+  else launch_r<D, 1, NORM>(a, grid, stream);
 }
 
 template <int D>
 void launch_d(const QkNormArgs &a, dim3 grid, hipStream_t stream) {
-  if (!a.use_rope) launch_r<D, 0>(a, grid, stream);
-  else if (a.rope_v2) launch_r<D, 2>(a, grid, stream);
-  else launch_r<D, 1>(a, grid, stream);
+  if (a.skip_norm) launch_n<D, false>(a, grid, stream);
+  else launch_n<D, true>(a, grid, stream);
 }
 
 }  // namespace

@@ -1,9 +1,16 @@
-// FP32 RoPE cos/sin table (layers page, MuseSparkRotaryEmbedding: FP32
-// adjacent-pair frequencies; cosine/sine of width head_dim / 2).
+// FP32 RoPE cos/sin tables.
 //
-// One thread per (position, pair).  The inverse frequency theta^(-2i/D) and
-// the cosine/sine are evaluated in double and rounded once to binary32; the
-// angle itself is the binary32 product of the position and that frequency.
+// 1-D (layers page, MuseSparkRotaryEmbedding: FP32 adjacent-pair frequencies;
+// cosine/sine of width head_dim / 2): pair i of position p has the angle
+// p * theta^(-2i/D).
+//
+// 2-D (vision page, _rope_frequencies: adjacent-pair 2-D frequencies of one
+// row-major patch grid): the first D/4 pairs of patch (y, x) take the 1-D
+// angles of a D/2-wide head at coordinate y, the last D/4 pairs those at x.
+//
+// One thread per (position, pair).  The inverse frequency and the cosine/sine
+// are evaluated in double and rounded once to binary32; the angle itself is
+// the binary32 product of the coordinate and that frequency.
 #include "kernels.hpp"
 
 namespace muse {
@@ -14,8 +21,15 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
   if (idx >= (int64_t)a.n_pos * half) return;
   const int p = (int)(idx / half);
   const int i = (int)(idx % half);
-  const float inv = (float)pow((double)a.theta, -2.0 * (double)i / (double)a.head_dim);
-  const float ang = (float)p * inv;
+  int coord = p, j = i, width = a.head_dim;
+  if (a.grid_w > 0) {
+    const int quarter = half / 2;
+    width = half;
+    coord = i < quarter ? p / a.grid_w : p % a.grid_w;
+    j = i < quarter ? i : i - quarter;
+  }
+  const float inv = (float)pow((double)a.theta, -2.0 * (double)j / (double)width);
+  const float ang = (float)coord * inv;
   a.cos_out[idx] = (float)cos((double)ang);
   a.sin_out[idx] = (float)sin((double)ang);
 }

@@ -85,6 +85,12 @@ typedef enum {
  *                     MuseSparkVisionAttention: packed bidirectional attention);
  *                     requires sliding_window <= 0.  Zero (the default of a
  *                     zero-initialised struct): causal.
+ * skip_qk_norm        non-zero: muse_qk_norm_rope leaves out the RMSNorm and
+ *                     gain and only scales/rotates the bf16 Q/K (vision page:
+ *                     MuseSparkVisionAttention has no Q/K norm, _apply_vision_rope
+ *                     rotates the projected Q/K); gains and rstd outputs must then
+ *                     be NULL.  The fused entry points, which normalise the query
+ *                     in their prologue, return UNSUPPORTED for it.  Zero: normalise.
  */
 typedef struct {
   int32_t head_dim;
@@ -99,6 +105,7 @@ typedef struct {
   float out_eps;
   float gain_center;
   int32_t bidirectional;
+  int32_t skip_qk_norm;
 } muse_attn_params;
 
 /*
@@ -117,6 +124,15 @@ typedef struct {
  *       lie in [0, n_pos) of the cos/sin table; out-of-range ids are clamped
  *       into it (memory stays safe, the result is unspecified).  Masking
  *       always uses the token's index inside its row/segment.
+ * attention_mask: optional device uint8 [batch, seqlen] token validity for
+ *       BSHD (model page, MuseSparkTextModel.forward attention_mask: nonzero =
+ *       valid; a boolean mask's bytes work as is).  A padded key is visible to
+ *       no query; the window still counts positions, padded or not; queries
+ *       themselves are computed whatever their own validity.  A query left
+ *       with no visible key gets the zero row: o = 0, lse = -inf, and the
+ *       gated output 0.  Read by the attention entry points only; with THD it
+ *       is INVALID_ARG (the pages leave the mask unused for packed THD: pack
+ *       the valid tokens instead).
  */
 typedef struct {
   int32_t batch;
@@ -126,6 +142,7 @@ typedef struct {
   int32_t total_tokens;
   int32_t max_seqlen;
   const int32_t *position_ids;
+  const uint8_t *attention_mask;
 } muse_layout;
 
 /*
@@ -146,12 +163,36 @@ muse_status muse_rope_cos_sin(float theta, int32_t head_dim, int32_t n_pos, floa
                               float *sin_out, void *stream);
 
 /*
+ * FP32 2-D RoPE cos/sin table of one row-major patch grid (vision page,
+ * _rope_frequencies: adjacent-pair 2-D frequencies [H*W, D/2, 2], read as a
+ * cos and a sin table of [H*W, D/2]).
+ *
+ * Patch p = y * grid_w + x (row y, column x).  With Q = head_dim / 4 and
+ * inv_j = float(theta ** (-2 j / (head_dim / 2))) for j in [0, Q) (double,
+ * rounded once), pair i of patch p has the angle
+ *   a = float(y) * inv_i          for i <  Q   (the row half)
+ *   a = float(x) * inv_(i - Q)    for i >= Q   (the column half)
+ * (binary32 products), and cos_out[p * head_dim/2 + i] = float(cos(a)),
+ * sin_out[...] = float(sin(a)) (double, rounded once): each half is the 1-D
+ * table of a head_dim/2-wide head at that coordinate.  Several grids packed
+ * into one THD batch use one table each (or one concatenated table) and
+ * position_ids that point each patch at its row.
+ * cos_out, sin_out: device fp32 [grid_h * grid_w, head_dim/2], written.
+ * Errors: INVALID_ARG for theta <= 0 or non-finite, head_dim not a positive
+ * multiple of 4, grid_h or grid_w < 0, null outputs (when the grid is not
+ * empty), overlapping outputs, more than 2^31 - 1 patches.
+ */
+muse_status muse_rope_cos_sin_2d(float theta, int32_t head_dim, int32_t grid_h, int32_t grid_w,
+                                 float *cos_out, float *sin_out, void *stream);
+
+/*
  * Q/K RMSNorm + gain + bf16 cast + query_scale + adjacent-pair RoPE
  * (layers page, _qk_norm_rope_core, _rms_norm_core, apply_rotary_embedding).
  *
  * For every (token, head) row x of D bf16 values:
  *   r = 1 / sqrt(mean(x^2) + qk_eps)                   (FP32 accumulation)
- *   y = bf16(x * r * (gain_center + g))                 (no gain multiply when g is NULL)
+ *   y = bf16(x * r * (gain_center + g))                 (no gain multiply when g is NULL;
+ *                                                        y = x when skip_qk_norm)
  *   Q only: y = bf16(y * query_scale)
  *   use_rope: (y0, y1) of each adjacent pair -> bf16(y0 C - y1 S), bf16(y0 S + y1 C)
  *             in FP32, with C, S = cos/sin[position][pair].
@@ -163,7 +204,7 @@ muse_status muse_rope_cos_sin(float theta, int32_t head_dim, int32_t n_pos, floa
  * cos, sin        fp32 [n_pos, D/2] table from muse_rope_cos_sin; required
  *                 when use_rope, ignored otherwise.  Implicit positions need
  *                 n_pos >= seqlen (BSHD) or >= max_seqlen (THD).
- * q_rstd, k_rstd  optional fp32 [N, Hq] / [N, Hkv] outputs of r.
+ * q_rstd, k_rstd  optional fp32 [N, Hq] / [N, Hkv] outputs of r (NULL with skip_qk_norm).
  * Errors: INVALID_ARG (see conventions; also when both q and k are NULL or an
  * input is given without its output), UNSUPPORTED (D not in {64,128}), DEVICE.
  */
@@ -180,7 +221,8 @@ muse_status muse_qk_norm_rope(const muse_attn_params *params, const muse_layout 
  *
  * For every query token i (index inside its row/segment) and head h, with
  * kv = h / (Hq / Hkv) and J(i) the visible keys (j <= i, j > i - W when W > 0,
- * same row/segment):
+ * same row/segment; every key of the row/segment when bidirectional; padded
+ * keys of layout->attention_mask removed):
  *   s_j = scaling * <q_hat[i,h], k_hat[j,kv]>   (bf16 products, FP32 accumulation)
  *   o[i,h] = bf16( sum_j softmax(s)_j v[j,kv] ),  lse[i,h] = ln sum_j exp(s_j)
  *

@@ -13,11 +13,13 @@ What it computes is defined by the NeMo AutoModel API reference pages for the
   ``MuseSparkRotaryEmbedding``, ``_rms_norm_core``, ``_qk_norm_rope_core``,
   ``apply_rotary_embedding``, ``_repeat_kv``, ``_output_norm_gate_core``);
 * "model page" -- ``nemo_automodel.components.models.muse_spark.model``
-  (section ``_causal_mask``);
+  (sections ``_causal_mask`` and ``MuseSparkTextModel.forward``'s
+  ``attention_mask``: token validity [batch, sequence]);
 * "adapter page" -- ``nemo_automodel.components.models.muse_spark.hf_state_dict_adapter``
   (section ``_permute_rope_rows``);
 * "vision page" -- ``nemo_automodel.components.models.muse_spark.vision``
-  (section ``MuseSparkVisionAttention``: packed bidirectional attention).
+  (sections ``MuseSparkVisionAttention``: packed bidirectional attention;
+  ``_apply_vision_rope``, ``_rope_frequencies``: adjacent-pair 2-D RoPE).
 
 The method is a composition of exact definitions (no approximation, heuristic
 or iteration), so every function below is that definition written out in
@@ -25,14 +27,18 @@ float64, with each dtype boundary the pages name emulated by an explicit
 round-to-nearest-even.  Flash-style blocking reaches the plain softmax result
 up to rounding order, so attention here is the plain masked softmax.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 RMS over the last dim per (token, head); eps inside the square root; effective
 gain ``f32(gain_center + g)`` applied after normalisation and before the cast;
 RoFormer rotation sign with frequencies ``theta**(-2i/D)``; cos/sin of width
 D/2; window ``W`` = number of visible causal keys including the query itself;
 no attention across packed segments (bidirectional mode: every key of the
-query's own segment, no window); bf16 boundary on the attention output;
-sigmoid and output norm in full precision with one final cast.
+query's own segment, no window); a padded key (attention_mask [B,S] False)
+is visible to no query, and a query left with no visible key gives the zero
+row with lse = -inf; bf16 boundary on the attention output;
+sigmoid and output norm in full precision with one final cast; the vision
+2-D table gives the first half of the pairs the patch row and the second
+half the patch column.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, library routines or brute force; none is "parity unpinned".
@@ -48,6 +54,7 @@ __all__ = [
     "round_f32",
     "rope_inv_freq",
     "rope_cos_sin",
+    "rope_cos_sin_2d",
     "rms_normalize",
     "rms_norm",
     "rope_rotate",
@@ -116,6 +123,27 @@ def rope_cos_sin(theta: float, head_dim: int, positions) -> tuple[np.ndarray, np
     """
     p = np.asarray(positions, dtype=np.float64).reshape(-1, 1)
     ang = round_f32(p * rope_inv_freq(theta, head_dim)[None, :])
+    return round_f32(np.cos(ang)), round_f32(np.sin(ang))
+
+
+def rope_cos_sin_2d(theta: float, head_dim: int, grid_h: int, grid_w: int):
+    """cos/sin [grid_h*grid_w, D/2] of one row-major patch grid (vision page,
+    _rope_frequencies: adjacent-pair 2-D frequencies [H*W, D/2, 2]).
+
+    Reading (the page gives only the shape): the trailing 2 is (cos, sin);
+    patch p = y*grid_w + x; the first D/4 pairs rotate with the row y and the
+    last D/4 with the column x, each half at the 1-D frequencies of a
+    D/2-wide head, theta**(-2j/(D/2)).  The angle is a binary32 product and
+    cos/sin are rounded once, as in the 1-D table.
+    """
+    if head_dim % 4:
+        raise ValueError("2-D RoPE needs head_dim % 4 == 0")
+    quarter = head_dim // 4
+    j = np.arange(quarter, dtype=np.float64)
+    inv = round_f32(np.power(np.float64(theta), -2.0 * j / (head_dim // 2)))
+    y = np.repeat(np.arange(grid_h, dtype=np.float64), grid_w)[:, None]
+    x = np.tile(np.arange(grid_w, dtype=np.float64), grid_h)[:, None]
+    ang = np.concatenate([round_f32(y * inv[None, :]), round_f32(x * inv[None, :])], axis=1)
     return round_f32(np.cos(ang)), round_f32(np.sin(ang))
 
 
@@ -224,14 +252,21 @@ class Segments:
 # --------------------------------------------------------------------------
 
 def qk_norm_rope(q, k, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
-                 query_scale=1.0, use_rope=True, cos=None, sin=None, upcast_rope=True):
+                 query_scale=1.0, use_rope=True, cos=None, sin=None, upcast_rope=True,
+                 normalize=True):
     """Q [N,Hq,D], K [N,Hkv,D] -> (q_hat, k_hat, q_rstd [N,Hq], k_rstd [N,Hkv]).
 
     ``cos``/``sin`` are the per-token rows [N, D/2] (already indexed by each
     token's position); they are ignored when ``use_rope`` is false.
+    normalize=False is the vision attention's rotation (vision page,
+    MuseSparkVisionAttention has no Q/K norm; _apply_vision_rope rotates the
+    bf16 projections directly): no RMSNorm, no gain, rstd returned as None.
     """
-    q1, q_rstd = rms_norm(q, eps, q_gain, gain_center)
-    k1, k_rstd = rms_norm(k, eps, k_gain, gain_center)
+    if normalize:
+        q1, q_rstd = rms_norm(q, eps, q_gain, gain_center)
+        k1, k_rstd = rms_norm(k, eps, k_gain, gain_center)
+    else:
+        q1, k1, q_rstd, k_rstd = np.asarray(q, np.float64), np.asarray(k, np.float64), None, None
     q1 = round_bf16(q1 * np.float64(round_f32(query_scale)))
     if use_rope:
         c = np.asarray(cos, dtype=np.float64)[:, None, :]
@@ -248,40 +283,56 @@ def qk_norm_rope(q, k, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
 # (window = number of causal key positions visible to each query).
 # --------------------------------------------------------------------------
 
-def visible_mask(qpos: np.ndarray, kpos: np.ndarray, window: int, causal: bool = True) -> np.ndarray:
+def visible_mask(qpos: np.ndarray, kpos: np.ndarray, window: int, causal: bool = True,
+                 key_ok=None) -> np.ndarray:
     """Key j visible to query i iff j <= i and, with a window W > 0, j > i - W.
 
     causal=False is the packed bidirectional attention of the vision tower
     (vision page, MuseSparkVisionAttention): every key of the segment is
-    visible (no window)."""
+    visible (no window).  ``key_ok`` (bool per key) is the token-validity
+    mask of a padded batch (model page, _causal_mask with an attention_mask
+    [B,S], True = valid): a padded key is visible to no query; the window
+    still counts positions."""
     i = np.asarray(qpos)[:, None]
     j = np.asarray(kpos)[None, :]
     if not causal:
-        return np.ones((i.shape[0], j.shape[1]), dtype=bool)
-    vis = j <= i
-    if window and window > 0:
-        vis &= j > i - window
+        vis = np.ones((i.shape[0], j.shape[1]), dtype=bool)
+    else:
+        vis = j <= i
+        if window and window > 0:
+            vis &= j > i - window
+    if key_ok is not None:
+        vis &= np.asarray(key_ok, dtype=bool)[None, :]
     return vis
 
 
-def _attend_block(qb, kseg, vseg, qpos, window, scaling, causal=True):
-    """Softmax attention of query rows qb [m,D] over one segment's keys [L,D]."""
+def _attend_block(qb, kseg, vseg, qpos, window, scaling, causal=True, key_ok=None):
+    """Softmax attention of query rows qb [m,D] over one segment's keys [L,D].
+
+    A row with no visible key (possible only with padded keys) is the zero
+    row with lse = -inf."""
     s = float(scaling) * (qb @ kseg.T)
-    vis = visible_mask(qpos, np.arange(kseg.shape[0]), window, causal)
+    vis = visible_mask(qpos, np.arange(kseg.shape[0]), window, causal, key_ok)
+    seen = vis.any(axis=1)
     s = np.where(vis, s, -np.inf)
-    mx = s.max(axis=1, keepdims=True)
-    e = np.exp(s - mx)
+    mx = np.where(seen, s.max(axis=1, initial=-np.inf), 0.0)[:, None]
+    e = np.where(vis, np.exp(s - mx), 0.0)
     z = e.sum(axis=1, keepdims=True)
-    o = (e @ vseg) / z
-    return o, mx[:, 0] + np.log(z[:, 0])
+    o = np.where(seen[:, None], (e @ vseg) / np.where(z > 0, z, 1.0), 0.0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(seen, mx[:, 0] + np.log(np.where(seen, z[:, 0], 1.0)), -np.inf)
+    return o, lse
 
 
-def attention(q_hat, k_hat, v, segments: Segments, *, window=0, scaling, row_block=2048, causal=True):
+def attention(q_hat, k_hat, v, segments: Segments, *, window=0, scaling, row_block=2048, causal=True,
+              key_valid=None):
     """Exact causal (or, causal=False, bidirectional) GQA softmax attention.
     Returns (bf16(o) [N,Hq,D], lse [N,Hq]).
 
     Query head h reads key/value head h // (Hq // Hkv).  lse uses the natural
-    log.  Rows outside every segment are left at zero.
+    log.  Rows outside every segment are left at zero.  ``key_valid`` [N]
+    (bool, per token) masks padded keys; a query left with no visible key
+    gets the zero row and lse = -inf.
     """
     q_hat = np.asarray(q_hat, dtype=np.float64)
     k_hat = np.asarray(k_hat, dtype=np.float64)
@@ -296,17 +347,18 @@ def attention(q_hat, k_hat, v, segments: Segments, *, window=0, scaling, row_blo
             g = h // groups
             kseg = k_hat[s0:s0 + length, g]
             vseg = v[s0:s0 + length, g]
+            kok = None if key_valid is None else np.asarray(key_valid)[s0:s0 + length]
             for r0 in range(0, length, row_block):
                 r1 = min(length, r0 + row_block)
                 ob, lb = _attend_block(q_hat[s0 + r0:s0 + r1, h], kseg, vseg,
-                                       np.arange(r0, r1), window, scaling, causal)
+                                       np.arange(r0, r1), window, scaling, causal, kok)
                 o[s0 + r0:s0 + r1, h] = ob
                 lse[s0 + r0:s0 + r1, h] = lb
     return round_bf16(o), lse
 
 
 def attention_rows(q_hat_rows, k_hat, v, segments: Segments, rows, *, num_heads, window=0, scaling,
-                   causal=True):
+                   causal=True, key_valid=None):
     """Attention for selected (token, head) rows only.
 
     ``q_hat_rows`` [len(rows), D] holds the normalised/rotated query of each
@@ -320,9 +372,10 @@ def attention_rows(q_hat_rows, k_hat, v, segments: Segments, rows, *, num_heads,
     for r, (t, h) in enumerate(rows):
         s0, length = segments.locate(int(t))
         g = int(h) // groups
+        kok = None if key_valid is None else np.asarray(key_valid)[s0:s0 + length]
         ob, lb = _attend_block(np.asarray(q_hat_rows[r], dtype=np.float64)[None, :],
                                k_hat[s0:s0 + length, g], v[s0:s0 + length, g],
-                               np.array([int(t) - s0]), window, scaling, causal)
+                               np.array([int(t) - s0]), window, scaling, causal, kok)
         o[r] = ob[0]
         lse[r] = lb[0]
     return round_bf16(o), lse
@@ -351,7 +404,7 @@ def out_norm_gate(o, gate, eps):
 
 def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling,
               window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
-              query_scale=1.0, position_ids=None, upcast_rope=True, causal=True):
+              query_scale=1.0, position_ids=None, upcast_rope=True, causal=True, key_valid=None):
     """Full forward over every row.  Inputs are float64 arrays of bf16 values.
 
     Returns a dict with q_hat, k_hat, q_rstd, k_rstd, o (bf16 values), lse,
@@ -363,7 +416,8 @@ def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling
     q_hat, k_hat, q_rstd, k_rstd = qk_norm_rope(
         q, k, eps=eps, q_gain=q_gain, k_gain=k_gain, gain_center=gain_center,
         query_scale=query_scale, use_rope=use_rope, cos=cos, sin=sin, upcast_rope=upcast_rope)
-    o, lse = attention(q_hat, k_hat, v, segments, window=window, scaling=scaling, causal=causal)
+    o, lse = attention(q_hat, k_hat, v, segments, window=window, scaling=scaling, causal=causal,
+                       key_valid=key_valid)
     out, o_rstd = out_norm_gate(o, gate, out_eps)
     return dict(q_hat=q_hat, k_hat=k_hat, q_rstd=q_rstd, k_rstd=k_rstd, o=o, lse=lse,
                 o_rstd=o_rstd, out=out)
@@ -371,7 +425,7 @@ def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling
 
 def attn_core_rows(q_rows, k, v, gate_rows, segments: Segments, rows, *, num_heads, theta, eps,
                    out_eps, scaling, window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
-                   query_scale=1.0, position_ids=None, upcast_rope=True, causal=True):
+                   query_scale=1.0, position_ids=None, upcast_rope=True, causal=True, key_valid=None):
     """The full forward for selected (token, head) rows only.
 
     ``q_rows``/``gate_rows`` [R, D] hold the query and gate values of the R
@@ -393,7 +447,7 @@ def attn_core_rows(q_rows, k, v, gate_rows, segments: Segments, rows, *, num_hea
     k1, _ = rms_norm(k, eps, k_gain, gain_center)
     k_hat = rope_rotate(k1, kc[:, None, :], ks[:, None, :], upcast_rope) if use_rope else k1
     o, lse = attention_rows(q_hat, k_hat, v, segments, rows, num_heads=num_heads,
-                            window=window, scaling=scaling, causal=causal)
+                            window=window, scaling=scaling, causal=causal, key_valid=key_valid)
     out, o_rstd = out_norm_gate(o, np.asarray(gate_rows, dtype=np.float64), out_eps)
     return dict(q_hat=q_hat, k_hat=k_hat, o=o, lse=lse, o_rstd=o_rstd, out=out)
 

@@ -153,3 +153,42 @@ def test_rope_table_argument_rules():
     assert lib.muse_rope_cos_sin(1e4, 64, -1, FAKE, FAKE + 4096, None) == 1
     assert lib.muse_rope_cos_sin(1e4, 64, 4, None, FAKE, None) == 1
     assert lib.muse_rope_cos_sin(1e4, 64, 4, FAKE, FAKE + 64, None) == 1   # overlapping outputs
+
+
+def test_rope_table_2d_argument_rules():
+    lib = m.library()
+    assert lib.muse_rope_cos_sin_2d(0.0, 64, 2, 2, FAKE, FAKE + 4096, None) == 1
+    assert lib.muse_rope_cos_sin_2d(1e4, 62, 2, 2, FAKE, FAKE + 4096, None) == 1   # D % 4 != 0
+    assert lib.muse_rope_cos_sin_2d(1e4, 64, -1, 2, FAKE, FAKE + 4096, None) == 1
+    assert lib.muse_rope_cos_sin_2d(1e4, 64, 2, -1, FAKE, FAKE + 4096, None) == 1
+    assert lib.muse_rope_cos_sin_2d(1e4, 64, 2, 2, None, FAKE, None) == 1
+    assert lib.muse_rope_cos_sin_2d(1e4, 64, 2, 2, FAKE, FAKE + 64, None) == 1   # overlapping outputs
+    assert lib.muse_rope_cos_sin_2d(1e4, 64, 1 << 16, 1 << 16, FAKE, FAKE + 4096, None) == 1
+    assert lib.muse_rope_cos_sin_2d(1e4, 64, 0, 7, None, None, None) == 0         # empty grid: no-op
+
+
+def test_skip_qk_norm_rules():
+    lib = m.library()
+    p, lay = _params(skip_qk_norm=1), _bshd()
+    qo, ko = FAKE + (4 << 24), FAKE + (5 << 24)
+
+    def qk(qg=None, qr=None):
+        return lib.muse_qk_norm_rope(ctypes.byref(p), ctypes.byref(lay), FAKE, FAKE + (1 << 24), qg, None,
+                                     FAKE + (2 << 24), FAKE + (3 << 24), 16, qo, ko, qr, None, None)
+    assert qk(qg=FAKE + (6 << 24)) == 1                    # no gain without the norm
+    assert qk(qr=FAKE + (7 << 24)) == 1                    # no rstd without the norm
+    # the fused core normalises the query in its prologue
+    st = lib.muse_attn_fused_fwd(ctypes.byref(p), ctypes.byref(lay), FAKE, FAKE + (1 << 24),
+                                 FAKE + (2 << 24), FAKE + (3 << 24), None, FAKE + (4 << 24),
+                                 FAKE + (5 << 24), 16, FAKE + (6 << 24), None, None)
+    assert st == 2
+
+
+def test_attention_mask_rules():
+    # a key-validity mask is for BSHD only; it is an input (no output may overlap it)
+    thd = m.c_layout(0, 0, FAKE + (9 << 24), 2, 10, 5, None, FAKE + (10 << 24))
+    assert _attn(_params(), thd) == 1
+    assert "THD" in m.library().muse_last_error().decode()
+    lay = m.c_layout(1, 16, None, 1, 0, 0, None, FAKE + (3 << 24) + 3)   # inside o, odd address is fine
+    assert _attn(_params(), lay) == 1
+    assert "overlaps" in m.library().muse_last_error().decode()

@@ -127,6 +127,83 @@ def test_rope_table_angle_is_binary32_product_like_an_fp32_module():
     np.testing.assert_array_equal(s, torch.sin(ang).to(torch.float32).double().numpy())
 
 
+# ---------------------------------------------------------------- 2-D (vision) RoPE table
+
+def test_rope_2d_table_axes_on_a_non_square_grid():
+    gh, gw, d = 3, 5, 64
+    c, s = O.rope_cos_sin_2d(1.0e4, d, gh, gw)
+    assert c.shape == s.shape == (gh * gw, d // 2)
+    q = d // 4
+    for p in range(gh * gw):
+        y, x = divmod(p, gw)
+        # a zero coordinate leaves its half unrotated
+        if y == 0:
+            np.testing.assert_array_equal(c[p, :q], 1.0)
+            np.testing.assert_array_equal(s[p, :q], 0.0)
+        if x == 0:
+            np.testing.assert_array_equal(c[p, q:], 1.0)
+            np.testing.assert_array_equal(s[p, q:], 0.0)
+        # pairs 0 and D/4 have inverse frequency 1: their angles are y and x
+        assert c[p, 0] == np.float32(math.cos(y)) and s[p, 0] == np.float32(math.sin(y))
+        assert c[p, q] == np.float32(math.cos(x)) and s[p, q] == np.float32(math.sin(x))
+        # pair D/8 of each half has inverse frequency theta**(-1/2) = 0.01 in binary32
+        a_y = float(np.float32(y) * np.float32(0.01))
+        a_x = float(np.float32(x) * np.float32(0.01))
+        assert c[p, q // 2] == np.float32(math.cos(a_y)) and s[p, q // 2] == np.float32(math.sin(a_y))
+        assert c[p, q + q // 2] == np.float32(math.cos(a_x))
+        assert s[p, q + q // 2] == np.float32(math.sin(a_x))
+    assert np.all(np.abs(c * c + s * s - 1.0) < 4 * 2.0 ** -24)
+    # the inverse frequencies decrease along each half
+    c1, s1 = O.rope_cos_sin_2d(1.0e4, d, 2, 2)
+    ang_y = np.arctan2(s1[2, :q], c1[2, :q])       # patch (1, 0)
+    ang_x = np.arctan2(s1[1, q:], c1[1, q:])       # patch (0, 1)
+    assert np.all(np.diff(ang_y) < 0) and np.allclose(ang_y, ang_x, rtol=0, atol=1e-7)
+
+
+def test_rope_2d_scores_depend_on_the_2d_offset_only():
+    rng = np.random.default_rng(21)
+    d, gh, gw = 128, 40, 40
+    qv = _bf16(rng.standard_normal(d))
+    kv = _bf16(rng.standard_normal(d))
+    c, s = O.rope_cos_sin_2d(1.0e4, d, gh, gw)
+
+    def score(y1, x1, y2, x2):
+        p1, p2 = y1 * gw + x1, y2 * gw + x2
+        return float(O.rope_rotate(qv, c[p1], s[p1]) @ O.rope_rotate(kv, c[p2], s[p2]))
+
+    base = score(5, 7, 2, 3)
+    for y1, x1, y2, x2 in [(13, 9, 10, 5), (30, 34, 27, 30), (3, 4, 0, 0)]:
+        assert abs(score(y1, x1, y2, x2) - base) < 0.05 * (abs(base) + 1.0)
+    # and it depends on both offsets
+    assert abs(score(6, 7, 2, 3) - base) > 1e-3
+    assert abs(score(5, 8, 2, 3) - base) > 1e-3
+
+
+def test_norm_free_rotation_of_the_vision_attention():
+    rng = np.random.default_rng(22)
+    n, hq, hkv, d = 12, 4, 2, 64
+    q = _bf16(3.0 * rng.standard_normal((n, hq, d)))
+    k = _bf16(rng.standard_normal((n, hkv, d)))
+    # no rotation and no norm: the bf16 inputs come back unchanged (and the
+    # query scale alone applies, exactly for a power of two)
+    q1, k1, qr, kr = O.qk_norm_rope(q, k, eps=1e-6, use_rope=False, normalize=False)
+    np.testing.assert_array_equal(q1, q)
+    np.testing.assert_array_equal(k1, k)
+    assert qr is None and kr is None
+    q2, _, _, _ = O.qk_norm_rope(q, k, eps=1e-6, use_rope=False, normalize=False, query_scale=0.5)
+    np.testing.assert_array_equal(q2, q / 2)
+    # with rotation: patch (0, 0) is the identity, other patches keep each pair's norm
+    c, s = O.rope_cos_sin_2d(1.0e4, d, 3, 4)
+    q3, k3, _, _ = O.qk_norm_rope(q, k, eps=1e-6, cos=c, sin=s, normalize=False)
+    np.testing.assert_array_equal(q3[0], q[0])
+    np.testing.assert_array_equal(k3[0], k[0])
+    n0 = q[..., 0::2] ** 2 + q[..., 1::2] ** 2
+    n1 = q3[..., 0::2] ** 2 + q3[..., 1::2] ** 2
+    assert np.all(np.abs(n1 - n0) <= 2 * 2.0 ** -7 * n0 + 1e-30)
+    # and the norm really is skipped: the rows keep their RMS of about 3
+    assert abs(np.sqrt(np.mean(q3 ** 2)) - 3.0) < 0.3
+
+
 # ---------------------------------------------------------------- RMSNorm
 
 def _bf16(x):
@@ -296,10 +373,11 @@ def test_qk_norm_rope_query_scale_and_gain_routing():
 
 # ---------------------------------------------------------------- attention
 
-def _brute_attention(q, k, v, seg_bounds, window, scaling, causal=True):
+def _brute_attention(q, k, v, seg_bounds, window, scaling, causal=True, valid=None):
     """Pure-Python softmax attention: query i sees the `window` most recent keys
     up to and including itself (all earlier keys when window == 0), or, when
-    not causal, every key of its segment."""
+    not causal, every key of its segment; with `valid` (per token) padded keys
+    drop out, and a query left with no key gets zeros and lse = -inf."""
     n, hq, d = q.shape
     hkv = k.shape[1]
     o = np.zeros((n, hq, d))
@@ -308,6 +386,11 @@ def _brute_attention(q, k, v, seg_bounds, window, scaling, causal=True):
         for i in range(length):
             first = 0 if window <= 0 else max(0, i - window + 1)
             keys = list(range(first, i + 1)) if causal else list(range(length))
+            if valid is not None:
+                keys = [j for j in keys if valid[s0 + j]]
+            if not keys:
+                lse[s0 + i, :] = -math.inf
+                continue
             for h in range(hq):
                 g = h * hkv // hq
                 sc = [scaling * sum(q[s0 + i, h, t] * k[s0 + j, g, t] for t in range(d)) for j in keys]
@@ -383,6 +466,66 @@ def test_bidirectional_attention_invariants():
     # zero queries: uniform weights over the whole segment -> the mean of V
     oz, _ = O.attention(np.zeros_like(q), k, v, segs, scaling=0.5, causal=False)
     np.testing.assert_array_equal(oz[:, 0], np.broadcast_to(_bf16(v[:, 0].mean(axis=0)), (sl, d)))
+
+
+@pytest.mark.parametrize("window", [0, 1, 3])
+def test_padded_keys_brute_force_bshd(window):
+    rng = np.random.default_rng(30 + window)
+    b, sl, hq, hkv, d = 3, 10, 4, 2, 4
+    q = _bf16(rng.standard_normal((b * sl, hq, d)))
+    k = _bf16(rng.standard_normal((b * sl, hkv, d)))
+    v = _bf16(rng.standard_normal((b * sl, hkv, d)))
+    valid = np.ones(b * sl, dtype=bool)
+    valid[:3] = False                   # row 0: left padding (its first queries see nothing)
+    valid[sl + 7:2 * sl] = False        # row 1: right padding
+    valid[2 * sl + 2] = valid[2 * sl + 5] = False   # row 2: holes
+    o, lse = O.attention(q, k, v, O.Segments.bshd(b, sl), window=window, scaling=0.6, key_valid=valid)
+    ro, rl = _brute_attention(q, k, v, [(0, sl), (sl, sl), (2 * sl, sl)], window, 0.6, valid=valid)
+    np.testing.assert_array_equal(o, _bf16(ro))
+    fin = np.isfinite(rl)
+    np.testing.assert_array_equal(np.isfinite(lse), fin)
+    np.testing.assert_allclose(lse[fin], rl[fin], rtol=1e-13, atol=1e-13)
+    # the left-padded queries have no visible key: zero rows
+    assert not fin[:3].any() and np.all(o[:3] == 0.0)
+
+
+def test_padded_keys_invariants():
+    rng = np.random.default_rng(31)
+    b, sl, hq, d = 2, 16, 2, 8
+    q = _bf16(rng.standard_normal((b * sl, hq, d)))
+    k = _bf16(rng.standard_normal((b * sl, 1, d)))
+    v = _bf16(rng.standard_normal((b * sl, 1, d)))
+    segs = O.Segments.bshd(b, sl)
+    # an all-valid mask is no mask
+    o0, l0 = O.attention(q, k, v, segs, scaling=0.5)
+    o1, l1 = O.attention(q, k, v, segs, scaling=0.5, key_valid=np.ones(b * sl, bool))
+    np.testing.assert_array_equal(o1, o0)
+    np.testing.assert_array_equal(l1, l0)
+    # the keys and values of padded tokens do not matter
+    valid = rng.random(b * sl) > 0.3
+    o2, l2 = O.attention(q, k, v, segs, scaling=0.5, key_valid=valid)
+    k2, v2 = k.copy(), v.copy()
+    k2[~valid] = 7.0
+    v2[~valid] = -3.0
+    o3, l3 = O.attention(q, k2, v2, segs, scaling=0.5, key_valid=valid)
+    np.testing.assert_array_equal(o3, o2)
+    np.testing.assert_array_equal(l3, l2)
+    # left padding by p: the valid queries equal the unpadded sequence (with
+    # its own positions) up to summation order
+    p = 5
+    valid = np.ones(sl, bool)
+    valid[:p] = False
+    one = O.Segments.bshd(1, sl)
+    op, lp = O.attention(q[:sl], k[:sl], v[:sl], one, scaling=0.5, key_valid=valid)
+    ou, lu = O.attention(q[p:sl], k[p:sl], v[p:sl], O.Segments.bshd(1, sl - p), scaling=0.5)
+    np.testing.assert_allclose(lp[p:], lu, rtol=1e-13)
+    assert np.all(np.abs(op[p:] - ou) <= 2.0 ** -8 * np.abs(ou))
+    # a window counts positions, padded or not: W = 3 after a padded key at i-1
+    # leaves the query with keys i-2 and i
+    valid = np.ones(sl, bool)
+    valid[9] = False
+    vis = O.visible_mask(np.array([10]), np.arange(sl), 3, key_ok=valid)[0]
+    assert list(np.nonzero(vis)[0]) == [8, 10]
 
 
 def test_attention_golden_tiny():

@@ -227,6 +227,160 @@ def test_bidirectional_fused_core(w):
     assert torch.equal(lse_f, lse)
 
 
+# ---------------------------------------------------------------- vision attention (2-D RoPE, no norm)
+
+def _table_ulp_check(g, r):
+    # the same binary32 angle, cos/sin rounded once from double: equal up to
+    # rare double-rounding cases (at most 1 ulp, at most a handful of entries)
+    diff = g != r
+    assert diff.sum() <= max(2, g.size // 1_000_000)
+    if diff.any():
+        ulp = np.spacing(np.abs(r[diff]).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(g[diff] - r[diff]) <= ulp)
+
+
+@pytest.mark.parametrize("theta,d,gh,gw", [(1.0e4, 64, 3, 5), (1.0e4, 128, 64, 48), (5.0e5, 128, 1, 1)])
+def test_rope_table_2d(theta, d, gh, gw):
+    cos, sin = m.muse_rope_cos_sin_2d(theta, d, gh, gw)
+    torch.cuda.synchronize()
+    rc, rs = O.rope_cos_sin_2d(theta, d, gh, gw)
+    _table_ulp_check(f64(cos), rc)
+    _table_ulp_check(f64(sin), rs)
+
+
+VISION = [
+    (64, 16, ((3, 5), (8, 8), (1, 1), (8, 8), (12, 7))),
+    (128, 8, ((16, 16), (2, 9), (0, 3), (5, 5), (16, 16))),
+]
+
+
+@pytest.mark.parametrize("d,heads,grids", VISION, ids=["d64_h16", "d128_h8"])
+def test_vision_attention_path(d, heads, grids):
+    """Packed grids: 2-D RoPE on un-normalised Q/K (one table per grid shape,
+    shared through position_ids), then bidirectional attention per grid."""
+    theta, name = 1.0e4, f"vision_d{d}"
+    lens = [h * w for h, w in grids]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n = int(cu[-1])
+    x = {t: W.draw_bf16((n, heads, d), 1.0, seed=0, workload=name, layer=0, tensor=t) for t in "qkv"}
+    shapes = sorted({g for g in grids if g[0] * g[1] > 0})
+    offs, off = {}, 0
+    for g in shapes:
+        offs[g] = off
+        off += g[0] * g[1]
+    cos = torch.empty((off, d // 2), dtype=torch.float32, device="cuda")
+    sin = torch.empty_like(cos)
+    for g in shapes:
+        o0 = offs[g]
+        m.muse_rope_cos_sin_2d(theta, d, g[0], g[1], cos[o0:o0 + g[0] * g[1]], sin[o0:o0 + g[0] * g[1]])
+    pos = np.concatenate([offs.get(g, 0) + np.arange(g[0] * g[1]) for g in grids]).astype(np.int32)
+    lay = m.Layout.thd(torch.from_numpy(cu).cuda(), max(lens), total_tokens=n,
+                       position_ids=torch.from_numpy(pos).cuda())
+    p = m.AttnParams(head_dim=d, num_heads=heads, num_key_value_heads=heads, use_rope=True,
+                     bidirectional=True, skip_qk_norm=True, scaling=float(np.float32(d ** -0.5)))
+    q, k, v = (dev_bf16(x[t]) for t in "qkv")
+    qh, kh, qr, kr = m.muse_qk_norm_rope(p, lay, q, k, None, None, cos, sin)
+    o, lse = m.muse_gqa_attn_fwd(p, lay, qh, kh, v, want_lse=True)
+    torch.cuda.synchronize()
+    assert qr is None and kr is None
+    # oracle: the per-token rows of each grid's own 2-D table
+    rc = np.zeros((n, d // 2))
+    rs = np.zeros((n, d // 2))
+    for g, s0, ln in zip(grids, cu[:-1], lens):
+        if ln:
+            rc[s0:s0 + ln], rs[s0:s0 + ln] = O.rope_cos_sin_2d(theta, d, g[0], g[1])
+    rq, rk, _, _ = O.qk_norm_rope(bits_f64(x["q"]), bits_f64(x["k"]), eps=EPS, cos=rc, sin=rs,
+                                  normalize=False)
+    sq = check_bf16(f64(qh), rq, what="vision q rotated")
+    sk = check_bf16(f64(kh), rk, what="vision k rotated")
+    assert sq["exact"] > 0.999 and sk["exact"] > 0.999, (sq, sk)
+    segs = O.Segments.thd(cu)
+    ro, rl = O.attention(f64(qh), f64(kh), bits_f64(x["v"]), segs, scaling=p.scaling, causal=False)
+    check_bf16(f64(o), ro, what="vision o")
+    check_fp32(f64(lse), rl, floor=1.0, what="vision lse")
+
+
+# ---------------------------------------------------------------- padded keys (BSHD attention_mask)
+
+def _pad_mask(kind, batch, seqlen, seed=0):
+    rng = np.random.default_rng(seed)
+    valid = np.ones((batch, seqlen), dtype=bool)
+    for b in range(batch):
+        if kind == "right":
+            valid[b, seqlen - int(rng.integers(1, seqlen)):] = False
+        elif kind == "left":                       # leading queries see no key at all
+            valid[b, :int(rng.integers(1, seqlen))] = False
+        elif kind == "holes":
+            valid[b] = rng.random(seqlen) > 0.35
+        elif kind == "tile":                       # a whole 64-key tile of padding
+            valid[b, 64:128] = False
+    return valid
+
+
+PADDED = [
+    (SMALL[1], "right"), (SMALL[1], "left"), (SMALL[2], "holes"), (SMALL[3], "left"),
+    (SMALL[4], "holes"), (SMALL[8], "tile"), (SMALL[9], "holes"),
+]
+PADDED_IDS = [f"{w.name}-{k}" for w, k in PADDED]
+
+
+def _check_lse(got, ref, what):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin) and np.all(got[~fin] == -np.inf), what
+    check_fp32(got[fin], ref[fin], floor=1.0, what=what)
+
+
+@pytest.mark.parametrize("w,kind", PADDED, ids=PADDED_IDS)
+def test_padded_keys_attention_stage(w, kind):
+    case = make_case(w)
+    valid = _pad_mask(kind, w.batch, w.seqlen, seed=len(kind))
+    lay = m.Layout.bshd(w.batch, w.seqlen, attention_mask=torch.from_numpy(valid).cuda())
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, lay, case.q, case.k, case.q_gain,
+                                             case.k_gain, case.cos, case.sin)
+    o, lse = m.muse_gqa_attn_fwd(case.params, lay, q_hat, k_hat, case.v, want_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs,
+                         window=case.x["window"], scaling=case.scaling, key_valid=valid.reshape(-1))
+    check_bf16(f64(o), ro, what=f"o padded {kind}")
+    _check_lse(f64(lse), rl, f"lse padded {kind}")
+    if kind == "left":
+        assert (~np.isfinite(rl)).any()          # the zero-row case is exercised
+
+
+@pytest.mark.parametrize("w,kind", PADDED[:4], ids=PADDED_IDS[:4])
+def test_padded_keys_fused_core(w, kind):
+    case = make_case(w)
+    valid = _pad_mask(kind, w.batch, w.seqlen, seed=len(kind))
+    lay = m.Layout.bshd(w.batch, w.seqlen, attention_mask=torch.from_numpy(valid).cuda())
+    out, _, lse_f = m.muse_attn_core_fwd(case.params, lay, case.q, case.k, case.v, case.gate,
+                                         case.q_gain, case.k_gain, case.cos, case.sin, want_lse=True)
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, lay, case.q, case.k, case.q_gain,
+                                             case.k_gain, case.cos, case.sin)
+    o, lse = m.muse_gqa_attn_fwd(case.params, lay, q_hat, k_hat, case.v, want_lse=True)
+    out_u, _ = m.muse_out_norm_gate(case.params, lay, o, case.gate)
+    torch.cuda.synchronize()
+    ref = O.attn_core(bits_f64(case.x["q"]), bits_f64(case.x["k"]), bits_f64(case.x["v"]),
+                      bits_f64(case.x["gate"]), case.segs, key_valid=valid.reshape(-1),
+                      **case.oracle_kw())
+    check_bf16(f64(out), ref["out"], what=f"fused out padded {kind}")
+    assert torch.equal(out.view(torch.int16), out_u.view(torch.int16))
+    assert torch.equal(lse_f, lse)
+
+
+def test_all_valid_mask_equals_no_mask():
+    w = SMALL[4]
+    case = make_case(w)
+    lay = m.Layout.bshd(w.batch, w.seqlen,
+                        attention_mask=torch.ones((w.batch, w.seqlen), dtype=torch.uint8, device="cuda"))
+    a, _, la = m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v, case.gate,
+                                    case.q_gain, case.k_gain, case.cos, case.sin, want_lse=True)
+    b, _, lb = m.muse_attn_core_fwd(case.params, lay, case.q, case.k, case.v, case.gate,
+                                    case.q_gain, case.k_gain, case.cos, case.sin, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(la, lb)
+
+
 # ---------------------------------------------------------------- bit-exact invariants
 
 def test_window_one_returns_v_exactly():
