@@ -67,12 +67,12 @@ typedef enum {
  *                     _repeat_kv).
  * sliding_window      W > 0: query i sees keys j with i - W < j <= i (W keys
  *                     including itself, model page _causal_mask).  W <= 0: no
- *                     window (the pages' "or None").
+ *                     window (the pages' None).
  * use_rope            non-zero: rotate Q and K (layers page, layer_uses_rope).
  * upcast_rope         non-zero: FP32 rotation (apply_rotary_embedding upcast=True,
  *                     the original checkpoint's arithmetic).  Zero: rotation in the
- *                     Q/K dtype (upcast=False, the HF release, which rounds both
- *                     products before adding them): C and S cast to bf16, each
+ *                     Q/K dtype (upcast=False, the HF release, where each of the
+ *                     two products is rounded before the sum): C and S cast to bf16, each
  *                     product rounded to bf16, then the bf16 difference / sum.
  * scaling             softmax scale, head_dim ** -0.5 for this model; finite, > 0.
  * query_scale         multiplier applied after the normalised query's bf16 cast

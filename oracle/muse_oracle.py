@@ -104,9 +104,9 @@ def round_f32(x) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# Rotary table -- layers page, MuseSparkRotaryEmbedding ("FP32 adjacent-pair
-# rotary frequencies shared by all text layers"; forward returns cosine/sine
-# shaped [batch, sequence, head_dim / 2]).
+# Rotary table -- layers page, MuseSparkRotaryEmbedding (one set of FP32
+# adjacent-pair frequencies serves every text layer; forward returns cosine and
+# sine of shape [batch, sequence, head_dim / 2]).
 # --------------------------------------------------------------------------
 
 def rope_inv_freq(theta: float, head_dim: int) -> np.ndarray:
@@ -149,8 +149,8 @@ def rope_cos_sin_2d(theta: float, head_dim: int, grid_h: int, grid_w: int):
 
 # --------------------------------------------------------------------------
 # RMSNorm -- layers page, MuseSparkRMSNorm / effective_weight / _rms_norm_core
-# ("Normalize in FP32, then apply the effective gain before the output cast";
-# eps is "added to the mean squared activation").
+# (normalisation in FP32, the effective gain applied before the cast to the
+# output dtype; eps is added to the mean of the squares).
 # --------------------------------------------------------------------------
 
 def rms_normalize(x: np.ndarray, eps: float) -> tuple[np.ndarray, np.ndarray]:
@@ -174,8 +174,8 @@ def rms_norm(x: np.ndarray, eps: float, gain=None, gain_center: float = 1.0):
 
 
 # --------------------------------------------------------------------------
-# RoPE rotation -- layers page, apply_rotary_embedding ("adjacent-pair";
-# the original checkpoint computes the rotation in FP32, upcast=True).
+# RoPE rotation -- layers page, apply_rotary_embedding (pairs of adjacent
+# elements; the original checkpoint computes the rotation in FP32, upcast=True).
 # --------------------------------------------------------------------------
 
 def rope_rotate(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, upcast: bool = True) -> np.ndarray:
@@ -248,7 +248,7 @@ class Segments:
 
 # --------------------------------------------------------------------------
 # Q/K norm + query scale + RoPE -- layers page, _qk_norm_rope_core
-# ("Multiplier applied after the normalized query's dtype cast").
+# (the query scale multiplies the normalised query after its dtype cast).
 # --------------------------------------------------------------------------
 
 def qk_norm_rope(q, k, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
@@ -280,7 +280,7 @@ def qk_norm_rope(q, k, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
 # Attention -- layers page, MuseSparkAttention (scaling = head_dim**-0.5,
 # num_key_value_groups = num_heads // num_key_value_heads), _repeat_kv
 # (KV heads repeated to the query-head count); model page, _causal_mask
-# (window = number of causal key positions visible to each query).
+# (the window W counts the causal key positions one query sees).
 # --------------------------------------------------------------------------
 
 def visible_mask(qpos: np.ndarray, kpos: np.ndarray, window: int, causal: bool = True,
