@@ -66,6 +66,12 @@ __all__ = [
     "Segments",
     "attn_core",
     "attn_core_rows",
+    "out_norm_gate_bwd",
+    "attention_bwd",
+    "rope_rotate_bwd",
+    "rms_norm_bwd",
+    "qk_norm_rope_bwd",
+    "attn_core_bwd",
 ]
 
 
@@ -458,3 +464,206 @@ def _q_rows(q_sel, eps, q_gain, gain_center, query_scale, use_rope, cos, sin, up
     if use_rope:
         q1 = rope_rotate(q1, cos, sin, upcast_rope)
     return q1
+
+
+# --------------------------------------------------------------------------
+# Backward of the core.  The pages train this module with autograd (layers
+# page, MuseSparkDecoderLayer is a GradientCheckpointingLayer; the compiled
+# cores and SDPA/TE are differentiated by their frameworks), so the backward
+# is the chain rule through the forward above, stage by stage in reverse:
+# output norm + gate, attention, RoPE, query scale, Q/K norm + gain.  A
+# gradient has its primal's dtype: with rnd=True every gradient of a bf16
+# tensor is rounded to bf16 where autograd would hold it (dO, dq_hat, dk_hat,
+# dv, the gradient after the rotation and after the query scale, dq, dk,
+# dgate); gain gradients stay in full precision.  rnd=False gives the exact
+# derivative of the unrounded forward (pinned against torch autograd).
+# --------------------------------------------------------------------------
+
+def _maybe_bf16(x, rnd):
+    return round_bf16(x) if rnd else np.asarray(x, dtype=np.float64)
+
+
+def out_norm_gate_bwd(o, gate, dout, eps, rnd=True):
+    """Gradients of out = normalize(o) * sigmoid(gate): returns (do, dgate).
+
+    With y = o r, r = (mean(o^2) + eps)^-1/2, s = sigmoid(gate):
+    dgate = dout y s (1 - s); dy = dout s; do = r dy - r^3 o mean(dy o).
+    """
+    o = np.asarray(o, dtype=np.float64)
+    g = np.asarray(gate, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    y, r = rms_normalize(o, eps)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-g))
+    dgate = dout * y * s * (1.0 - s)
+    dy = dout * s
+    r = r[..., None]
+    do = r * dy - r ** 3 * o * np.mean(dy * o, axis=-1, keepdims=True)
+    return _maybe_bf16(do, rnd), _maybe_bf16(dgate, rnd)
+
+
+def attention_bwd(q_hat, k_hat, v, d_o, segments: Segments, *, window=0, scaling, causal=True,
+                  key_valid=None, rnd=True):
+    """Gradients of o = softmax(scaling q k^T, masked) v per segment and head.
+
+    With P the softmax, dP = dO v^T, delta_i = sum_j P_ij dP_ij and
+    dS = P (dP - delta): dq = scaling dS k, dk = scaling dS^T q, dv = P^T dO;
+    a key/value head sums the contributions of its query heads.  Returns
+    (dq_hat [N,Hq,D], dk_hat [N,Hkv,D], dv [N,Hkv,D]).
+    """
+    q_hat = np.asarray(q_hat, dtype=np.float64)
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_o = np.asarray(d_o, dtype=np.float64)
+    n, hq, d = q_hat.shape
+    hkv = k_hat.shape[1]
+    groups = hq // hkv
+    dq = np.zeros_like(q_hat)
+    dk = np.zeros_like(k_hat)
+    dv = np.zeros_like(v)
+    for s0, length in zip(segments.starts, segments.lengths):
+        if length == 0:
+            continue
+        kok = None if key_valid is None else np.asarray(key_valid)[s0:s0 + length]
+        vis = visible_mask(np.arange(length), np.arange(length), window, causal, kok)
+        seen = vis.any(axis=1)
+        for h in range(hq):
+            g = h // groups
+            qs, ks, vs = q_hat[s0:s0 + length, h], k_hat[s0:s0 + length, g], v[s0:s0 + length, g]
+            dos = d_o[s0:s0 + length, h]
+            sc = np.where(vis, float(scaling) * (qs @ ks.T), -np.inf)
+            mx = np.where(seen, sc.max(axis=1, initial=-np.inf), 0.0)[:, None]
+            e = np.where(vis, np.exp(sc - mx), 0.0)
+            z = e.sum(axis=1, keepdims=True)
+            p = e / np.where(z > 0, z, 1.0)
+            dp = dos @ vs.T
+            delta = np.sum(p * dp, axis=1, keepdims=True)
+            ds = p * (dp - delta)
+            dq[s0:s0 + length, h] = float(scaling) * (ds @ ks)
+            dk[s0:s0 + length, g] += float(scaling) * (ds.T @ qs)
+            dv[s0:s0 + length, g] += p.T @ dos
+    return _maybe_bf16(dq, rnd), _maybe_bf16(dk, rnd), _maybe_bf16(dv, rnd)
+
+
+def rope_rotate_bwd(dy, cos, sin):
+    """Transpose of the FP32 rotation: each pair's gradient rotated back,
+    (dy0 C + dy1 S, -dy0 S + dy1 C), unrounded."""
+    dy = np.asarray(dy, dtype=np.float64)
+    d0, d1 = dy[..., 0::2], dy[..., 1::2]
+    dx = np.empty_like(dy)
+    dx[..., 0::2] = d0 * cos + d1 * sin
+    dx[..., 1::2] = -d0 * sin + d1 * cos
+    return dx
+
+
+def rms_norm_bwd(x, dy, eps, gain=None, gain_center=1.0):
+    """Gradients of y = x r w (r = (mean(x^2) + eps)^-1/2, w = f32(gain_center + g)):
+    returns (dx unrounded, dgain summed over every row, or None without a gain).
+
+    dgain = sum over rows of dy x r; with u = dy w: dx = r u - r^3 x mean(u x).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    xn, r = rms_normalize(x, eps)
+    r = r[..., None]
+    if gain is not None:
+        w = round_f32(np.float64(round_f32(gain_center)) + np.asarray(gain, dtype=np.float64))
+        dgain = np.sum((dy * xn).reshape(-1, x.shape[-1]), axis=0)
+        u = dy * w
+    else:
+        dgain = None
+        u = dy
+    dx = r * u - r ** 3 * x * np.mean(u * x, axis=-1, keepdims=True)
+    return dx, dgain
+
+
+def qk_norm_rope_bwd(q, k, dq_hat, dk_hat, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
+                     query_scale=1.0, use_rope=True, cos=None, sin=None, normalize=True, rnd=True):
+    """Gradients through _qk_norm_rope_core (FP32 rotation): returns
+    (dq, dk, dq_gain, dk_gain).  ``cos``/``sin`` are the per-token rows [N, D/2]."""
+    dq1 = np.asarray(dq_hat, dtype=np.float64)
+    dk1 = np.asarray(dk_hat, dtype=np.float64)
+    if use_rope:
+        c = np.asarray(cos, dtype=np.float64)[:, None, :]
+        s = np.asarray(sin, dtype=np.float64)[:, None, :]
+        dq1 = _maybe_bf16(rope_rotate_bwd(dq1, c, s), rnd)
+        dk1 = _maybe_bf16(rope_rotate_bwd(dk1, c, s), rnd)
+    dq1 = _maybe_bf16(dq1 * np.float64(round_f32(query_scale)), rnd)
+    if not normalize:
+        return dq1, dk1, None, None
+    dq, dqg = rms_norm_bwd(q, dq1, eps, q_gain, gain_center)
+    dk, dkg = rms_norm_bwd(k, dk1, eps, k_gain, gain_center)
+    return _maybe_bf16(dq, rnd), _maybe_bf16(dk, rnd), dqg, dkg
+
+
+def attn_core_bwd(q, k, v, gate, dout, segments: Segments, *, theta, eps, out_eps, scaling,
+                  window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
+                  query_scale=1.0, position_ids=None, causal=True, key_valid=None, rnd=True):
+    """The whole backward: recomputes the forward (FP32 rotation), then returns a dict
+    with dq, dk, dv, dgate (bf16 values when rnd), dq_gain, dk_gain, and the forward's
+    o and lse, plus the intermediate d_o, dq_hat and dk_hat.
+
+    With rnd=False the forward is evaluated without any rounding, so the result
+    is the exact derivative of the real-valued composition.
+    """
+    d = q.shape[-1]
+    pos = segments.local_positions() if position_ids is None else np.asarray(position_ids)
+    cos, sin = rope_cos_sin(theta, d, pos) if use_rope else (None, None)
+    if rnd:
+        fw = attn_core(q, k, v, gate, segments, theta=theta, eps=eps, out_eps=out_eps,
+                       scaling=scaling, window=window, use_rope=use_rope, q_gain=q_gain,
+                       k_gain=k_gain, gain_center=gain_center, query_scale=query_scale,
+                       position_ids=position_ids, causal=causal, key_valid=key_valid)
+        q_hat, k_hat, o, lse = fw["q_hat"], fw["k_hat"], fw["o"], fw["lse"]
+    else:
+        q_hat, k_hat, o, lse = _exact_forward(q, k, v, segments, eps=eps, scaling=scaling,
+                                              window=window, use_rope=use_rope, cos=cos, sin=sin,
+                                              q_gain=q_gain, k_gain=k_gain, gain_center=gain_center,
+                                              query_scale=query_scale, causal=causal,
+                                              key_valid=key_valid)
+    d_o, dgate = out_norm_gate_bwd(o, gate, dout, out_eps, rnd)
+    dq_hat, dk_hat, dv = attention_bwd(q_hat, k_hat, v, d_o, segments, window=window, scaling=scaling,
+                                       causal=causal, key_valid=key_valid, rnd=rnd)
+    dq, dk, dqg, dkg = qk_norm_rope_bwd(q, k, dq_hat, dk_hat, eps=eps, q_gain=q_gain, k_gain=k_gain,
+                                        gain_center=gain_center, query_scale=query_scale,
+                                        use_rope=use_rope, cos=cos, sin=sin, rnd=rnd)
+    return dict(dq=dq, dk=dk, dv=dv, dgate=dgate, dq_gain=dqg, dk_gain=dkg, o=o, lse=lse,
+                d_o=d_o, dq_hat=dq_hat, dk_hat=dk_hat)
+
+
+def _exact_forward(q, k, v, segments, *, eps, scaling, window, use_rope, cos, sin, q_gain, k_gain,
+                   gain_center, query_scale, causal, key_valid):
+    """The forward with no rounding anywhere (for the exact-derivative mode)."""
+    def norm(x, gain):
+        y, _ = rms_normalize(x, eps)
+        if gain is not None:
+            y = y * round_f32(np.float64(round_f32(gain_center)) + np.asarray(gain, dtype=np.float64))
+        return y
+
+    def rot(x):
+        c = np.asarray(cos, dtype=np.float64)[:, None, :]
+        s = np.asarray(sin, dtype=np.float64)[:, None, :]
+        y = np.empty_like(x)
+        y[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+        y[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+        return y
+
+    q1 = norm(q, q_gain) * np.float64(round_f32(query_scale))
+    k1 = norm(k, k_gain)
+    if use_rope:
+        q1, k1 = rot(q1), rot(k1)
+    n, hq, d = q1.shape
+    groups = hq // k1.shape[1]
+    o = np.zeros_like(q1)
+    lse = np.zeros((n, hq))
+    for s0, length in zip(segments.starts, segments.lengths):
+        if length == 0:
+            continue
+        kok = None if key_valid is None else np.asarray(key_valid)[s0:s0 + length]
+        for h in range(hq):
+            ob, lb = _attend_block(q1[s0:s0 + length, h], k1[s0:s0 + length, h // groups],
+                                   np.asarray(v, dtype=np.float64)[s0:s0 + length, h // groups],
+                                   np.arange(length), window, scaling, causal, kok)
+            o[s0:s0 + length, h] = ob
+            lse[s0:s0 + length, h] = lb
+    return q1, k1, o, lse
