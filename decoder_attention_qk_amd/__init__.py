@@ -18,8 +18,10 @@ import os
 __all__ = [
     "MuseError", "AttnParams", "Layout", "library", "library_path", "symbols",
     "muse_rope_cos_sin", "muse_rope_cos_sin_2d", "muse_qk_norm_rope", "muse_gqa_attn_fwd",
-    "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_validate_cu_seqlens",
-    "muse_status_string", "muse_version",
+    "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd",
+    "muse_attn_bwd_delta", "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd",
+    "muse_qk_norm_rope_bwd_workspace_size", "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size",
+    "muse_validate_cu_seqlens", "muse_status_string", "muse_version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,8 +32,10 @@ MUSE_OK, MUSE_ERR_INVALID_ARG, MUSE_ERR_UNSUPPORTED, MUSE_ERR_DEVICE = 0, 1, 2, 
 # Every symbol include/muse_attn.h declares.
 symbols = (
     "muse_rope_cos_sin", "muse_rope_cos_sin_2d", "muse_qk_norm_rope", "muse_gqa_attn_fwd", "muse_out_norm_gate",
-    "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_validate_cu_seqlens", "muse_status_string",
-    "muse_last_error", "muse_version",
+    "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd", "muse_attn_bwd_delta",
+    "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd", "muse_qk_norm_rope_bwd_workspace_size",
+    "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size", "muse_validate_cu_seqlens",
+    "muse_status_string", "muse_last_error", "muse_version",
 )
 
 
@@ -68,6 +72,15 @@ _SIGS = {
     "muse_out_norm_gate": [_P, _P, _P, _P, _P, _P, _P],
     "muse_attn_core_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P],
     "muse_attn_fused_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
+    "muse_out_norm_gate_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "muse_attn_bwd_delta": [_P, _P, _P, _P, _P, _P],
+    "muse_gqa_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "muse_qk_norm_rope_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
+                              ctypes.c_size_t, _P],
+    "muse_qk_norm_rope_bwd_workspace_size": [_P, _P, _P],
+    "muse_attn_core_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                           _P, _P, ctypes.c_size_t, _P],
+    "muse_attn_core_bwd_workspace_size": [_P, _P, _P],
     "muse_validate_cu_seqlens": [_P, _I32, _I32, _I32],
     "muse_status_string": [ctypes.c_int],
     "muse_last_error": [],
@@ -345,6 +358,124 @@ def muse_attn_fused_fwd(params: AttnParams, layout: Layout, q, k_hat, v, gate, q
         _ptr(cos, "cos", "fp32"), _ptr(sin, "sin", "fp32"), n_pos, _ptr(out, "out", "bf16"),
         _ptr(lse, "lse", "fp32"), _stream(stream)))
     return out, lse
+
+
+# ---------------------------------------------------------------- backward
+
+def _workspace(fn, params, layout, workspace, like):
+    """A caller's workspace, or a fresh one of the size the library reports."""
+    import torch
+    size = ctypes.c_size_t(0)
+    p, l = params.to_c(), layout.to_c()
+    _check(fn(ctypes.byref(p), ctypes.byref(l), ctypes.byref(size)))
+    if workspace is None:
+        workspace = torch.empty(max(1, size.value), dtype=torch.uint8, device=like.device)
+    return workspace, size.value
+
+
+def _ws_ptr(ws):
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise TypeError("workspace: expected a contiguous GPU tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def muse_out_norm_gate_bwd(params: AttnParams, layout: Layout, o, gate, dout, *, d_o=None, dgate=None,
+                           delta=None, stream=None):
+    """Backward of the output norm + gate; returns (d_o, dgate, delta)."""
+    import torch
+    d_o = torch.empty_like(o) if d_o is None else d_o
+    dgate = torch.empty_like(o) if dgate is None else dgate
+    delta = _empty(o.shape[:2], torch.float32, o) if delta is None else delta
+    p, l = params.to_c(), layout.to_c()
+    _check(library().muse_out_norm_gate_bwd(
+        ctypes.byref(p), ctypes.byref(l), _ptr(o, "o", "bf16"), _ptr(gate, "gate", "bf16"),
+        _ptr(dout, "dout", "bf16"), _ptr(d_o, "d_o", "bf16"), _ptr(dgate, "dgate", "bf16"),
+        _ptr(delta, "delta", "fp32"), _stream(stream)))
+    return d_o, dgate, delta
+
+
+def muse_attn_bwd_delta(params: AttnParams, layout: Layout, o, d_o, *, delta=None, stream=None):
+    """delta = rowsum(d_o * o) [N, Hq] fp32."""
+    import torch
+    delta = _empty(o.shape[:2], torch.float32, o) if delta is None else delta
+    p, l = params.to_c(), layout.to_c()
+    _check(library().muse_attn_bwd_delta(ctypes.byref(p), ctypes.byref(l), _ptr(o, "o", "bf16"),
+                                         _ptr(d_o, "d_o", "bf16"), _ptr(delta, "delta", "fp32"),
+                                         _stream(stream)))
+    return delta
+
+
+def muse_gqa_attn_bwd(params: AttnParams, layout: Layout, q_hat, k_hat, v, d_o, lse, delta, *,
+                      dq_hat=None, dk_hat=None, dv=None, stream=None):
+    """Attention backward; returns (dq_hat, dk_hat, dv)."""
+    import torch
+    dq_hat = torch.empty_like(q_hat) if dq_hat is None else dq_hat
+    dk_hat = torch.empty_like(k_hat) if dk_hat is None else dk_hat
+    dv = torch.empty_like(v) if dv is None else dv
+    p, l = params.to_c(), layout.to_c()
+    _check(library().muse_gqa_attn_bwd(
+        ctypes.byref(p), ctypes.byref(l), _ptr(q_hat, "q_hat", "bf16"), _ptr(k_hat, "k_hat", "bf16"),
+        _ptr(v, "v", "bf16"), _ptr(d_o, "d_o", "bf16"), _ptr(lse, "lse", "fp32"),
+        _ptr(delta, "delta", "fp32"), _ptr(dq_hat, "dq_hat", "bf16"), _ptr(dk_hat, "dk_hat", "bf16"),
+        _ptr(dv, "dv", "bf16"), _stream(stream)))
+    return dq_hat, dk_hat, dv
+
+
+def muse_qk_norm_rope_bwd(params: AttnParams, layout: Layout, q, k, q_gain, k_gain, cos, sin, dq_hat,
+                          dk_hat, *, dq=None, dk=None, dq_gain=None, dk_gain=None, workspace=None,
+                          stream=None):
+    """Backward of the Q/K norm + RoPE; returns (dq, dk, dq_gain, dk_gain)."""
+    import torch
+    like = q if q is not None else k
+    if q is not None and dq is None:
+        dq = torch.empty_like(q)
+    if k is not None and dk is None:
+        dk = torch.empty_like(k)
+    if q_gain is not None and dq_gain is None:
+        dq_gain = torch.empty_like(q_gain)
+    if k_gain is not None and dk_gain is None:
+        dk_gain = torch.empty_like(k_gain)
+    workspace, _ = _workspace(library().muse_qk_norm_rope_bwd_workspace_size, params, layout, workspace, like)
+    wp, wb = _ws_ptr(workspace)
+    n_pos = cos.shape[0] if cos is not None else 0
+    p, l = params.to_c(), layout.to_c()
+    _check(library().muse_qk_norm_rope_bwd(
+        ctypes.byref(p), ctypes.byref(l), _ptr(q, "q", "bf16"), _ptr(k, "k", "bf16"),
+        _ptr(q_gain, "q_gain", "fp32"), _ptr(k_gain, "k_gain", "fp32"), _ptr(cos, "cos", "fp32"),
+        _ptr(sin, "sin", "fp32"), n_pos, _ptr(dq_hat, "dq_hat", "bf16"), _ptr(dk_hat, "dk_hat", "bf16"),
+        _ptr(dq, "dq", "bf16"), _ptr(dk, "dk", "bf16"), _ptr(dq_gain, "dq_gain", "fp32"),
+        _ptr(dk_gain, "dk_gain", "fp32"), wp, wb, _stream(stream)))
+    return dq, dk, dq_gain, dk_gain
+
+
+def muse_attn_core_bwd(params: AttnParams, layout: Layout, q, k, v, gate, dout, q_gain=None, k_gain=None,
+                       cos=None, sin=None, o=None, lse=None, *, dq=None, dk=None, dv=None, dgate=None,
+                       dq_gain=None, dk_gain=None, workspace=None, stream=None):
+    """Backward of the whole core; returns (dq, dk, dv, dgate, dq_gain, dk_gain).
+
+    o and lse from the forward (attention output before the output norm, and
+    its LSE) may be omitted together: they are recomputed."""
+    import torch
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dgate = torch.empty_like(gate) if dgate is None else dgate
+    if q_gain is not None and dq_gain is None:
+        dq_gain = torch.empty_like(q_gain)
+    if k_gain is not None and dk_gain is None:
+        dk_gain = torch.empty_like(k_gain)
+    workspace, _ = _workspace(library().muse_attn_core_bwd_workspace_size, params, layout, workspace, q)
+    wp, wb = _ws_ptr(workspace)
+    n_pos = cos.shape[0] if cos is not None else 0
+    p, l = params.to_c(), layout.to_c()
+    _check(library().muse_attn_core_bwd(
+        ctypes.byref(p), ctypes.byref(l), _ptr(q, "q", "bf16"), _ptr(k, "k", "bf16"), _ptr(v, "v", "bf16"),
+        _ptr(gate, "gate", "bf16"), _ptr(q_gain, "q_gain", "fp32"), _ptr(k_gain, "k_gain", "fp32"),
+        _ptr(cos, "cos", "fp32"), _ptr(sin, "sin", "fp32"), n_pos, _ptr(o, "o", "bf16"),
+        _ptr(lse, "lse", "fp32"), _ptr(dout, "dout", "bf16"), _ptr(dq, "dq", "bf16"), _ptr(dk, "dk", "bf16"),
+        _ptr(dv, "dv", "bf16"), _ptr(dgate, "dgate", "bf16"), _ptr(dq_gain, "dq_gain", "fp32"),
+        _ptr(dk_gain, "dk_gain", "fp32"), wp, wb, _stream(stream)))
+    return dq, dk, dv, dgate, dq_gain, dk_gain
 
 
 def muse_validate_cu_seqlens(cu_seqlens, num_segments, total_tokens, max_seqlen) -> int:

@@ -14,8 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmuseattn.so")
 
-SOURCES = ["rope_table.hip", "qk_norm_rope.hip", "out_norm_gate.hip", "attn_fwd.hip", "api.cpp",
-           "validate.cpp"]
+SOURCES = ["rope_table.hip", "qk_norm_rope.hip", "out_norm_gate.hip", "attn_fwd.hip", "norm_bwd.hip",
+           "attn_bwd.hip", "api.cpp", "validate.cpp"]
 # Per-source extra flags.  The attention kernel never forms a NaN score (masked
 # scores are -inf, never NaN), so max() needs no NaN quieting; infinities stay
 # honoured.

@@ -406,3 +406,294 @@ extern "C" muse_status muse_attn_core_fwd(const muse_attn_params *p, const muse_
   if (s != MUSE_OK) return s;
   return muse_attn_fused_fwd(p, l, q, k_hat_out, v, gate, q_gain, cos, sin, n_pos, out, lse, stream);
 }
+
+// ---------------------------------------------------------------- backward
+
+namespace muse {
+namespace {
+
+constexpr size_t kWsAlign = 256;
+size_t ws_round(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// The FP32 rotation is the only one with a backward here.
+muse_status check_bwd_params(const muse_attn_params *p) {
+  if (p->use_rope && !p->upcast_rope)
+    return set_error(MUSE_ERR_UNSUPPORTED, "the backward of the Q/K-dtype rotation (upcast_rope = 0) is not built");
+  return MUSE_OK;
+}
+
+size_t qk_bwd_partial_bytes(const Geometry &g, bool q_gain, bool k_gain) {
+  int32_t qb = 0, kb = 0;
+  qk_norm_bwd_blocks(g.d, g.n_tokens * g.hq, g.n_tokens * g.hkv, &qb, &kb);
+  return ws_round((size_t)(q_gain ? qb : 0) * g.d * 4) + ws_round((size_t)(k_gain ? kb : 0) * g.d * 4);
+}
+
+// Core workspace: q_hat, k_hat, o, lse, d_o, delta, dq_hat, dk_hat, gain partials.
+struct CoreWs {
+  size_t q_hat, k_hat, o, lse, d_o, delta, dq_hat, dk_hat, part, total;
+};
+CoreWs core_ws(const Geometry &g) {
+  CoreWs w;
+  const size_t nq = (size_t)g.n_tokens * g.hq, nk = (size_t)g.n_tokens * g.hkv;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off += ws_round(bytes); return at; };
+  w.q_hat = take(nq * g.d * 2);
+  w.k_hat = take(nk * g.d * 2);
+  w.o = take(nq * g.d * 2);
+  w.lse = take(nq * 4);
+  w.d_o = take(nq * g.d * 2);
+  w.delta = take(nq * 4);
+  w.dq_hat = take(nq * g.d * 2);
+  w.dk_hat = take(nk * g.d * 2);
+  w.part = take(qk_bwd_partial_bytes(g, true, true));
+  w.total = off;
+  return w;
+}
+
+muse_status check_workspace(void *ws, size_t have, size_t need) {
+  if (need == 0) return MUSE_OK;
+  if (!ws) return set_error(MUSE_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", need);
+  if ((uintptr_t)ws % 16) return set_error(MUSE_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (have < need) return set_error(MUSE_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed", have, need);
+  return MUSE_OK;
+}
+
+AttnBwdArgs attn_bwd_args(const muse_attn_params *p, const muse_layout *l, const Geometry &g) {
+  AttnBwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.scaling = p->scaling;
+  a.scale_log2 = p->scaling * 1.4426950408889634f;
+  a.hq = g.hq;
+  a.hkv = g.hkv;
+  a.group = g.group;
+  attn_shape(g.group, &a.heads_per_wg, &a.tok_per_wg, &a.head_chunks);
+  a.window = p->sliding_window > 0 ? p->sliding_window : 0;
+  a.bidirectional = p->bidirectional ? 1 : 0;
+  a.key_valid = g.thd ? nullptr : l->attention_mask;
+  a.q_blocks = (g.maxlen + a.tok_per_wg - 1) / a.tok_per_wg;
+  const int kpw = attn_bwd_keys_per_workgroup();
+  a.k_blocks = (g.maxlen + kpw - 1) / kpw;
+  a.lay = token_layout(l, g);
+  return a;
+}
+
+}  // namespace
+}  // namespace muse
+
+extern "C" muse_status muse_out_norm_gate_bwd(const muse_attn_params *p, const muse_layout *l, const void *o,
+                                              const void *gate, const void *dout, void *d_o, void *dgate,
+                                              float *delta, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  if (N > 0 && (!o || !gate || !dout || !d_o || !dgate || !delta))
+    return set_error(MUSE_ERR_INVALID_ARG, "o, gate, dout, d_o, dgate and delta are required");
+  const int64_t tb = bf16_bytes(N, g.hq, g.d);
+  s = check_disjoint({{o, tb, "o"}, {gate, tb, "gate"}, {dout, tb, "dout"}},
+                     {{d_o, tb, "d_o"}, {dgate, tb, "dgate"}, {delta, N * g.hq * 4, "delta", 4}});
+  if (s != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  OutGateBwdArgs a{(const uint16_t *)o, (const uint16_t *)gate, (const uint16_t *)dout, (uint16_t *)d_o,
+                   (uint16_t *)dgate, delta, N * g.hq, p->out_eps};
+  return device_status(launch_out_norm_gate_bwd(g.d, a, (hipStream_t)stream), "out_norm_gate_bwd launch");
+}
+
+extern "C" muse_status muse_attn_bwd_delta(const muse_attn_params *p, const muse_layout *l, const void *o,
+                                           const void *d_o, float *delta, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  if (N > 0 && (!o || !d_o || !delta)) return set_error(MUSE_ERR_INVALID_ARG, "o, d_o and delta are required");
+  const int64_t tb = bf16_bytes(N, g.hq, g.d);
+  s = check_disjoint({{o, tb, "o"}, {d_o, tb, "d_o"}}, {{delta, N * g.hq * 4, "delta", 4}});
+  if (s != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  OutGateBwdArgs a{(const uint16_t *)o, nullptr, (const uint16_t *)d_o, nullptr, nullptr, delta, N * g.hq, 0.0f};
+  return device_status(launch_out_norm_gate_bwd(g.d, a, (hipStream_t)stream), "attention delta launch");
+}
+
+extern "C" muse_status muse_gqa_attn_bwd(const muse_attn_params *p, const muse_layout *l, const void *q_hat,
+                                         const void *k_hat, const void *v, const void *d_o, const float *lse,
+                                         const float *delta, void *dq_hat, void *dk_hat, void *dv, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  if (N > 0 && (!q_hat || !k_hat || !v || !d_o || !lse || !delta || !dq_hat || !dk_hat || !dv))
+    return set_error(MUSE_ERR_INVALID_ARG, "every tensor of the attention backward is required");
+  const int64_t qb = bf16_bytes(N, g.hq, g.d), kb = bf16_bytes(N, g.hkv, g.d);
+  s = check_disjoint({{q_hat, qb, "q_hat"}, {k_hat, kb, "k_hat"}, {v, kb, "v"}, {d_o, qb, "d_o"},
+                      {lse, N * g.hq * 4, "lse", 4}, {delta, N * g.hq * 4, "delta", 4}, layout_range(l, g, 0),
+                      layout_range(l, g, 1), layout_range(l, g, 2)},
+                     {{dq_hat, qb, "dq_hat"}, {dk_hat, kb, "dk_hat"}, {dv, kb, "dv"}});
+  if (s != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  AttnBwdArgs a = attn_bwd_args(p, l, g);
+  a.q = (const uint16_t *)q_hat;
+  a.k = (const uint16_t *)k_hat;
+  a.v = (const uint16_t *)v;
+  a.d_o = (const uint16_t *)d_o;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = (uint16_t *)dq_hat;
+  a.dk = (uint16_t *)dk_hat;
+  a.dv = (uint16_t *)dv;
+  return device_status(launch_attn_bwd(g.d, a, (hipStream_t)stream), "attention backward launch");
+}
+
+extern "C" muse_status muse_qk_norm_rope_bwd_workspace_size(const muse_attn_params *p, const muse_layout *l,
+                                                            size_t *bytes) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, nullptr, &g);
+  if (s != MUSE_OK) return s;
+  if (!bytes) return set_error(MUSE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = p->skip_qk_norm ? 0 : qk_bwd_partial_bytes(g, true, true);
+  clear_error();
+  return MUSE_OK;
+}
+
+extern "C" muse_status muse_qk_norm_rope_bwd(const muse_attn_params *p, const muse_layout *l, const void *q,
+                                             const void *k, const float *q_gain, const float *k_gain,
+                                             const float *cos, const float *sin, int32_t n_pos, const void *dq_hat,
+                                             const void *dk_hat, void *dq, void *dk, float *dq_gain, float *dk_gain,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  if ((s = check_bwd_params(p)) != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  const bool has_q = q || dq_hat || dq, has_k = k || dk_hat || dk;
+  if (has_q && !(q && dq_hat && dq)) return set_error(MUSE_ERR_INVALID_ARG, "q, dq_hat and dq must be given together");
+  if (has_k && !(k && dk_hat && dk)) return set_error(MUSE_ERR_INVALID_ARG, "k, dk_hat and dk must be given together");
+  if (!has_q && !has_k) return set_error(MUSE_ERR_INVALID_ARG, "neither q nor k given");
+  if ((q_gain != nullptr) != (dq_gain != nullptr) || (k_gain != nullptr) != (dk_gain != nullptr))
+    return set_error(MUSE_ERR_INVALID_ARG, "a gain gradient is given exactly when its gain is");
+  if ((q_gain && !has_q) || (k_gain && !has_k))
+    return set_error(MUSE_ERR_INVALID_ARG, "a gain is given without its tensor");
+  if (p->skip_qk_norm && (q_gain || k_gain))
+    return set_error(MUSE_ERR_INVALID_ARG, "skip_qk_norm takes no gains");
+  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  const int64_t qb = bf16_bytes(N, g.hq, g.d), kb = bf16_bytes(N, g.hkv, g.d);
+  const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
+  const size_t need = (q_gain || k_gain) ? qk_bwd_partial_bytes(g, q_gain != nullptr, k_gain != nullptr) : 0;
+  s = check_disjoint({{q, qb, "q"}, {k, kb, "k"}, {q_gain, g.d * 4, "q_gain"}, {k_gain, g.d * 4, "k_gain"},
+                      {cos, tab, "cos"}, {sin, tab, "sin"}, {dq_hat, qb, "dq_hat"}, {dk_hat, kb, "dk_hat"},
+                      layout_range(l, g, 0), layout_range(l, g, 1)},
+                     {{dq, qb, "dq"}, {dk, kb, "dk"}, {dq_gain, g.d * 4, "dq_gain"}, {dk_gain, g.d * 4, "dk_gain"},
+                      {workspace, (int64_t)need, "workspace"}});
+  if (s != MUSE_OK) return s;
+  if ((s = check_workspace(workspace, workspace_bytes, need)) != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  QkNormBwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.dq_hat = (const uint16_t *)dq_hat;
+  a.dk_hat = (const uint16_t *)dk_hat;
+  a.dq = (uint16_t *)dq;
+  a.dk = (uint16_t *)dk;
+  a.q_gain = q_gain;
+  a.k_gain = k_gain;
+  a.cos_tab = cos;
+  a.sin_tab = sin;
+  a.n_pos = n_pos;
+  a.hq_div = FastDiv((uint32_t)g.hq);
+  a.hkv_div = FastDiv((uint32_t)g.hkv);
+  a.q_rows = has_q ? (int32_t)(N * g.hq) : 0;
+  a.k_rows = has_k ? (int32_t)(N * g.hkv) : 0;
+  int32_t nqb = 0, nkb = 0;
+  qk_norm_bwd_blocks(g.d, a.q_rows, a.k_rows, &nqb, &nkb);
+  a.q_part = q_gain ? (float *)workspace : nullptr;
+  a.k_part = k_gain ? (float *)((char *)workspace + (q_gain ? ws_round((size_t)nqb * g.d * 4) : 0)) : nullptr;
+  a.dq_gain = dq_gain;
+  a.dk_gain = dk_gain;
+  a.eps = p->qk_eps;
+  a.gain_center = p->gain_center;
+  a.query_scale = p->query_scale;
+  a.use_rope = p->use_rope ? 1 : 0;
+  a.skip_norm = p->skip_qk_norm ? 1 : 0;
+  a.lay = token_layout(l, g);
+  return device_status(launch_qk_norm_rope_bwd(g.d, a, (hipStream_t)stream), "qk_norm_rope_bwd launch");
+}
+
+extern "C" muse_status muse_attn_core_bwd_workspace_size(const muse_attn_params *p, const muse_layout *l,
+                                                         size_t *bytes) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, nullptr, &g);
+  if (s != MUSE_OK) return s;
+  if (!bytes) return set_error(MUSE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = core_ws(g).total;
+  clear_error();
+  return MUSE_OK;
+}
+
+extern "C" muse_status muse_attn_core_bwd(const muse_attn_params *p, const muse_layout *l, const void *q,
+                                          const void *k, const void *v, const void *gate, const float *q_gain,
+                                          const float *k_gain, const float *cos, const float *sin, int32_t n_pos,
+                                          const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                                          void *dv, void *dgate, float *dq_gain, float *dk_gain, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  if ((s = check_bwd_params(p)) != MUSE_OK) return s;
+  if (p->skip_qk_norm) return set_error(MUSE_ERR_UNSUPPORTED, "the core normalises Q/K; skip_qk_norm is for muse_qk_norm_rope_bwd");
+  Geometry g;
+  s = check_layout(l, p, (hipStream_t)stream, &g);
+  if (s != MUSE_OK) return s;
+  const int64_t N = g.n_tokens;
+  if (N > 0 && (!q || !k || !v || !gate || !dout || !dq || !dk || !dv || !dgate))
+    return set_error(MUSE_ERR_INVALID_ARG, "q, k, v, gate, dout, dq, dk, dv and dgate are required");
+  if ((o == nullptr) != (lse == nullptr))
+    return set_error(MUSE_ERR_INVALID_ARG, "o and lse are given together (or both recomputed)");
+  if ((q_gain != nullptr) != (dq_gain != nullptr) || (k_gain != nullptr) != (dk_gain != nullptr))
+    return set_error(MUSE_ERR_INVALID_ARG, "a gain gradient is given exactly when its gain is");
+  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  if (s != MUSE_OK) return s;
+  const CoreWs w = core_ws(g);
+  const int64_t qb = bf16_bytes(N, g.hq, g.d), kb = bf16_bytes(N, g.hkv, g.d);
+  const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
+  s = check_disjoint({{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {gate, qb, "gate"}, {q_gain, g.d * 4, "q_gain"},
+                      {k_gain, g.d * 4, "k_gain"}, {cos, tab, "cos"}, {sin, tab, "sin"}, {o, qb, "o"},
+                      {lse, N * g.hq * 4, "lse", 4}, {dout, qb, "dout"}, layout_range(l, g, 0),
+                      layout_range(l, g, 1), layout_range(l, g, 2)},
+                     {{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {dgate, qb, "dgate"},
+                      {dq_gain, g.d * 4, "dq_gain"}, {dk_gain, g.d * 4, "dk_gain"},
+                      {workspace, (int64_t)w.total, "workspace"}});
+  if (s != MUSE_OK) return s;
+  if ((s = check_workspace(workspace, workspace_bytes, w.total)) != MUSE_OK) return s;
+  if (N == 0) { clear_error(); return MUSE_OK; }
+  char *ws = (char *)workspace;
+  void *q_hat = ws + w.q_hat, *k_hat = ws + w.k_hat;
+  // forward recompute: Q/K norm + RoPE (and the attention output when not kept)
+  s = muse_qk_norm_rope(p, l, q, k, q_gain, k_gain, cos, sin, n_pos, q_hat, k_hat, nullptr, nullptr, stream);
+  if (s != MUSE_OK) return s;
+  if (!o) {
+    o = ws + w.o;
+    lse = (const float *)(ws + w.lse);
+    s = muse_gqa_attn_fwd(p, l, q_hat, k_hat, v, (void *)o, (float *)lse, stream);
+    if (s != MUSE_OK) return s;
+  }
+  void *d_o = ws + w.d_o, *dq_hat = ws + w.dq_hat, *dk_hat = ws + w.dk_hat;
+  float *delta = (float *)(ws + w.delta);
+  s = muse_out_norm_gate_bwd(p, l, o, gate, dout, d_o, dgate, delta, stream);
+  if (s != MUSE_OK) return s;
+  s = muse_gqa_attn_bwd(p, l, q_hat, k_hat, v, d_o, lse, delta, dq_hat, dk_hat, dv, stream);
+  if (s != MUSE_OK) return s;
+  return muse_qk_norm_rope_bwd(p, l, q, k, q_gain, k_gain, cos, sin, n_pos, dq_hat, dk_hat, dq, dk, dq_gain,
+                               dk_gain, ws + w.part, w.total - w.part, stream);
+}

@@ -1,0 +1,506 @@
+// Backward of the causal/windowed/bidirectional GQA attention on bf16 MFMA
+// (gfx950): the chain rule through layers page, MuseSparkAttention's softmax
+// attention (scaling = head_dim^-0.5, KV heads repeated to the query-head
+// count, model page _causal_mask), given the forward's LSE and
+// delta = rowsum(dO * O):
+//   P = exp(scaling q k^T - lse),  dP = dO v^T,  dS = P (dP - delta),
+//   dq = scaling dS k,  dk = scaling dS^T q,  dv = P^T dO
+// with dk and dv summed over the query heads of each KV head.
+//
+// Two kernels, no atomics, so every result is deterministic:
+//
+// dQ kernel -- the forward's work shape: a workgroup of 4 waves owns 128
+//   (token, head) query columns of one KV group; K and V tiles of 64 keys
+//   stream through LDS by DMA (double-buffered).  Per 32-key half a wave
+//   forms S^T = K Q^T and dP^T = V dO^T (lane l owns query column l % 32, so
+//   its LSE and delta are one register each), P^T and dS^T in registers, and
+//   dQ^T += K^T dS^T with dS^T in the B-operand layout and K^T read by
+//   ds_read_b64_tr_b16 -- the forward's O^T += V^T P^T step.
+//
+// dK/dV kernel -- keys stationary: a workgroup owns 128 keys of one KV head,
+//   32 per wave, held as B fragments (K and V) in registers; Q and dO tiles
+//   of 64 tokens of one query head stream through LDS together with their
+//   LSE and delta rows, for every head of the group.  Per 32-query half a
+//   wave forms S = Q K^T and dP = dO V^T (lane l owns key column l % 32),
+//   then dV^T += dO^T P and dK^T += Q^T dS with P and dS in the B-operand
+//   layout and dO^T, Q^T read transposed from LDS.
+//
+// Tiles are read both row-wise and transposed, so their 16-byte chunks use
+// the swizzle that keeps both patterns free of bank conflicts (Tile::swz_kv).
+// Masked scores get P = 0 explicitly (a query whose every key is padding has
+// lse = -inf).  Tiles no wave of the workgroup can see are never loaded.
+#include <cmath>
+
+#include "attn_common.hpp"
+#include "kernels.hpp"
+
+namespace muse {
+
+namespace {
+
+constexpr int BN = 64;        // keys (dQ) or queries (dK/dV) per LDS tile
+constexpr int NW = 4;         // waves per workgroup
+constexpr int COLS = 32 * NW; // dQ: query columns per workgroup; dK/dV: keys per workgroup
+static_assert(BN == 64, "Tile<D> holds 64-row tiles");
+
+// Row-fragment read addresses (A operand: lane row n, chunk 2 ks + g) and the
+// two transposed-read address sets (rows 4 g + (r >> 2) and 8 more) of a
+// swz_kv tile.
+template <int D>
+struct TileAddr {
+  int row[D / 16];
+  int tr_lo[D / 32], tr_hi[D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    using T = Tile<D>;
+    constexpr int RB = T::ROW_BYTES;
+    const int n = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) row[ks] = n * RB + (((2 * ks + g) ^ T::swz_kv(n)) << 4);
+    const int r = lane & 15, q = (lane >> 4) & 1;
+    const int r0 = 4 * g + (r >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int ch = dt * 4 + 2 * q + ((r & 3) >> 1);
+      tr_lo[dt] = r0 * RB + ((ch ^ T::swz_kv(r0)) << 4) + (r & 1) * 8;
+      tr_hi[dt] = (r0 + 8) * RB + ((ch ^ T::swz_kv(r0 + 8)) << 4) + (r & 1) * 8;
+    }
+  }
+};
+
+// A fragments of 32 rows x D from a tile (rows base .. base + 31), then
+// acc += A B over the D/16 k-steps.
+template <int D>
+__device__ __forceinline__ f32x16 rows_times(const lds_char *tile, const TileAddr<D> &ad, int base_bytes,
+                                             const bf16x8 (&b)[D / 16]) {
+  constexpr int KS = D / 16;
+  bf16x8 af[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    af[ks] = *(const __attribute__((address_space(3))) bf16x8 *)(tile + ad.row[ks] + base_bytes);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], b[ks], acc, 0, 0, 0);
+  return acc;
+}
+
+// acc[dt] += (tile rows base .. base + 31)^T (D x 32) times the B fragments
+// b0 (rows base .. base + 15) and b1 (base + 16 .. base + 31).
+template <int D>
+__device__ __forceinline__ void tr_times(const lds_char *tile, const TileAddr<D> &ad, int base_row,
+                                         const bf16x8 &b0, const bf16x8 &b1, f32x16 (&acc)[D / 32]) {
+  constexpr int RB = Tile<D>::ROW_BYTES;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int r0 = (base_row + 16 * kk) * RB;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4 *)(tile + ad.tr_lo[dt] + r0));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4 *)(tile + ad.tr_hi[dt] + r0));
+      const bf16x8 af = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, kk ? b1 : b0, acc[dt], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void pack16(const float (&x)[16], bf16x8 &b0, bf16x8 &b1) {
+  uint4 lo, hi;
+  lo.x = pack_bf16x2(x[0], x[1]);   lo.y = pack_bf16x2(x[2], x[3]);
+  lo.z = pack_bf16x2(x[4], x[5]);   lo.w = pack_bf16x2(x[6], x[7]);
+  hi.x = pack_bf16x2(x[8], x[9]);   hi.y = pack_bf16x2(x[10], x[11]);
+  hi.z = pack_bf16x2(x[12], x[13]); hi.w = pack_bf16x2(x[14], x[15]);
+  b0 = __builtin_bit_cast(bf16x8, lo);
+  b1 = __builtin_bit_cast(bf16x8, hi);
+}
+
+// Store a D x 32 accumulator (element i of tile dt: d = 32 dt + 8 (i/4) +
+// 4 g + i%4, column = this lane's) scaled by s, as bf16, to row ptr.
+template <int D>
+__device__ __forceinline__ void store_cols(uint16_t *ptr, const f32x16 (&acc)[D / 32], float s, int g,
+                                           bool zero) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      uint2 w;
+      w.x = zero ? 0u : pack_bf16x2(acc[dt][i4 * 4 + 0] * s, acc[dt][i4 * 4 + 1] * s);
+      w.y = zero ? 0u : pack_bf16x2(acc[dt][i4 * 4 + 2] * s, acc[dt][i4 * 4 + 3] * s);
+      *reinterpret_cast<uint2 *>(ptr + dt * 32 + i4 * 8 + g * 4) = w;
+    }
+}
+
+// Segment bounds of segment `seg` (BSHD row or packed document).
+__device__ __forceinline__ void segment_bounds(const TokenLayout &l, int seg, int &s0, int &L) {
+  if (l.cu_seqlens) {
+    const int T_ = l.n_tokens;
+    int c0 = l.cu_seqlens[seg];
+    int c1 = l.cu_seqlens[seg + 1];
+    c0 = min(max(c0, 0), T_);
+    c1 = min(max(c1, c0), T_);
+    s0 = c0;
+    L = c1 - c0;
+  } else {
+    s0 = seg * l.seqlen;
+    L = l.seqlen;
+  }
+}
+
+// ===========================================================================
+template <int D, bool PAD>
+__global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+  using T = Tile<D>;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int DMA_PER_WAVE = T::TILE_BYTES / 1024 / NW;
+  __shared__ __attribute__((aligned(16))) char lds_k0[T::TILE_BYTES], lds_v0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_k1[T::TILE_BYTES], lds_v1[T::TILE_BYTES];
+  auto kbuf = [&](int buf) __attribute__((always_inline)) { return (lds_char *)(buf ? lds_k1 : lds_k0); };
+  auto vbuf = [&](int buf) __attribute__((always_inline)) { return (lds_char *)(buf ? lds_v1 : lds_v0); };
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+
+  // work item: as the forward (segment-major, longest query blocks first, kv head)
+  const int per_seg = a.q_blocks * a.hkv * a.head_chunks;
+  const int b = blockIdx.x;
+  const int seg = b / per_seg;
+  int rest = b % per_seg;
+  const int qb = a.q_blocks - 1 - rest / (a.hkv * a.head_chunks);
+  rest %= a.hkv * a.head_chunks;
+  const int hc = rest % a.head_chunks;
+  const int kvh = rest / a.head_chunks;
+  int s0, L;
+  segment_bounds(a.lay, seg, s0, L);
+  const int HPW = a.heads_per_wg;
+  const int BMT = a.tok_per_wg;
+  const int q0 = qb * BMT;
+  if (q0 >= L) return;
+  const int q1 = min(q0 + BMT, L);
+
+  const int col = wave * 32 + n;
+  const int ct = col / HPW;
+  const int head = kvh * a.group + hc * HPW + (col - ct * HPW);
+  const int qpos = q0 + ct;
+  const bool qvalid = ct < BMT && qpos < L;
+  const int wcol0 = wave * 32;
+  const int wcol1 = min(wcol0 + 31, BMT * HPW - 1);
+  const bool wave_active = wcol0 < BMT * HPW && q0 + wcol0 / HPW < L;
+  const int q0w = q0 + wcol0 / HPW;
+  const int q1w = min(q0 + wcol1 / HPW + 1, q1);
+  const int64_t lrow = (int64_t)(s0 + (qvalid ? qpos : 0)) * a.hq + (qvalid ? head : 0);
+  const int64_t qrow = lrow * D;
+
+  // stationary B fragments: q_hat and dO of this lane's column (d = 16 ks + 8 g + [0, 8))
+  bf16x8 qf[KS], dof[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint4 zq = make_uint4(0, 0, 0, 0);
+    qf[ks] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4 *>(a.q + qrow + ks * 16 + g * 8) : zq);
+    dof[ks] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4 *>(a.d_o + qrow + ks * 16 + g * 8) : zq);
+  }
+  const float lse2 = qvalid ? a.lse[lrow] * kLog2e : 0.0f;
+  const float dlt = qvalid ? a.delta[lrow] : 0.0f;
+
+  const int64_t kv_stride = (int64_t)a.hkv * D;
+  const uint16_t *kbase = a.k + ((int64_t)s0 * a.hkv + kvh) * D;
+  const uint16_t *vbase = a.v + ((int64_t)s0 * a.hkv + kvh) * D;
+  int off[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int slot = (wave * DMA_PER_WAVE + i) * 64 + lane;
+    const int row = slot / T::CHUNKS;
+    const int pch = slot % T::CHUNKS;
+    off[i] = (row * (int)kv_stride + (pch ^ T::swz_kv(row)) * 8) * 2;
+  }
+  TileAddr<D> ad;
+  ad.init(lane);
+
+  const uint8_t *kvalid = a.key_valid + s0;   // read only when PAD
+  int vbyte = 1;
+  uint64_t kmask = ~0ull;
+  auto take_mask = [&]() __attribute__((always_inline)) {
+    if constexpr (PAD) kmask = __ballot(vbyte != 0);
+  };
+
+  auto issue_dma = [&](int kt, int buf) {
+    const int k0 = kt * BN;
+    if constexpr (PAD) vbyte = k0 + lane < L ? (int)kvalid[k0 + lane] : 0;
+    lds_char *kdst = kbuf(buf) + wave * DMA_PER_WAVE * 1024;
+    lds_char *vdst = vbuf(buf) + wave * DMA_PER_WAVE * 1024;
+    const int valid_bytes = ((min(L - k0, BN) - 1) * (int)kv_stride + D) * 2;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)k0 * kv_stride, valid_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)k0 * kv_stride, valid_bytes);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      dma16(kr, off[i], kdst + i * 1024);
+      dma16(vr, off[i], vdst + i * 1024);
+    }
+  };
+
+  f32x16 dqacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dqacc[dt] = f32x16{};
+
+  const int W = a.window;
+  const bool bidir = a.bidirectional != 0;
+  const float c2 = a.scale_log2;
+  constexpr int RB = T::ROW_BYTES;
+
+  auto compute = [&](int kt, int BUF) __attribute__((always_inline)) {
+    const int k0 = kt * BN;
+    const bool none_visible = !wave_active || (!bidir && ((k0 > q1w - 1) || (W > 0 && k0 + BN - 1 <= q0w - W)));
+    if (none_visible) return;
+    const bool all_visible = bidir ? k0 + BN <= L : (k0 + BN - 1 <= q0w) && (W <= 0 || k0 > q1w - 1 - W);
+    const bool padded = PAD && kmask != ~0ull;
+    const lds_char *Kt = kbuf(BUF);
+    const lds_char *Vt = vbuf(BUF);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const f32x16 s = rows_times<D>(Kt, ad, half * 32 * RB, qf);
+      const f32x16 dp = rows_times<D>(Vt, ad, half * 32 * RB, dof);
+      float p[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2));
+      if (!all_visible || padded) {
+        const uint32_t kbits = (uint32_t)(kmask >> (half * 32 + g * 4));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kp = k0 + half * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+          bool vis = bidir ? kp < L : kp <= qpos && (W <= 0 || kp > qpos - W);
+          if (padded) vis = vis && ((kbits >> ((i >> 2) * 8 + (i & 3))) & 1u);
+          p[i] = vis ? p[i] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp[i] - dlt);
+      bf16x8 d0, d1;
+      pack16(ds, d0, d1);
+      tr_times<D>(Kt, ad, half * 32, d0, d1, dqacc);
+    }
+  };
+
+  const int lo = W > 0 && !bidir ? max(0, q0 - W + 1) : 0;
+  const int kt_lo = lo / BN;
+  const int kt_hi = ((bidir ? L : q1) - 1) / BN;
+  const int ntiles = kt_hi - kt_lo + 1;
+
+  issue_dma(kt_hi, 0);
+  vmem_wait_all();
+  __syncthreads();
+  for (int it = 0;;) {
+    take_mask();
+    if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 1);
+    compute(kt_hi - it, 0);
+    vmem_wait_all();
+    __syncthreads();
+    if (++it >= ntiles) break;
+    take_mask();
+    if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 0);
+    compute(kt_hi - it, 1);
+    vmem_wait_all();
+    __syncthreads();
+    if (++it >= ntiles) break;
+  }
+  if (!wave_active || !qvalid) return;
+  store_cols<D>(a.dq + qrow, dqacc, a.scaling, g, false);
+}
+
+// ===========================================================================
+// D = 128 holds 2 x 64 accumulator registers, 2 x 32 for the K/V fragments
+// and the per-half scores: more than the 256 registers of two waves per SIMD,
+// so that instantiation runs one wave per SIMD (accumulators in AGPRs).
+template <int D, bool PAD>
+__global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+  using T = Tile<D>;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int DMA_PER_WAVE = T::TILE_BYTES / 1024 / NW;
+  constexpr int RB = T::ROW_BYTES;
+  __shared__ __attribute__((aligned(16))) char lds_q0[T::TILE_BYTES], lds_o0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_q1[T::TILE_BYTES], lds_o1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float lds_l0[BN], lds_d0[BN], lds_l1[BN], lds_d1[BN];
+  auto qbuf = [&](int buf) __attribute__((always_inline)) { return (lds_char *)(buf ? lds_q1 : lds_q0); };
+  auto obuf = [&](int buf) __attribute__((always_inline)) { return (lds_char *)(buf ? lds_o1 : lds_o0); };
+  auto lbuf = [&](int buf) __attribute__((always_inline)) {
+    return (__attribute__((address_space(3))) float *)(buf ? lds_l1 : lds_l0);
+  };
+  auto dbuf = [&](int buf) __attribute__((always_inline)) {
+    return (__attribute__((address_space(3))) float *)(buf ? lds_d1 : lds_d0);
+  };
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+
+  // work item: segment-major, key blocks ascending (the most queries first),
+  // then kv head -- consecutive workgroups take consecutive kv heads, so each
+  // XCD keeps one head group's Q/dO rows in its L2.
+  const int per_seg = a.k_blocks * a.hkv;
+  const int b = blockIdx.x;
+  const int seg = b / per_seg;
+  const int rest = b % per_seg;
+  const int kb = rest / a.hkv;
+  const int kvh = rest % a.hkv;
+  int s0, L;
+  segment_bounds(a.lay, seg, s0, L);
+  const int kb0 = kb * COLS;
+  if (kb0 >= L) return;
+  const int kw0 = kb0 + wave * 32;
+  const int kw1 = min(kw0 + 31, L - 1);
+  const bool wave_active = kw0 < L;
+  const int key = kw0 + n;
+  const bool kin = key < L;
+  const int64_t krow = ((int64_t)(s0 + (kin ? key : 0)) * a.hkv + kvh) * D;
+
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    kf[ks] = __builtin_bit_cast(bf16x8, kin ? *reinterpret_cast<const uint4 *>(a.k + krow + ks * 16 + g * 8) : z);
+    vf[ks] = __builtin_bit_cast(bf16x8, kin ? *reinterpret_cast<const uint4 *>(a.v + krow + ks * 16 + g * 8) : z);
+  }
+  bool kpad = false;
+  if constexpr (PAD) kpad = kin && a.key_valid[s0 + key] == 0;
+
+  const int W = a.window;
+  const bool bidir = a.bidirectional != 0;
+  const float c2 = a.scale_log2;
+  // queries that can see a key of this block
+  const int qlo = bidir ? 0 : kb0;
+  const int qhi = bidir || W <= 0 ? L - 1 : min(L - 1, min(kb0 + COLS - 1, L - 1) + W - 1);
+  const int qt_lo = qlo / BN;
+  const int nqt = qhi / BN - qt_lo + 1;
+  const int ntiles = nqt * a.group;
+
+  const int64_t q_stride = (int64_t)a.hq * D;
+  int off[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int slot = (wave * DMA_PER_WAVE + i) * 64 + lane;
+    const int row = slot / T::CHUNKS;
+    const int pch = slot % T::CHUNKS;
+    off[i] = (row * (int)q_stride + (pch ^ T::swz_kv(row)) * 8) * 2;
+  }
+  TileAddr<D> ad;
+  ad.init(lane);
+
+  auto issue_dma = [&](int it, int buf) {
+    const int h = kvh * a.group + it / nqt;
+    const int t0 = (qt_lo + it % nqt) * BN;
+    const int rows = min(L - t0, BN);
+    const int64_t r0 = (int64_t)(s0 + t0) * a.hq + h;
+    const int valid_bytes = ((rows - 1) * (int)q_stride + D) * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + r0 * D, valid_bytes);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(a.d_o + r0 * D, valid_bytes);
+    lds_char *qdst = qbuf(buf) + wave * DMA_PER_WAVE * 1024;
+    lds_char *odst = obuf(buf) + wave * DMA_PER_WAVE * 1024;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      dma16(qr, off[i], qdst + i * 1024);
+      dma16(orr, off[i], odst + i * 1024);
+    }
+    // the tile's LSE and delta rows (rows past the segment read as 0)
+    if (wave < 2) {
+      const int fbytes = ((rows - 1) * a.hq + 1) * 4;
+      const __amdgpu_buffer_rsrc_t fr = make_rsrc((wave ? a.delta : a.lse) + r0, fbytes);
+      dma4(fr, lane * a.hq * 4, (lds_char *)(wave ? dbuf(buf) : lbuf(buf)));
+    }
+  };
+
+  f32x16 dkacc[DT], dvacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
+
+  auto compute = [&](int it, int BUF) __attribute__((always_inline)) {
+    const int t0 = (qt_lo + it % nqt) * BN;
+    const bool none_visible = !wave_active || (!bidir && (t0 + BN - 1 < kw0 || (W > 0 && t0 > kw1 + W - 1)));
+    if (none_visible) return;
+    const bool all_visible = t0 + BN <= L && (bidir || (t0 >= kw1 && (W <= 0 || t0 + BN - 1 <= kw0 + W - 1)));
+    const lds_char *Qt = qbuf(BUF);
+    const lds_char *Ot = obuf(BUF);
+    const __attribute__((address_space(3))) float *Lt = lbuf(BUF);
+    const __attribute__((address_space(3))) float *Dl = dbuf(BUF);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const f32x16 s = rows_times<D>(Qt, ad, half * 32 * RB, kf);
+      const f32x16 dp = rows_times<D>(Ot, ad, half * 32 * RB, vf);
+      float p[16], ds[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(Lt + half * 32 + 8 * j + 4 * g);
+        const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(Dl + half * 32 + 8 * j + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * j + e;
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -(l4[e] * kLog2e)));
+          if (!all_visible) {
+            const int qp = t0 + half * 32 + 8 * j + 4 * g + e;
+            const bool vis = qp < L && (bidir || (key <= qp && (W <= 0 || key > qp - W)));
+            p[i] = vis ? p[i] : 0.0f;
+          }
+          ds[i] = p[i] * (dp[i] - d4[e]);
+        }
+      }
+      bf16x8 p0, p1, d0, d1;
+      pack16(p, p0, p1);
+      pack16(ds, d0, d1);
+      tr_times<D>(Ot, ad, half * 32, p0, p1, dvacc);
+      tr_times<D>(Qt, ad, half * 32, d0, d1, dkacc);
+    }
+  };
+
+  issue_dma(0, 0);
+  vmem_wait_all();
+  __syncthreads();
+  for (int it = 0;;) {
+    if (it + 1 < ntiles) issue_dma(it + 1, 1);
+    compute(it, 0);
+    vmem_wait_all();
+    __syncthreads();
+    if (++it >= ntiles) break;
+    if (it + 1 < ntiles) issue_dma(it + 1, 0);
+    compute(it, 1);
+    vmem_wait_all();
+    __syncthreads();
+    if (++it >= ntiles) break;
+  }
+  if (!kin) return;
+  // a padded key is seen by no query: its gradients are zero
+  store_cols<D>(a.dk + krow, dkacc, a.scaling, g, kpad);
+  store_cols<D>(a.dv + krow, dvacc, 1.0f, g, kpad);
+}
+
+template <int D, bool PAD>
+hipError_t launch_d(const AttnBwdArgs &a, hipStream_t stream) {
+  const int64_t nseg = a.lay.num_segments;
+  const int64_t dq_blocks = (int64_t)a.q_blocks * nseg * a.hkv * a.head_chunks;
+  const int64_t kv_blocks = (int64_t)a.k_blocks * nseg * a.hkv;
+  if (dq_blocks > 0)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, PAD>), dim3((unsigned)dq_blocks), dim3(64 * NW), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (kv_blocks > 0)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, PAD>), dim3((unsigned)kv_blocks), dim3(64 * NW), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int attn_bwd_keys_per_workgroup() { return COLS; }
+
+hipError_t launch_attn_bwd(int head_dim, const AttnBwdArgs &a, hipStream_t stream) {
+  if (a.heads_per_wg < 1 || a.heads_per_wg > COLS || a.tok_per_wg < 1 || a.tok_per_wg * a.heads_per_wg > COLS)
+    return hipErrorInvalidConfiguration;
+  const bool pad = a.key_valid != nullptr;
+  if (head_dim == 128) return pad ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);
+  return pad ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);
+}
+
+}  // namespace muse

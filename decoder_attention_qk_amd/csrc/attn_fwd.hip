@@ -45,7 +45,7 @@
 // the zero row.
 #include <cmath>
 
-#include "device_common.hpp"
+#include "attn_common.hpp"
 #include "kernels.hpp"
 
 namespace muse {
@@ -56,55 +56,14 @@ constexpr int BN = 64;        // keys per tile
 constexpr int NW = 4;         // waves per workgroup
 constexpr int COLS = 32 * NW; // query columns per workgroup
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-template <int D>
-struct Tile {
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int CHUNKS = D / 8;                    // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BN * ROW_BYTES;       // one K or V tile
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;      // K + V
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;       // double buffered
-  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / NW;
-  static constexpr int ROWS_PER_256B = 256 / ROW_BYTES;
-  // K rows are read 16 rows x one chunk per 16-lane group: spread 16 rows over 16 slots.
-  static __device__ __forceinline__ int swz_k(int row) { return (row / ROWS_PER_256B) % CHUNKS; }
-  // V is read 4 rows x 32 columns per half-wave: give each row its own quarter
-  // of the 256-byte bank window (XOR on 4-chunk groups).
-  static __device__ __forceinline__ int swz_v(int row) {
-    return 4 * ((row / ROWS_PER_256B) & (CHUNKS / 4 - 1));
-  }
-};
-
-// Buffer resource over [base, base + bytes): loads past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
-}
-
-// 16 bytes per lane at byte offset voff of the buffer, straight into LDS at
-// dst + 16 * lane (dst must be the same for the whole wave).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, lds_char *dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 0);
-}
-
-// x of the lower-half lane and of the upper-half lane of this lane's pair
-// (l, l ^ 32), by one VALU lane swap (no LDS round trip).
-__device__ __forceinline__ void swap32(float x, float &lo, float &hi) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  lo = __uint_as_float(r[0]);
-  hi = __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ void vmem_wait_all() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
-}
+static_assert(BN == 64, "Tile<D> holds 64-row tiles");
 
 // PAD: keys may be padding (a.key_valid given); a separate instantiation so
 // the unpadded kernel carries none of its registers.
 template <int D, bool FUSED, bool PAD>
 __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   using T = Tile<D>;
+  constexpr int DMA_PER_WAVE = T::TILE_BYTES / 1024 / NW;   // KiB of one tile per wave
   constexpr int KS = D / 16;   // QK^T k-steps
   constexpr int DT = D / 32;   // O^T row tiles
   constexpr int KK = BN / 16;  // PV k-steps
@@ -261,10 +220,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   const int64_t kv_stride = (int64_t)a.hkv * D;
   const uint16_t *kbase = a.k + ((int64_t)s0 * a.hkv + kvh) * D;
   const uint16_t *vbase = a.v + ((int64_t)s0 * a.hkv + kvh) * D;
-  int off_k[T::DMA_PER_WAVE], off_v[T::DMA_PER_WAVE];   // byte offsets inside a tile's rows
+  int off_k[DMA_PER_WAVE], off_v[DMA_PER_WAVE];   // byte offsets inside a tile's rows
 #pragma unroll
-  for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
-    const int slot = (wave * T::DMA_PER_WAVE + i) * 64 + lane;
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int slot = (wave * DMA_PER_WAVE + i) * 64 + lane;
     const int row = slot / T::CHUNKS;
     const int pch = slot % T::CHUNKS;
     off_k[i] = (row * (int)kv_stride + (pch ^ T::swz_k(row)) * 8) * 2;
@@ -299,15 +258,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   auto issue_dma = [&](int kt, int buf) {
     const int k0 = kt * BN;
     if constexpr (PAD) vbyte = k0 + lane < L ? (int)kvalid[k0 + lane] : 0;
-    lds_char *kdst = kbuf(buf) + wave * T::DMA_PER_WAVE * 1024;
-    lds_char *vdst = vbuf(buf) + wave * T::DMA_PER_WAVE * 1024;
+    lds_char *kdst = kbuf(buf) + wave * DMA_PER_WAVE * 1024;
+    lds_char *vdst = vbuf(buf) + wave * DMA_PER_WAVE * 1024;
     // the tile's rows k0 .. L-1 of this kv head; rows past the segment read as zeros
     // (zero keys are masked out of every score, zero values add nothing)
     const int valid_bytes = ((min(L - k0, BN) - 1) * (int)kv_stride + D) * 2;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)k0 * kv_stride, valid_bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)k0 * kv_stride, valid_bytes);
 #pragma unroll
-    for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
       dma16(kr, off_k[i], kdst + i * 1024);
       dma16(vr, off_v[i], vdst + i * 1024);
     }

@@ -64,6 +64,40 @@ struct OutGateArgs {
   float eps;
 };
 
+// Backward of the output norm + gate: d_o, dgate and delta = rowsum(d_o * o);
+// with gate == nullptr only delta = rowsum(dout * o) is formed (dout is d_o).
+struct OutGateBwdArgs {
+  const uint16_t *o;       // [N, Hq, D]
+  const uint16_t *gate;    // [N, Hq, D] or nullptr (delta only)
+  const uint16_t *dout;    // [N, Hq, D]
+  uint16_t *d_o;           // [N, Hq, D] (unused in delta-only mode)
+  uint16_t *dgate;         // [N, Hq, D] (unused in delta-only mode)
+  float *delta;            // [N, Hq]
+  int64_t rows;            // N * Hq
+  float eps;
+};
+
+// Backward of the Q/K norm + query scale + RoPE.  Blocks [0, q_blocks) take
+// Q rows, the rest K rows; each block walks its rows with a fixed stride and
+// writes one partial gain gradient per column (part[block][D]), summed in a
+// fixed order by the reduce kernel.
+struct QkNormBwdArgs {
+  const uint16_t *q, *k;            // raw inputs (re-normalised here)
+  const uint16_t *dq_hat, *dk_hat;  // gradients of the rotated outputs
+  uint16_t *dq, *dk;
+  const float *q_gain, *k_gain;     // nullptr: no gain
+  float *q_part, *k_part;           // [blocks, D] partial gain gradients (nullptr: no gain)
+  float *dq_gain, *dk_gain;         // [D] gain gradients (with their partial buffers)
+  const float *cos_tab, *sin_tab;
+  int32_t n_pos;
+  FastDiv hq_div, hkv_div;
+  int32_t q_rows, k_rows;
+  int32_t q_blocks, k_blocks;       // set by the launcher
+  float eps, gain_center, query_scale;
+  int32_t use_rope, skip_norm;
+  TokenLayout lay;
+};
+
 struct AttnArgs {
   const uint16_t *q;       // fused: raw Q; otherwise normalised, rotated Q
   const uint16_t *k;       // normalised, rotated K [N, Hkv, D]
@@ -94,10 +128,34 @@ struct AttnArgs {
   TokenLayout lay;
 };
 
+// Attention backward (dQ kernel and dK/dV kernel).
+struct AttnBwdArgs {
+  const uint16_t *q, *k, *v;   // q_hat [N, Hq, D]; k_hat, v [N, Hkv, D]
+  const uint16_t *d_o;         // [N, Hq, D]
+  const float *lse;            // [N, Hq] natural-log LSE of the forward
+  const float *delta;          // [N, Hq] rowsum(d_o * o)
+  uint16_t *dq;                // [N, Hq, D] gradient of q_hat
+  uint16_t *dk, *dv;           // [N, Hkv, D]
+  float scaling, scale_log2;
+  int32_t hq, hkv, group;
+  int32_t heads_per_wg, head_chunks, tok_per_wg;   // dQ kernel work shape (as the forward)
+  int32_t window, bidirectional;
+  const uint8_t *key_valid;    // BSHD token validity or nullptr
+  int32_t q_blocks;            // dQ kernel: query blocks per segment
+  int32_t k_blocks;            // dK/dV kernel: 128-key blocks per segment
+  TokenLayout lay;
+};
+
 hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t stream);
 hipError_t launch_qk_norm_rope(int head_dim, const QkNormArgs &a, hipStream_t stream);
 hipError_t launch_out_norm_gate(int head_dim, const OutGateArgs &a, hipStream_t stream);
 hipError_t launch_attn_fwd(int head_dim, bool fused, const AttnArgs &a, hipStream_t stream);
+hipError_t launch_out_norm_gate_bwd(int head_dim, const OutGateBwdArgs &a, hipStream_t stream);
+// blocks the Q/K backward uses for q_rows / k_rows rows (the partial buffers' first dimension)
+void qk_norm_bwd_blocks(int head_dim, int64_t q_rows, int64_t k_rows, int32_t *q_blocks, int32_t *k_blocks);
+hipError_t launch_qk_norm_rope_bwd(int head_dim, const QkNormBwdArgs &a, hipStream_t stream);
+hipError_t launch_attn_bwd(int head_dim, const AttnBwdArgs &a, hipStream_t stream);
+int attn_bwd_keys_per_workgroup();
 int attn_columns_per_workgroup();  // (token, head) query columns one attention workgroup holds
 
 // Position of token t for RoPE (clamped into the table), and its segment.

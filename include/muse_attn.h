@@ -12,8 +12,11 @@
  * Definitions come from the NeMo AutoModel API reference pages of the
  * muse_spark package: the "layers" page (MuseSparkAttention, MuseSparkRMSNorm,
  * MuseSparkRotaryEmbedding, _rms_norm_core, _qk_norm_rope_core,
- * apply_rotary_embedding, _repeat_kv, _output_norm_gate_core) and the "model"
- * page (_causal_mask, _validate_thd_documents).
+ * apply_rotary_embedding, _repeat_kv, _output_norm_gate_core), the "model"
+ * page (_causal_mask, _validate_thd_documents, MuseSparkTextModel.forward) and
+ * the "vision" page (MuseSparkVisionAttention, _apply_vision_rope,
+ * _rope_frequencies).  The backward entry points are the chain rule through
+ * the same stages (the pages train the module with autograd).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -44,6 +47,7 @@
 #ifndef MUSE_ATTN_H
 #define MUSE_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -284,6 +288,102 @@ muse_status muse_attn_fused_fwd(const muse_attn_params *params, const muse_layou
                                 const void *q, const void *k_hat, const void *v, const void *gate,
                                 const float *q_gain, const float *cos, const float *sin,
                                 int32_t n_pos, void *out, float *lse, void *stream);
+
+/*
+ * ---------------------------------------------------------------- backward
+ *
+ * The gradients of the forward stages above, each following autograd's
+ * dtypes: a gradient of a bf16 tensor is bf16, gain gradients are fp32.
+ * The rotation's backward is built for the FP32 rotation only
+ * (upcast_rope = 0 with use_rope returns UNSUPPORTED).  Entry points that
+ * need scratch memory take a caller-owned workspace (16-byte aligned, at
+ * least the size the matching *_workspace_size call reports); its contents
+ * are overwritten, and calls that share a workspace must not overlap in time.
+ * Results are deterministic: no atomics, fixed reduction orders.
+ */
+
+/*
+ * Backward of the output norm + gate (layers page, _output_norm_gate_core).
+ * With y = o r, r = 1 / sqrt(mean(o^2) + out_eps), s = sigmoid(gate):
+ *   dgate = bf16(dout y s (1 - s)),  d_o = bf16(r dout s - r^3 o mean(dout s o)),
+ *   delta = sum_d d_o * o  (fp32, the softmax correction of muse_gqa_attn_bwd).
+ * o, gate, dout [N, Hq, D] bf16 in; d_o, dgate [N, Hq, D] bf16 out; delta fp32 [N, Hq] out.
+ * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}), DEVICE.
+ */
+muse_status muse_out_norm_gate_bwd(const muse_attn_params *params, const muse_layout *layout,
+                                   const void *o, const void *gate, const void *dout, void *d_o,
+                                   void *dgate, float *delta, void *stream);
+
+/*
+ * delta = sum_d d_o * o (fp32 [N, Hq]) for an attention backward without the
+ * output gate (o, d_o [N, Hq, D] bf16).
+ */
+muse_status muse_attn_bwd_delta(const muse_attn_params *params, const muse_layout *layout,
+                                const void *o, const void *d_o, float *delta, void *stream);
+
+/*
+ * Backward of muse_gqa_attn_fwd (same masking rules: causal/window,
+ * bidirectional, padded keys).  With P the softmax of the forward,
+ * recomputed as exp(scaling q_hat k_hat^T - lse):
+ *   dP = d_o v^T,  dS = P (dP - delta),
+ *   dq_hat = bf16(scaling dS k_hat),  dk_hat = bf16(scaling sum_heads dS^T q_hat),
+ *   dv = bf16(sum_heads P^T d_o)   (sums over the query heads of each KV head).
+ * q_hat [N, Hq, D], k_hat, v [N, Hkv, D], d_o [N, Hq, D] bf16 in; lse (natural
+ * log, from the forward) and delta fp32 [N, Hq] in; dq_hat [N, Hq, D], dk_hat,
+ * dv [N, Hkv, D] bf16 out.  A padded key gets zero gradients.
+ * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}), DEVICE.
+ */
+muse_status muse_gqa_attn_bwd(const muse_attn_params *params, const muse_layout *layout,
+                              const void *q_hat, const void *k_hat, const void *v, const void *d_o,
+                              const float *lse, const float *delta, void *dq_hat, void *dk_hat,
+                              void *dv, void *stream);
+
+/*
+ * Backward of muse_qk_norm_rope.  For each row: g = the FP32 inverse rotation
+ * of the incoming gradient, (g0 C + g1 S, -g0 S + g1 C), rounded to bf16;
+ * for Q, g = bf16(g * query_scale); then with x the raw input, r its rstd and
+ * w = gain_center + gain (1 without a gain), u = g w:
+ *   dx = bf16(r u - r^3 x mean(u x)),  dgain += g x r  (summed over all rows, fp32).
+ * skip_qk_norm: dx = g, no gain gradients.
+ * q, dq_hat, dq [N, Hq, D] (all three NULL: skip Q); k, dk_hat, dk [N, Hkv, D]
+ * (all NULL: skip K); q_gain, k_gain as in the forward; dq_gain, dk_gain fp32
+ * [D] out, given exactly when the matching gain is (for one gain shared by
+ * Q and K, its gradient is dq_gain + dk_gain); cos/sin as in the forward.
+ * workspace: muse_qk_norm_rope_bwd_workspace_size bytes (gain partial sums).
+ * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}, upcast_rope = 0), DEVICE.
+ */
+muse_status muse_qk_norm_rope_bwd(const muse_attn_params *params, const muse_layout *layout,
+                                  const void *q, const void *k, const float *q_gain,
+                                  const float *k_gain, const float *cos, const float *sin,
+                                  int32_t n_pos, const void *dq_hat, const void *dk_hat, void *dq,
+                                  void *dk, float *dq_gain, float *dk_gain, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+muse_status muse_qk_norm_rope_bwd_workspace_size(const muse_attn_params *params,
+                                                 const muse_layout *layout, size_t *bytes);
+
+/*
+ * Backward of the whole core (muse_attn_core_fwd): gradients of q, k, v, the
+ * gate logits and the two gains, from dout [N, Hq, D] bf16.
+ * o: the forward's attention output before the output norm ([N, Hq, D] bf16,
+ * as muse_gqa_attn_fwd writes it) and lse (fp32 [N, Hq]); both NULL: they are
+ * recomputed here (the fused forward keeps neither).  Steps: Q/K norm + RoPE
+ * forward into the workspace, muse_out_norm_gate_bwd, muse_gqa_attn_bwd,
+ * muse_qk_norm_rope_bwd.
+ * Outputs: dq [N, Hq, D], dk, dv [N, Hkv, D], dgate [N, Hq, D] bf16;
+ * dq_gain, dk_gain fp32 [D] (given exactly when the matching gain is).
+ * workspace: muse_attn_core_bwd_workspace_size bytes.
+ * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}, upcast_rope = 0 with
+ * use_rope, skip_qk_norm), DEVICE.
+ */
+muse_status muse_attn_core_bwd(const muse_attn_params *params, const muse_layout *layout,
+                               const void *q, const void *k, const void *v, const void *gate,
+                               const float *q_gain, const float *k_gain, const float *cos,
+                               const float *sin, int32_t n_pos, const void *o, const float *lse,
+                               const void *dout, void *dq, void *dk, void *dv, void *dgate,
+                               float *dq_gain, float *dk_gain, void *workspace,
+                               size_t workspace_bytes, void *stream);
+muse_status muse_attn_core_bwd_workspace_size(const muse_attn_params *params,
+                                              const muse_layout *layout, size_t *bytes);
 
 /*
  * Pure host check of a packed layout (model page, _validate_thd_documents):

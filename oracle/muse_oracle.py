@@ -475,8 +475,10 @@ def _q_rows(q_sel, eps, q_gain, gain_center, query_scale, use_rope, cos, sin, up
 # gradient has its primal's dtype: with rnd=True every gradient of a bf16
 # tensor is rounded to bf16 where autograd would hold it (dO, dq_hat, dk_hat,
 # dv, the gradient after the rotation and after the query scale, dq, dk,
-# dgate); gain gradients stay in full precision.  rnd=False gives the exact
-# derivative of the unrounded forward (pinned against torch autograd).
+# dgate); gain gradients stay in full precision; the softmax correction
+# delta is formed from the stored bf16 attention output, as the fused
+# SDPA/TE backward kernels do.  rnd=False gives the exact derivative of the
+# unrounded forward (pinned against torch autograd).
 # --------------------------------------------------------------------------
 
 def _maybe_bf16(x, rnd):
@@ -503,13 +505,23 @@ def out_norm_gate_bwd(o, gate, dout, eps, rnd=True):
 
 
 def attention_bwd(q_hat, k_hat, v, d_o, segments: Segments, *, window=0, scaling, causal=True,
-                  key_valid=None, rnd=True):
+                  key_valid=None, rnd=True, o=None, mags=False, d_o_abs=None):
     """Gradients of o = softmax(scaling q k^T, masked) v per segment and head.
 
     With P the softmax, dP = dO v^T, delta_i = sum_j P_ij dP_ij and
     dS = P (dP - delta): dq = scaling dS k, dk = scaling dS^T q, dv = P^T dO;
     a key/value head sums the contributions of its query heads.  Returns
     (dq_hat [N,Hq,D], dk_hat [N,Hkv,D], dv [N,Hkv,D]).
+
+    ``o`` given: delta_i = sum_d dO_id o_id from that attention output, as the
+    fused SDPA / Transformer Engine backward kernels the pages run form it
+    from the stored (bf16) output; sum_j P_ij dP_ij equals it for the exact o.
+
+    mags=True also returns the same sums taken over magnitudes (the scale of
+    the rounding error of each result, for tolerances): with
+    |dS| <= P (|dO| |v|^T + |delta|), dq_abs = scaling |dS| |k|,
+    dk_abs = scaling |dS|^T |q|, dv_abs = P^T |dO|; ``d_o_abs`` replaces |dO|
+    by a magnitude bound of an upstream result.
     """
     q_hat = np.asarray(q_hat, dtype=np.float64)
     k_hat = np.asarray(k_hat, dtype=np.float64)
@@ -521,6 +533,9 @@ def attention_bwd(q_hat, k_hat, v, d_o, segments: Segments, *, window=0, scaling
     dq = np.zeros_like(q_hat)
     dk = np.zeros_like(k_hat)
     dv = np.zeros_like(v)
+    if mags:
+        dqa, dka, dva = np.zeros_like(q_hat), np.zeros_like(k_hat), np.zeros_like(v)
+        doa_all = np.abs(d_o) if d_o_abs is None else np.asarray(d_o_abs, dtype=np.float64)
     for s0, length in zip(segments.starts, segments.lengths):
         if length == 0:
             continue
@@ -537,12 +552,27 @@ def attention_bwd(q_hat, k_hat, v, d_o, segments: Segments, *, window=0, scaling
             z = e.sum(axis=1, keepdims=True)
             p = e / np.where(z > 0, z, 1.0)
             dp = dos @ vs.T
-            delta = np.sum(p * dp, axis=1, keepdims=True)
+            if o is None:
+                delta = np.sum(p * dp, axis=1, keepdims=True)
+            else:
+                delta = np.sum(dos * np.asarray(o, dtype=np.float64)[s0:s0 + length, h], axis=1,
+                               keepdims=True)
             ds = p * (dp - delta)
             dq[s0:s0 + length, h] = float(scaling) * (ds @ ks)
             dk[s0:s0 + length, g] += float(scaling) * (ds.T @ qs)
             dv[s0:s0 + length, g] += p.T @ dos
-    return _maybe_bf16(dq, rnd), _maybe_bf16(dk, rnd), _maybe_bf16(dv, rnd)
+            if mags:
+                doa = doa_all[s0:s0 + length, h]
+                oa = np.abs(dp) if o is None else np.abs(np.asarray(o, dtype=np.float64)[s0:s0 + length, h])
+                da = (doa @ np.abs(vs).T)
+                dla = (np.sum(p * da, axis=1, keepdims=True) if o is None
+                       else np.sum(doa * oa, axis=1, keepdims=True))
+                dsa = p * (da + dla)
+                dqa[s0:s0 + length, h] = float(scaling) * (dsa @ np.abs(ks))
+                dka[s0:s0 + length, g] += float(scaling) * (dsa.T @ np.abs(qs))
+                dva[s0:s0 + length, g] += p.T @ doa
+    out = (_maybe_bf16(dq, rnd), _maybe_bf16(dk, rnd), _maybe_bf16(dv, rnd))
+    return out + (dqa, dka, dva) if mags else out
 
 
 def rope_rotate_bwd(dy, cos, sin):
@@ -623,7 +653,7 @@ def attn_core_bwd(q, k, v, gate, dout, segments: Segments, *, theta, eps, out_ep
                                               key_valid=key_valid)
     d_o, dgate = out_norm_gate_bwd(o, gate, dout, out_eps, rnd)
     dq_hat, dk_hat, dv = attention_bwd(q_hat, k_hat, v, d_o, segments, window=window, scaling=scaling,
-                                       causal=causal, key_valid=key_valid, rnd=rnd)
+                                       causal=causal, key_valid=key_valid, rnd=rnd, o=o if rnd else None)
     dq, dk, dqg, dkg = qk_norm_rope_bwd(q, k, dq_hat, dk_hat, eps=eps, q_gain=q_gain, k_gain=k_gain,
                                         gain_center=gain_center, query_scale=query_scale,
                                         use_rope=use_rope, cos=cos, sin=sin, rnd=rnd)

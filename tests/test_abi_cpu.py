@@ -192,3 +192,38 @@ def test_attention_mask_rules():
     lay = m.c_layout(1, 16, None, 1, 0, 0, None, FAKE + (3 << 24) + 3)   # inside o, odd address is fine
     assert _attn(_params(), lay) == 1
     assert "overlaps" in m.library().muse_last_error().decode()
+
+
+def test_backward_argument_rules():
+    lib = m.library()
+    p, lay = _params(), _bshd(1, 16)
+    size = ctypes.c_size_t(0)
+    assert lib.muse_attn_core_bwd_workspace_size(ctypes.byref(p), ctypes.byref(lay), ctypes.byref(size)) == 0
+    # q_hat, k_hat, o, lse, d_o, delta, dq_hat, dk_hat and the gain partials
+    assert size.value >= 16 * 8 * 128 * 2 * 4 + 16 * 2 * 128 * 2 * 2
+    need = size.value
+    assert lib.muse_qk_norm_rope_bwd_workspace_size(ctypes.byref(p), ctypes.byref(lay), ctypes.byref(size)) == 0
+    assert 0 < size.value < need
+
+    A = [FAKE + (i << 24) for i in range(24)]
+
+    def core(pp=p, o=None, lse=None, qg=None, dqg=None, ws=A[20], wsb=need):
+        return lib.muse_attn_core_bwd(ctypes.byref(pp), ctypes.byref(lay), A[0], A[1], A[2], A[3], qg, None,
+                                      A[4], A[5], 16, o, lse, A[6], A[7], A[8], A[9], A[10], dqg, None, ws,
+                                      wsb, None)
+    assert core(o=A[11]) == 1                              # o without lse
+    assert core(qg=A[12]) == 1                             # a gain without its gradient
+    assert core(ws=None) == 1                              # no workspace
+    assert core(wsb=need - 1) == 1                         # too small
+    assert "workspace" in lib.muse_last_error().decode()
+    assert core(ws=A[20] + 8) == 1                         # misaligned workspace
+    assert core(pp=_params(upcast_rope=0)) == 2            # no backward for the Q/K-dtype rotation
+    assert core(pp=_params(skip_qk_norm=1)) == 2
+    # the attention backward needs every tensor
+    st = lib.muse_gqa_attn_bwd(ctypes.byref(p), ctypes.byref(lay), A[0], A[1], A[2], A[3], A[4], None,
+                               A[6], A[7], A[8], None)
+    assert st == 1
+    # and the Q/K backward takes a tensor's three buffers together
+    st = lib.muse_qk_norm_rope_bwd(ctypes.byref(p), ctypes.byref(lay), A[0], None, None, None, A[4], A[5], 16,
+                                   None, None, A[7], None, None, None, None, 0, None)
+    assert st == 1

@@ -243,3 +243,30 @@ def test_rounded_backward_sits_near_the_exact_one():
     for name in ("dq_gain", "dk_gain"):
         err = np.abs(a[name] - b[name]).max() / np.abs(b[name]).max()
         assert err < 0.05, (name, err)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_delta_from_the_exact_output_is_the_softmax_correction(case):
+    # sum_j P_ij dP_ij = sum_d dO_id O_id when O = P V exactly: forming delta
+    # from the attention output changes nothing but its rounding
+    x, segs, _, _ = _inputs(case, 47)
+    q_hat = _bf16(np.random.default_rng(3).standard_normal(x["q"].shape))
+    k_hat = _bf16(np.random.default_rng(4).standard_normal(x["k"].shape))
+    kw = dict(window=case["window"], scaling=0.35, causal=case["causal"], key_valid=case["valid"], rnd=False)
+    o_exact = np.zeros_like(q_hat)
+    groups = case["hq"] // case["hkv"]
+    for s0, length in case["bounds"]:
+        kok = None if case["valid"] is None else case["valid"][s0:s0 + length]
+        for h in range(case["hq"]):
+            ob, _ = O.muse_oracle._attend_block(q_hat[s0:s0 + length, h], k_hat[s0:s0 + length, h // groups],
+                                                x["v"][s0:s0 + length, h // groups], np.arange(length),
+                                                case["window"], 0.35, case["causal"], kok)
+            o_exact[s0:s0 + length, h] = ob
+    a = O.attention_bwd(q_hat, k_hat, x["v"], x["dout"], segs, **kw)
+    b = O.attention_bwd(q_hat, k_hat, x["v"], x["dout"], segs, o=o_exact, **kw)
+    for u, w_ in zip(a, b):
+        np.testing.assert_allclose(u, w_, rtol=1e-10, atol=1e-12)
+    # with the bf16 output only delta moves, by dO . (bf16(O) - O)
+    c = O.attention_bwd(q_hat, k_hat, x["v"], x["dout"], segs, o=_bf16(o_exact), **kw)
+    np.testing.assert_allclose(c[2], a[2], rtol=1e-12, atol=1e-12)      # dv does not use delta
+    assert np.abs(c[0] - a[0]).max() > 0.0
