@@ -4,7 +4,9 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 the FP32 RoPE table, then for each layer of the workload the key norm/RoPE
 pass and the fused attention kernel (query norm/RoPE prologue, causal GQA
 flash attention, output norm x sigmoid gate epilogue).  Inputs are resident in
-HBM before the timed region.  Prints one JSON line.
+HBM before the timed region.  Prints one JSON line.  Besides the step it
+reports the unfused stages (flushed caches) and the backward entry points of
+layer 0 (--no-stages, --no-backward skip them).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -12,6 +14,7 @@ HBM before the timed region.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -56,6 +59,7 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage (unfused) measurements")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (reference kernel for HBM counters)")
     return ap.parse_args()
@@ -196,6 +200,70 @@ def measure_stages(b: Bench, iters: int = 5) -> dict:
     return res
 
 
+def measure_backward(b: Bench, warmup: int = 20, iters: int = 50) -> dict:
+    """The backward of layer 0 (warm clocks, back-to-back launches, events
+    around each entry point): output norm/gate backward, attention backward
+    (dQ kernel + dK/dV kernel), Q/K norm/RoPE backward, and the whole
+    muse_attn_core_bwd with the forward's O and LSE given.  Attention FLOP
+    are algorithmic: five products of 2 D flop per visible (query, key, head)
+    -- 2.5x the forward's -- although the kernels recompute S and dP once more."""
+    torch, m, w = b.torch, b.m, b.w
+    t = b.layers[0]
+    p, lay = t["params"], b.layout
+    cos, sin = (b.cos, b.sin) if p.use_rope else (None, None)
+    m.muse_rope_cos_sin(w.theta, w.head_dim, b.n_pos, b.cos, b.sin)
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(p, lay, t["q"], t["k"], t["q_gain"], t["k_gain"], cos, sin)
+    o, lse = m.muse_gqa_attn_fwd(p, lay, q_hat, k_hat, t["v"], want_lse=True)
+    g = torch.Generator(device=b.dev)
+    g.manual_seed(7)
+    dout = torch.randn(t["q"].shape, generator=g, device=b.dev).to(torch.bfloat16)
+    d_o, dgate, delta = m.muse_out_norm_gate_bwd(p, lay, o, t["gate"], dout)
+    dq_hat, dk_hat, dv = m.muse_gqa_attn_bwd(p, lay, q_hat, k_hat, t["v"], d_o, lse, delta)
+    dq, dk, dqg, dkg = m.muse_qk_norm_rope_bwd(p, lay, t["q"], t["k"], t["q_gain"], t["k_gain"], cos, sin,
+                                               dq_hat, dk_hat)
+    res_core = m.muse_attn_core_bwd(p, lay, t["q"], t["k"], t["v"], t["gate"], dout, t["q_gain"], t["k_gain"],
+                                    cos, sin, o=o, lse=lse)
+    size = ctypes.c_size_t(0)
+    pc, lc = p.to_c(), lay.to_c()
+    m.library().muse_attn_core_bwd_workspace_size(ctypes.byref(pc), ctypes.byref(lc), ctypes.byref(size))
+    ws = torch.empty(size.value, dtype=torch.uint8, device=b.dev)
+    calls = [
+        lambda: m.muse_out_norm_gate_bwd(p, lay, o, t["gate"], dout, d_o=d_o, dgate=dgate, delta=delta),
+        lambda: m.muse_gqa_attn_bwd(p, lay, q_hat, k_hat, t["v"], d_o, lse, delta, dq_hat=dq_hat,
+                                    dk_hat=dk_hat, dv=dv),
+        lambda: m.muse_qk_norm_rope_bwd(p, lay, t["q"], t["k"], t["q_gain"], t["k_gain"], cos, sin, dq_hat,
+                                        dk_hat, dq=dq, dk=dk, dq_gain=dqg, dk_gain=dkg),
+        lambda: m.muse_attn_core_bwd(p, lay, t["q"], t["k"], t["v"], t["gate"], dout, t["q_gain"],
+                                     t["k_gain"], cos, sin, o=o, lse=lse, dq=res_core[0], dk=res_core[1],
+                                     dv=res_core[2], dgate=res_core[3], dq_gain=res_core[4],
+                                     dk_gain=res_core[5], workspace=ws),
+    ]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(iters)]
+    for i in range(iters):
+        evs[i][0].record()
+        for j, c in enumerate(calls):
+            c()
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    us = [float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(iters)])) * 1e3
+          for j in range(len(calls))]
+    qb, kb = t["q"].numel() * 2, t["k"].numel() * 2
+    flop = 2.5 * layer_flop(w, t["window"])
+    return {
+        "out_norm_gate_bwd": {"us": round(us[0], 2), "GBps": round(5 * qb / us[0] / 1e3, 1),
+                              "frac_hbm": round(5 * qb / us[0] / 1e3 / PEAK_HBM_GBPS, 4)},
+        "gqa_attn_bwd": {"us": round(us[1], 2), "TFLOPs": round(flop / us[1] / 1e6, 2),
+                         "frac_mfma": round(flop / us[1] / 1e6 / PEAK_BF16_TFLOPS, 4),
+                         "flop_algorithmic": int(flop)},
+        "qk_norm_rope_bwd": {"us": round(us[2], 2), "GBps": round(3 * (qb + kb) / us[2] / 1e3, 1),
+                             "frac_hbm": round(3 * (qb + kb) / us[2] / 1e3 / PEAK_HBM_GBPS, 4)},
+        "attn_core_bwd": {"us": round(us[3], 2), "TFLOPs": round(flop / us[3] / 1e6, 2)},
+    }
+
+
 def cpu_baseline(w: W.Workload, budget_s: float = 12.0) -> dict:
     """The FP64 oracle, as it stands, on whole (sequence, KV group) units of
     the same workload until about `budget_s` seconds of CPU work are done."""
@@ -314,6 +382,8 @@ def main():
     }
     if not args.no_stages:
         line["stages_flushed"] = measure_stages(b)
+    if not args.no_backward:
+        line["backward"] = measure_backward(b)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

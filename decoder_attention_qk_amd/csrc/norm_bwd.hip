@@ -193,13 +193,38 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_bwd_kernel(QkNormBwdArg
   }
 }
 
-// Column sums of the block partials, in block order.
-__global__ __launch_bounds__(256) void gain_reduce_kernel(const float *part, float *out, int blocks, int d) {
-  const int col = blockIdx.x * blockDim.x + threadIdx.x;
-  if (col >= d) return;
-  float s = 0.0f;
-  for (int b = 0; b < blocks; ++b) s += part[(int64_t)b * d + col];
-  out[col] = s;
+// Column sums of the block partials in a fixed order: a block of 1024
+// threads takes 32 columns; each of the 32 slices of a column sums the
+// partial rows slice, slice + 32, ... with 8 loads in flight (8 independent
+// accumulators added pairwise), and the 32 slice sums are added pairwise
+// through LDS.  Deterministic, and wide enough that a few thousand partial
+// rows cost a few microseconds.
+constexpr int kRedThreads = 1024;
+__global__ __launch_bounds__(kRedThreads) void gain_reduce_kernel(const float *part, float *out, int blocks,
+                                                                   int d) {
+  __shared__ float red[32][33];
+  const int cl = threadIdx.x & 31;
+  const int sl = threadIdx.x >> 5;          // slice 0..31
+  const int c = blockIdx.x * 32 + cl;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c < d) {
+    int b = sl;
+    for (; b + 7 * 32 < blocks; b += 8 * 32) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += part[(int64_t)(b + u * 32) * d + c];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (b + u * 32 < blocks) acc[u] += part[(int64_t)(b + u * 32) * d + c];
+  }
+  red[sl][cl] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  __syncthreads();
+#pragma unroll
+  for (int w = 16; w >= 1; w >>= 1) {
+    if (sl < w) red[sl][cl] = red[sl][cl] + red[sl + w][cl];
+    __syncthreads();
+  }
+  if (sl == 0 && c < d) out[c] = red[0][cl];
 }
 
 template <int D, bool ROPE, bool NORM>
@@ -259,12 +284,12 @@ hipError_t launch_qk_norm_rope_bwd(int head_dim, const QkNormBwdArgs &args, hipS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.skip_norm) return e;
   if (a.q_part && a.q_blocks > 0) {
-    hipLaunchKernelGGL(gain_reduce_kernel, dim3((head_dim + 255) / 256), dim3(256), 0, stream, a.q_part,
+    hipLaunchKernelGGL(gain_reduce_kernel, dim3((head_dim + 31) / 32), dim3(kRedThreads), 0, stream, a.q_part,
                        a.dq_gain, a.q_blocks, head_dim);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.k_part && a.k_blocks > 0) {
-    hipLaunchKernelGGL(gain_reduce_kernel, dim3((head_dim + 255) / 256), dim3(256), 0, stream, a.k_part,
+    hipLaunchKernelGGL(gain_reduce_kernel, dim3((head_dim + 31) / 32), dim3(kRedThreads), 0, stream, a.k_part,
                        a.dk_gain, a.k_blocks, head_dim);
     e = hipGetLastError();
   }
