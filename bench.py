@@ -66,13 +66,19 @@ def parse():
 
 
 def kernel_source_digest() -> str:
-    """Digest of the sources the fused attention kernel is built from."""
+    """Digest of the sources the fused attention kernel is built from: its
+    own file, the two device headers it includes, and its argument struct
+    (the rest of kernels.hpp declares other kernels)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decoder_attention_qk_amd", "csrc")
-    for name in ("attn_fwd.hip", "device_common.hpp", "kernels.hpp"):
+    for name in ("attn_fwd.hip", "attn_common.hpp", "device_common.hpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(csrc, "kernels.hpp")) as f:
+        text = f.read()
+    start = text.index("struct AttnArgs {")
+    h.update(text[start:text.index("};", start)].encode())
     return h.hexdigest()[:16]
 
 
