@@ -72,6 +72,8 @@ __all__ = [
     "rms_norm_bwd",
     "qk_norm_rope_bwd",
     "attn_core_bwd",
+    "attention_bwd_rows",
+    "attention_bwd_keys",
 ]
 
 
@@ -697,3 +699,77 @@ def _exact_forward(q, k, v, segments, *, eps, scaling, window, use_rope, cos, si
             o[s0:s0 + length, h] = ob
             lse[s0:s0 + length, h] = lb
     return q1, k1, o, lse
+
+
+def attention_bwd_rows(q_hat_rows, k_hat, v, d_o_rows, o_rows, segments: Segments, rows, *, num_heads,
+                       window=0, scaling, causal=True, key_valid=None):
+    """dq_hat of selected (token, head) rows, each from its own row of the
+    softmax: dq = scaling sum_j P_j (dP_j - delta) k_j with delta = dO . o
+    (o the stored output of that row).  Returns bf16 values [len(rows), D]."""
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    groups = num_heads // k_hat.shape[1]
+    dq = np.zeros((len(rows), k_hat.shape[2]))
+    for r, (t, h) in enumerate(rows):
+        s0, length = segments.locate(int(t))
+        g = int(h) // groups
+        ks, vs = k_hat[s0:s0 + length, g], v[s0:s0 + length, g]
+        kok = None if key_valid is None else np.asarray(key_valid)[s0:s0 + length]
+        vis = visible_mask(np.array([int(t) - s0]), np.arange(length), window, causal, kok)[0]
+        if not vis.any():
+            continue
+        sc = np.where(vis, float(scaling) * (ks @ np.asarray(q_hat_rows[r], dtype=np.float64)), -np.inf)
+        p = np.exp(sc - sc.max())
+        p /= p.sum()
+        dor = np.asarray(d_o_rows[r], dtype=np.float64)
+        dp = vs @ dor
+        delta = float(dor @ np.asarray(o_rows[r], dtype=np.float64))
+        dq[r] = float(scaling) * ((p * (dp - delta)) @ ks)
+    return round_bf16(dq)
+
+
+def attention_bwd_keys(q_hat, k_hat, v, d_o, o, segments: Segments, keys, *, window=0, scaling, causal=True,
+                       key_valid=None, row_block=1024):
+    """dk_hat and dv of selected (token, kv head) keys: the column of every
+    softmax row (of the group's query heads) that sees the key, each row
+    normalised over all its own keys; delta from the stored output o.
+    Returns bf16 values ([len(keys), D], [len(keys), D])."""
+    q_hat = np.asarray(q_hat, dtype=np.float64)
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_o = np.asarray(d_o, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    hq, hkv = q_hat.shape[1], k_hat.shape[1]
+    groups = hq // hkv
+    dk = np.zeros((len(keys), k_hat.shape[2]))
+    dv = np.zeros((len(keys), k_hat.shape[2]))
+    for r, (t, g) in enumerate(keys):
+        s0, length = segments.locate(int(t))
+        j = int(t) - s0
+        kok = None if key_valid is None else np.asarray(key_valid)[s0:s0 + length]
+        if kok is not None and not kok[j]:
+            continue
+        ks, vs = k_hat[s0:s0 + length, g], v[s0:s0 + length, g]
+        # the rows that can see key j
+        if causal:
+            lo_i, hi_i = j, (length if not window or window <= 0 else min(length, j + window))
+        else:
+            lo_i, hi_i = 0, length
+        for h in range(g * groups, (g + 1) * groups):
+            for r0 in range(lo_i, hi_i, row_block):
+                r1 = min(hi_i, r0 + row_block)
+                qb = q_hat[s0 + r0:s0 + r1, h]
+                vis = visible_mask(np.arange(r0, r1), np.arange(length), window, causal, kok)
+                sc = np.where(vis, float(scaling) * (qb @ ks.T), -np.inf)
+                seen = vis.any(axis=1)
+                mx = np.where(seen, sc.max(axis=1, initial=-np.inf), 0.0)[:, None]
+                e = np.where(vis, np.exp(sc - mx), 0.0)
+                z = e.sum(axis=1)
+                pj = np.where(seen, e[:, j] / np.where(z > 0, z, 1.0), 0.0)
+                dob = d_o[s0 + r0:s0 + r1, h]
+                dpj = dob @ vs[j]
+                delta = np.sum(dob * o[s0 + r0:s0 + r1, h], axis=1)
+                dsj = pj * (dpj - delta)
+                dk[r] += float(scaling) * (dsj @ qb)
+                dv[r] += pj @ dob
+    return round_bf16(dk), round_bf16(dv)

@@ -270,3 +270,26 @@ def test_delta_from_the_exact_output_is_the_softmax_correction(case):
     c = O.attention_bwd(q_hat, k_hat, x["v"], x["dout"], segs, o=_bf16(o_exact), **kw)
     np.testing.assert_allclose(c[2], a[2], rtol=1e-12, atol=1e-12)      # dv does not use delta
     assert np.abs(c[0] - a[0]).max() > 0.0
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_row_and_key_subsets_match_the_full_backward(case):
+    x, segs, _, _ = _inputs(case, 48)
+    q_hat = _bf16(np.random.default_rng(5).standard_normal(x["q"].shape))
+    k_hat = _bf16(np.random.default_rng(6).standard_normal(x["k"].shape))
+    o = _bf16(np.random.default_rng(7).standard_normal(x["q"].shape))
+    kw = dict(window=case["window"], scaling=0.35, causal=case["causal"], key_valid=case["valid"])
+    dq, dk, dv = O.attention_bwd(q_hat, k_hat, x["v"], x["dout"], segs, o=o, **kw)
+    n = q_hat.shape[0]
+    rows = [(t, h) for t in range(n) for h in range(case["hq"])]
+    tok = np.array([t for t, _ in rows])
+    hd = np.array([h for _, h in rows])
+    got = O.attention_bwd_rows(q_hat[tok, hd], k_hat, x["v"], x["dout"][tok, hd], o[tok, hd], segs, rows,
+                               num_heads=case["hq"], **kw)
+    np.testing.assert_allclose(got, dq[tok, hd], rtol=0, atol=1e-12)
+    keys = [(t, g) for t in range(n) for g in range(case["hkv"])]
+    gk, gv = O.attention_bwd_keys(q_hat, k_hat, x["v"], x["dout"], o, segs, keys, row_block=3, **kw)
+    kt = np.array([t for t, _ in keys])
+    kg = np.array([g for _, g in keys])
+    np.testing.assert_allclose(gk, dk[kt, kg], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gv, dv[kt, kg], rtol=0, atol=1e-12)
