@@ -74,7 +74,8 @@ def _core_bwd_magnitudes(case, dout_f64, ref, kw):
     dgate_a = np.abs(dout_f64 * y * sig * (1.0 - sig))
     _, _, _, dqh_a, dkh_a, dv_a = O.attention_bwd(fw["q_hat"], fw["k_hat"], bits_f64(case.x["v"]), ref["d_o"],
                                                   case.segs, window=kw["window"], scaling=kw["scaling"], o=o,
-                                                  mags=True, d_o_abs=do_a, causal=kw.get("causal", True))
+                                                  mags=True, d_o_abs=do_a, causal=kw.get("causal", True),
+                                                  key_valid=kw.get("key_valid"))
 
     def back(g_a, x_bits, gain, qs):
         if kw["use_rope"]:
@@ -207,3 +208,72 @@ def test_bwd_is_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------- modes: bidirectional, padded keys
+
+MODES = [
+    (W.small_workload("thd_bidir_g4", num_heads=8, num_kv_heads=2, head_dim=128,
+                      segment_lengths=(64, 1, 129, 200, 0, 65)), dict(bidirectional=True), None),
+    (W.small_workload("bshd_bidir_d64", num_heads=4, num_kv_heads=1, head_dim=64, batch=2, seqlen=100),
+     dict(bidirectional=True), None),
+    (BWD[1], {}, "left"),
+    (BWD[2], {}, "holes"),
+    (BWD[6], {}, "holes"),
+]
+MODE_IDS = ["thd_bidir", "bshd_bidir_d64", "pad_left", "pad_holes_w37", "pad_holes_w1"]
+
+
+def _mask(kind, batch, seqlen):
+    rng = np.random.default_rng(len(kind))
+    valid = np.ones((batch, seqlen), dtype=bool)
+    for b in range(batch):
+        if kind == "left":
+            valid[b, :int(rng.integers(1, seqlen))] = False
+        else:
+            valid[b] = rng.random(seqlen) > 0.35
+    return valid
+
+
+@pytest.mark.parametrize("w,kw,pad", MODES, ids=MODE_IDS)
+def test_attention_bwd_modes(w, kw, pad):
+    case = make_case(w, **kw)
+    valid = None
+    lay = case.layout
+    if pad:
+        valid = _mask(pad, w.batch, w.seqlen)
+        lay = m.Layout.bshd(w.batch, w.seqlen, attention_mask=torch.from_numpy(valid).cuda())
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, lay, case.q, case.k, case.q_gain, case.k_gain,
+                                             case.cos, case.sin)
+    o, lse = m.muse_gqa_attn_fwd(case.params, lay, q_hat, k_hat, case.v, want_lse=True)
+    d_o = dev_bf16(_grad(case, "d_o"))
+    delta = m.muse_attn_bwd_delta(case.params, lay, o, d_o)
+    dq, dk, dv = m.muse_gqa_attn_bwd(case.params, lay, q_hat, k_hat, case.v, d_o, lse, delta)
+    torch.cuda.synchronize()
+    okw = dict(window=case.x["window"], scaling=case.scaling, causal=not case.params.bidirectional,
+               key_valid=None if valid is None else valid.reshape(-1))
+    rq, rk, rv = O.attention_bwd(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), f64(d_o), case.segs,
+                                 o=f64(o), **okw)
+    check_bf16(f64(dq), rq, what="dq_hat")
+    check_bf16(f64(dk), rk, what="dk_hat")
+    check_bf16(f64(dv), rv, what="dv")
+    if valid is not None:
+        # padded keys get exactly zero gradients; queries with no key get a zero dq
+        flat = torch.from_numpy(~valid.reshape(-1)).cuda()
+        assert torch.all(dk[flat] == 0) and torch.all(dv[flat] == 0)
+        none = torch.from_numpy(~np.isfinite(f64(lse)).all(axis=1)).cuda()
+        if bool(none.any()):
+            assert torch.all(dq[none] == 0)
+    # the whole core, end to end, on the same mode
+    dout = dev_bf16(_grad(case, "dout"))
+    res = m.muse_attn_core_bwd(case.params, lay, case.q, case.k, case.v, case.gate, dout, case.q_gain,
+                               case.k_gain, case.cos, case.sin)
+    torch.cuda.synchronize()
+    ckw = case.oracle_kw()
+    ckw.pop("upcast_rope")
+    ref = O.attn_core_bwd(bits_f64(case.x["q"]), bits_f64(case.x["k"]), bits_f64(case.x["v"]),
+                          bits_f64(case.x["gate"]), f64(dout), case.segs,
+                          key_valid=None if valid is None else valid.reshape(-1), **ckw)
+    mag = _core_bwd_magnitudes(case, f64(dout), ref, dict(ckw, key_valid=None if valid is None else valid.reshape(-1)))
+    for name, got in zip(("dq", "dk", "dv", "dgate"), res[:4]):
+        _check_scaled(f64(got), ref[name], mag[name], f"core {name}")
