@@ -250,6 +250,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) 
   const bool bidir = a.bidirectional != 0;
   const float c2 = a.scale_log2;
   constexpr int RB = T::ROW_BYTES;
+  // causal: qpos - kp in [0, W) (or [0, inf) without a window); bidirectional:
+  // L - 1 - kp in [0, L), i.e. kp inside the segment
+  const int mask_base = bidir ? L - 1 : qpos;
+  const uint32_t mask_lim = bidir ? (uint32_t)L : (W > 0 ? (uint32_t)W : 0x7FFFFFFFu);
 
   auto compute = [&](int kt, int BUF) __attribute__((always_inline)) {
     const int k0 = kt * BN;
@@ -267,12 +271,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) 
 #pragma unroll
       for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2));
       if (!all_visible || padded) {
-        const uint32_t kbits = (uint32_t)(kmask >> (half * 32 + g * 4));
+        // key kp is visible iff (unsigned)(mask_base - kp) < mask_lim (one compare, no branches)
+        const uint32_t kbits = padded ? (uint32_t)(kmask >> (half * 32 + g * 4)) : ~0u;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kp = k0 + half * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          bool vis = bidir ? kp < L : kp <= qpos && (W <= 0 || kp > qpos - W);
-          if (padded) vis = vis && ((kbits >> ((i >> 2) * 8 + (i & 3))) & 1u);
+          const bool vis = ((uint32_t)(mask_base - kp) < mask_lim) & ((kbits >> ((i >> 2) * 8 + (i & 3))) & 1u);
           p[i] = vis ? p[i] : 0.0f;
         }
       }
@@ -372,6 +376,11 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
   const int W = a.window;
   const bool bidir = a.bidirectional != 0;
   const float c2 = a.scale_log2;
+  // causal: qp - key in [0, min(W, L - key)) -- the query is at or after the
+  // key, inside the window and inside the segment; bidirectional: qp in [0, L)
+  const int mask_base = bidir ? 0 : key;
+  const int lim_c = W > 0 ? min(W, L - key) : L - key;
+  const uint32_t mask_lim = bidir ? (uint32_t)L : (uint32_t)max(lim_c, 0);
   // queries that can see a key of this block
   const int qlo = bidir ? 0 : kb0;
   const int qhi = bidir || W <= 0 ? L - 1 : min(L - 1, min(kb0 + COLS - 1, L - 1) + W - 1);
@@ -431,23 +440,27 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
     for (int half = 0; half < 2; ++half) {
       const f32x16 s = rows_times<D>(Qt, ad, half * 32 * RB, kf);
       const f32x16 dp = rows_times<D>(Ot, ad, half * 32 * RB, vf);
-      float p[16], ds[16];
+      float p[16], ds[16], dl[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(Lt + half * 32 + 8 * j + 4 * g);
         const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(Dl + half * 32 + 8 * j + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 4 * j + e;
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -(l4[e] * kLog2e)));
-          if (!all_visible) {
-            const int qp = t0 + half * 32 + 8 * j + 4 * g + e;
-            const bool vis = qp < L && (bidir || (key <= qp && (W <= 0 || key > qp - W)));
-            p[i] = vis ? p[i] : 0.0f;
-          }
-          ds[i] = p[i] * (dp[i] - d4[e]);
+          p[4 * j + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * j + e], c2, -(l4[e] * kLog2e)));
+          dl[4 * j + e] = d4[e];
         }
       }
+      if (!all_visible) {
+        // query qp sees this lane's key iff (unsigned)(qp - mask_base) < mask_lim
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qp = t0 + half * 32 + (i >> 2) * 8 + 4 * g + (i & 3);
+          p[i] = (uint32_t)(qp - mask_base) < mask_lim ? p[i] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp[i] - dl[i]);
       bf16x8 p0, p1, d0, d1;
       pack16(p, p0, p1);
       pack16(ds, d0, d1);
