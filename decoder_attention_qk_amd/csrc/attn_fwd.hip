@@ -281,6 +281,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   const int W = a.window;
   const bool bidir = a.bidirectional != 0;
   const float c2 = a.scale_log2;
+  // key kp is visible iff (unsigned)(mask_base - kp) < mask_lim: causal,
+  // qpos - kp in [0, W) (or [0, inf) without a window); bidirectional,
+  // L - 1 - kp in [0, L)
+  const int mask_base = bidir ? L - 1 : qpos;
+  const uint32_t mask_lim = bidir ? (uint32_t)L : (W > 0 ? (uint32_t)W : 0x7FFFFFFFu);
 
   // called with literal buffer indices so LDS offsets fold into immediates
   auto compute = [&](int kt, int BUF) __attribute__((always_inline)) {
@@ -313,14 +318,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     };
     auto mask = [&](f32x16 &sv, int half) __attribute__((always_inline)) {
       // this lane's keys of the half as bits at compile-time positions
-      // (8 (i/4) + i%4) of one 32-bit word
-      const uint32_t kbits = (uint32_t)(kmask >> (half * 32 + g * 4));
+      // (8 (i/4) + i%4) of one 32-bit word; visibility is one unsigned range
+      // compare per key (no branches)
+      const uint32_t kbits = padded ? (uint32_t)(kmask >> (half * 32 + g * 4)) : ~0u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kp = k0 + half * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        bool vis = bidir ? kp < L : kp <= qpos && (W <= 0 || kp > qpos - W);
-        if (padded) vis = vis && ((kbits >> ((i >> 2) * 8 + (i & 3))) & 1u);
-        if (!vis) sv[i] = -INFINITY;
+        const bool vis = ((uint32_t)(mask_base - kp) < mask_lim) & ((kbits >> ((i >> 2) * 8 + (i & 3))) & 1u);
+        sv[i] = vis ? sv[i] : -INFINITY;
       }
     };
     // row max of both halves (a tree, for short dependency chains), folded
