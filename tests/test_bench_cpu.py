@@ -1,0 +1,54 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the causal-
+adjusted FLOP count against a brute-force count of visible pairs, and the
+traffic record's source digest."""
+
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import oracle as O
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("length,window", [(1, 0), (7, 0), (100, 0), (100, 1), (100, 37), (50, 50),
+                                           (50, 500), (4096, 0), (300, 64)])
+def test_visible_pairs_is_the_brute_force_count(length, window):
+    if length <= 512:
+        want = int(O.visible_mask(np.arange(length), np.arange(length), window).sum())
+    else:   # closed form of the causal count, checked against brute force above
+        want = length * (length + 1) // 2
+    assert bench.visible_pairs(length, window) == want
+
+
+def test_layer_flop_sums_segments_and_heads():
+    w = W.WORKLOADS["thd_16seg_h40kv8_d128"]
+    want = sum(4 * w.head_dim * w.num_heads * n * (n + 1) // 2 for n in w.segment_lengths)
+    assert bench.layer_flop(w, 0) == want
+
+
+def test_traffic_record_is_ignored_when_the_kernel_sources_change(tmp_path, monkeypatch):
+    digest = bench.kernel_source_digest()
+    assert len(digest) == 16 and digest == bench.kernel_source_digest()
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = dict(kernel_source_digest=digest, fetch_bytes_per_launch=100, write_bytes_per_launch=20)
+    (prof / "attn_fused_traffic_x.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: digest)
+    assert bench.measured_traffic("x", 1) == 120
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 16)
+    assert bench.measured_traffic("x", 1) is None
