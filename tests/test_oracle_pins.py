@@ -669,3 +669,19 @@ def test_core_rows_match_full_core():
         np.testing.assert_array_equal(part["q_hat"][r], full["q_hat"][t, h])
         assert part["lse"][r] == full["lse"][t, h]
     np.testing.assert_array_equal(part["k_hat"], full["k_hat"])
+
+
+def test_rope_rotations_compose():
+    # R(a) R(b) = R(a + b): two rotations by the table rows of positions a and b
+    # equal one rotation by the row of a + b, up to the FP32 table and the two
+    # bf16 roundings
+    rng = np.random.default_rng(50)
+    x = _bf16(rng.standard_normal((16, 64)))
+    for a, b in [(3, 5), (100, 27), (1000, 2500)]:
+        ca, sa = O.rope_cos_sin(1.0e4, 64, [a])
+        cb, sb = O.rope_cos_sin(1.0e4, 64, [b])
+        cab, sab = O.rope_cos_sin(1.0e4, 64, [a + b])
+        two = O.rope_rotate(O.rope_rotate(x, ca[0], sa[0]), cb[0], sb[0])
+        one = O.rope_rotate(x, cab[0], sab[0])
+        pair = np.maximum(np.abs(one[..., 0::2]), np.abs(one[..., 1::2])).repeat(2, axis=-1)
+        assert np.all(np.abs(two - one) <= 3 * 2.0 ** -8 * pair + 1e-3 * (a + b) * 2.0 ** -20)
