@@ -66,7 +66,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int DMA_PER_WAVE = T::TILE_BYTES / 1024 / NW;   // KiB of one tile per wave
   constexpr int KS = D / 16;   // QK^T k-steps
   constexpr int DT = D / 32;   // O^T row tiles
-  constexpr int KK = BN / 16;  // PV k-steps
   constexpr int RB = T::ROW_BYTES;
   // One array per buffer: distinct objects let the compiler see that the DMA
   // into one stage never aliases reads of the other, so LDS reads of the
