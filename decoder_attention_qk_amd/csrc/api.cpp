@@ -187,7 +187,6 @@ AttnArgs attn_args(const muse_attn_params *p, const muse_layout *l, const Geomet
   a.rope_v2 = p->upcast_rope ? 0 : 1;
   a.scaling = p->scaling;
   a.scale_log2 = p->scaling * 1.4426950408889634f;
-  a.rescale_slack = kRescaleSlackLog2 / a.scale_log2;
   a.hq = g.hq;
   a.hkv = g.hkv;
   a.group = g.group;

@@ -35,10 +35,13 @@
 // normalises its Q fragments and fetches its gate fragments while that DMA is
 // in flight.  Tiles are visited from the diagonal downwards; tiles no column of the
 // workgroup sees are never loaded, tiles every column of a wave sees skip the
-// element mask.  Softmax keeps a lagging reference max that moves only when a
-// tile exceeds it by kRescaleSlackLog2 (log2 units), so the O rescale runs on
-// few tiles; probabilities stay below 2^kRescaleSlackLog2 and the final
-// division by the running sum removes the reference.  Bidirectional mode
+// element mask.  Softmax keeps a per-column reference (a score already seen)
+// instead of a running max: each 32-key half forms its probabilities against
+// it and is kept when no lane's partial sum exceeds kSumLimit, so no
+// probability is near overflow; only a half that fails (or a column without a
+// reference yet) takes the exact column max, rescales O and the sum, and forms
+// its probabilities again.  The final division by the sum removes the
+// reference.  Bidirectional mode
 // (vision page, MuseSparkVisionAttention) sees every key of the segment;
 // padded keys of a BSHD batch (model page, MuseSparkTextModel.forward
 // attention_mask) are masked per tile, and a query left with no key gives
@@ -55,6 +58,8 @@ namespace {
 constexpr int BN = 64;        // keys per tile
 constexpr int NW = 4;         // waves per workgroup
 constexpr int COLS = 32 * NW; // query columns per workgroup
+// largest per-lane probability sum of a 32-key half kept without moving the reference
+constexpr float kSumLimit = 1048576.0f;
 
 static_assert(BN == 64, "Tile<D> holds 64-row tiles");
 
@@ -274,7 +279,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;   // reference max (raw score units) of this lane's column
+  float mc = 0.0f;           // m_run * scale_log2 (0 without a reference)
+  float sum_lim = -1.0f;     // kSumLimit once the column has a reference
   float l_run = 0.0f;
 
   const int W = a.window;
@@ -327,41 +334,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
         sv[i] = vis ? sv[i] : -INFINITY;
       }
     };
-    // row max of both halves (a tree, for short dependency chains), folded
-    // into the lagging reference once per tile
-    auto tile_max = [&](const f32x16 &s0, const f32x16 &s1) __attribute__((always_inline)) {
-      float m8[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        m8[j] = fmaxf(fmaxf(s0[4 * j], s0[4 * j + 1]), fmaxf(s0[4 * j + 2], s0[4 * j + 3]));
-        m8[4 + j] = fmaxf(fmaxf(s1[4 * j], s1[4 * j + 1]), fmaxf(s1[4 * j + 2], s1[4 * j + 3]));
-      }
-      float tmax = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                         fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-      float lo, hi;
-      swap32(tmax, lo, hi);
-      tmax = fmaxf(lo, hi);
-      const bool grow = tmax > m_run + a.rescale_slack;
-      if (__any(grow)) {
-        // other lanes may enter with this lane still at -inf (no visible key
-        // yet): its sum and accumulator are zero, keep them (no -inf - -inf)
-        const float m_new = grow ? tmax : m_run;
-        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-        m_run = m_new;
-      }
-    };
-    auto softmax = [&](const f32x16 &sv, bf16x8 &p0, bf16x8 &p1) __attribute__((always_inline)) {
-      const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c2;
+    auto softmax = [&](const f32x16 &sv, bf16x8 &p0, bf16x8 &p1) __attribute__((always_inline)) -> float {
       float pf[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c2, -mc));
       float t[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) t[j] = (pf[4 * j] + pf[4 * j + 1]) + (pf[4 * j + 2] + pf[4 * j + 3]);
-      l_run += (t[0] + t[1]) + (t[2] + t[3]);
+      const float tsum = (t[0] + t[1]) + (t[2] + t[3]);
       uint4 lo, hi;
       lo.x = pack_bf16x2(pf[0], pf[1]);   lo.y = pack_bf16x2(pf[2], pf[3]);
       lo.z = pack_bf16x2(pf[4], pf[5]);   lo.w = pack_bf16x2(pf[6], pf[7]);
@@ -369,6 +349,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       hi.z = pack_bf16x2(pf[12], pf[13]); hi.w = pack_bf16x2(pf[14], pf[15]);
       p0 = __builtin_bit_cast(bf16x8, lo);
       p1 = __builtin_bit_cast(bf16x8, hi);
+      return tsum;
     };
     auto pv = [&](int half, const bf16x8 &p0, const bf16x8 &p1) __attribute__((always_inline)) {
 #pragma unroll
@@ -386,18 +367,44 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       }
     };
 
+    // One half: probabilities against the current reference; the half is
+    // kept when every lane's partial sum is at most kSumLimit (so no
+    // probability is near overflow) and its column has a reference.  Else the
+    // column's exact max over the half becomes the reference (if larger), O and
+    // l are rescaled, and the probabilities are formed again.
+    auto half_step = [&](const f32x16 &sv, int half) __attribute__((always_inline)) {
+      bf16x8 p0, p1;
+      float t = softmax(sv, p0, p1);
+      if (__any(!(t <= sum_lim))) {
+        float m4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(sv[4 * j], sv[4 * j + 1]), fmaxf(sv[4 * j + 2], sv[4 * j + 3]));
+        float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        float lo, hi;
+        swap32(cm, lo, hi);
+        const float m_new = fmaxf(m_run, fmaxf(lo, hi));
+        // a column without a reference has l = 0 and O = 0 (no half was kept)
+        const float alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+        mc = m_run == -INFINITY ? 0.0f : m_run * c2;
+        sum_lim = m_run == -INFINITY ? -1.0f : kSumLimit;
+        t = softmax(sv, p0, p1);
+      }
+      l_run += t;
+      pv(half, p0, p1);
+    };
+
     f32x16 s0v = qk(0);
     f32x16 s1v = qk(1);
     if (!all_visible || padded) {
       mask(s0v, 0);
       mask(s1v, 1);
     }
-    tile_max(s0v, s1v);
-    bf16x8 pa0, pa1, pb0, pb1;
-    softmax(s0v, pa0, pa1);
-    pv(0, pa0, pa1);
-    softmax(s1v, pb0, pb1);
-    pv(1, pb0, pb1);
+    half_step(s0v, 0);
+    half_step(s1v, 1);
   };
 
   const int lo = W > 0 && !bidir ? max(0, q0 - W + 1) : 0;

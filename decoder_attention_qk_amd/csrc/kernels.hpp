@@ -8,10 +8,6 @@
 
 namespace muse {
 
-// Lagging-max slack of the attention softmax, in log2 units: probabilities
-// stay below 2^kRescaleSlackLog2 between rescales.
-constexpr float kRescaleSlackLog2 = 8.0f;
-
 // Where each token sits: its row/segment and its RoPE position.
 struct TokenLayout {
   int32_t n_tokens;              // N
@@ -116,7 +112,6 @@ struct AttnArgs {
   // attention
   float scaling;           // softmax scale
   float scale_log2;        // scaling * log2(e)
-  float rescale_slack;     // raw-score slack before the running max moves
   int32_t hq, hkv, group;  // group = hq / hkv
   int32_t heads_per_wg;    // query heads of one kv group handled by one workgroup
   int32_t head_chunks;     // group / heads_per_wg

@@ -381,6 +381,44 @@ def test_all_valid_mask_equals_no_mask():
     assert torch.equal(la, lb)
 
 
+# ---------------------------------------------------------------- softmax reference moves
+
+def _spiky_attention_inputs(seed, L, hq, hkv, d, spikes):
+    """q_hat aligned (or anti-aligned) with a common direction u, k_hat small noise
+    except 'spike' keys c * u, so a query's scores jump by many log2 units between
+    the tiles the kernel visits (diagonal first, then downwards)."""
+    rng = np.random.default_rng(seed)
+    u = np.ones(d)
+    sign = np.where(np.arange(hq) % 2 == 0, 1.0, -1.0)
+    q = 0.3 * rng.standard_normal((L, hq, d)) + sign[None, :, None] * u
+    k = 0.5 * rng.standard_normal((L, hkv, d))
+    for pos, c in spikes:
+        k[pos] = c * u + 0.05 * rng.standard_normal((hkv, d))
+    v = rng.standard_normal((L, hkv, d))
+    return [torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16) for a in (q, k, v)]
+
+
+@pytest.mark.parametrize("window", [0, 100])
+def test_attention_reference_moves_with_score_spikes(window):
+    # raw score of a spike key for an aligned query ~ 128 c; in log2 units of the
+    # softmax (scaling 128^-0.5) ~ 16.3 c: jumps of 8 .. 200 log2 units between
+    # visited tiles, both below the reference-move threshold (kept with a stale
+    # reference) and above it (O and the sum rescaled, or the old part flushed
+    # to zero), and far below every seen score for the anti-aligned heads
+    L, hq, hkv, d = 320, 4, 1, 128
+    spikes = [(300, 0.5), (250, 1.0), (200, 1.5), (130, 3.0), (100, 3.0), (64, 1.2), (20, 2.0), (5, 12.0)]
+    qc, kc, vc = _spiky_attention_inputs(7, L, hq, hkv, d, spikes)
+    params = m.AttnParams(head_dim=d, num_heads=hq, num_key_value_heads=hkv, sliding_window=window,
+                          use_rope=False, scaling=float(np.float32(d ** -0.5)))
+    layout = m.Layout.bshd(1, L)
+    o, lse = m.muse_gqa_attn_fwd(params, layout, qc.cuda(), kc.cuda(), vc.cuda(), want_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.attention(f64(qc), f64(kc), f64(vc), O.Segments.bshd(1, L), window=window,
+                         scaling=float(np.float32(d ** -0.5)))
+    check_bf16(f64(o), ro, what="o")
+    check_fp32(f64(lse), rl, floor=1.0, what="lse")
+
+
 # ---------------------------------------------------------------- bit-exact invariants
 
 def test_window_one_returns_v_exactly():
