@@ -32,8 +32,8 @@
 // per row on the DMA source side so both read patterns avoid bank conflicts.
 //
 // A workgroup first issues the DMA of its first tile, then loads and
-// normalises its Q fragments and fetches its gate fragments while that DMA is
-// in flight.  Tiles are visited from the diagonal downwards; tiles no column of the
+// normalises its Q fragments (and, at D = 128, fetches its gate fragments)
+// while that DMA is in flight.  Tiles are visited from the diagonal downwards; tiles no column of the
 // workgroup sees are never loaded, tiles every column of a wave sees skip the
 // element mask.  Softmax keeps a per-column reference (a score already seen)
 // instead of a running max: each 32-key half forms its probabilities against
@@ -304,11 +304,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     const lds_char *Kt = kbuf(BUF);
     const lds_char *Vt = vbuf(BUF);
 
-    // The tile is processed as two 32-key halves; the lagging reference max
-    // makes a per-half softmax exact.  Order: QK(h0), QK(h1), softmax(h0),
-    // PV(h0), softmax(h1), PV(h1) -- the MFMA chains of one half are
-    // independent of the other half's softmax, which another wave on the SIMD
-    // overlaps.
+    // The tile is processed as two 32-key halves; the per-column reference
+    // makes a per-half softmax exact (order below).
     // All K fragments of a half are read before its MFMA chain starts, so
     // the LDS latency is paid once per half rather than once per k-step.
     auto qk = [&](int half) __attribute__((always_inline)) {
@@ -372,8 +369,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     // probability is near overflow) and its column has a reference.  Else the
     // column's exact max over the half becomes the reference (if larger), O and
     // l are rescaled, and the probabilities are formed again.
-    auto half_step = [&](const f32x16 &sv, int half) __attribute__((always_inline)) {
-      bf16x8 p0, p1;
+    auto half_step = [&](const f32x16 &sv, bf16x8 &p0, bf16x8 &p1) __attribute__((always_inline)) {
       float t = softmax(sv, p0, p1);
       if (__any(!(t <= sum_lim))) {
         float m4[4];
@@ -394,17 +390,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
         t = softmax(sv, p0, p1);
       }
       l_run += t;
-      pv(half, p0, p1);
     };
 
+    // Order: QK(h0), [mask h0], QK(h1) beside softmax(h0), [mask h1], PV(h0)
+    // beside softmax(h1), PV(h1).  The masks sit in wave-uniform branches of
+    // their own, so on unmasked tiles each MFMA run and the softmax it overlaps
+    // share one basic block and the wave interleaves them.
+    const bool masked = __builtin_amdgcn_readfirstlane((int)(!all_visible || padded)) != 0;
+    bf16x8 pa0, pa1, pb0, pb1;
     f32x16 s0v = qk(0);
+    if (masked) mask(s0v, 0);
     f32x16 s1v = qk(1);
-    if (!all_visible || padded) {
-      mask(s0v, 0);
-      mask(s1v, 1);
-    }
-    half_step(s0v, 0);
-    half_step(s1v, 1);
+    half_step(s0v, pa0, pa1);
+    if (masked) mask(s1v, 1);
+    pv(0, pa0, pa1);
+    half_step(s1v, pb0, pb1);
+    pv(1, pb0, pb1);
   };
 
   const int lo = W > 0 && !bidir ? max(0, q0 - W + 1) : 0;
@@ -414,16 +415,20 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 
   issue_dma(kt_hi, 0);
   load_q();
-  // the gate fragments of the epilogue are fetched now (qrow always addresses
-  // a real row), so their latency is long hidden when they are needed
+  // The gate fragments of the epilogue (qrow always addresses a real row).
+  // At D = 128 they are fetched now, so their latency is long hidden when
+  // they are needed; at D = 64 holding them through the loop costs more than
+  // fetching them after it (measured), so the epilogue fetches them.
+  constexpr bool kGateEarly = D == 128;
   uint2 gw[DT][4];
-  if constexpr (FUSED) {
+  auto load_gate = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4)
         gw[dt][i4] = *reinterpret_cast<const uint2 *>(a.gate + qrow + dt * 32 + i4 * 8 + g * 4);
-  }
+  };
+  if constexpr (FUSED && kGateEarly) load_gate();
   vmem_wait_all();
   __syncthreads();
   for (int it = 0;;) {
@@ -442,6 +447,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 
   if (!wave_active) return;
+  if constexpr (FUSED && !kGateEarly) load_gate();
   float l_lo, l_hi;
   swap32(l_run, l_lo, l_hi);
   const float l_tot = l_lo + l_hi;
