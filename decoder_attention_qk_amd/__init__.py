@@ -17,8 +17,8 @@ import os
 
 __all__ = [
     "MuseError", "AttnParams", "Layout", "library", "library_path", "symbols",
-    "muse_rope_cos_sin", "muse_rope_cos_sin_2d", "muse_qk_norm_rope", "muse_gqa_attn_fwd",
-    "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd",
+    "muse_rope_cos_sin", "muse_rope_cos_sin_2d", "muse_qk_norm_rope", "muse_qk_norm_rope_table",
+    "muse_gqa_attn_fwd", "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd",
     "muse_attn_bwd_delta", "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd",
     "muse_qk_norm_rope_bwd_workspace_size", "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size",
     "muse_validate_cu_seqlens", "muse_status_string", "muse_version",
@@ -31,8 +31,8 @@ MUSE_OK, MUSE_ERR_INVALID_ARG, MUSE_ERR_UNSUPPORTED, MUSE_ERR_DEVICE = 0, 1, 2, 
 
 # Every symbol include/muse_attn.h declares.
 symbols = (
-    "muse_rope_cos_sin", "muse_rope_cos_sin_2d", "muse_qk_norm_rope", "muse_gqa_attn_fwd", "muse_out_norm_gate",
-    "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd", "muse_attn_bwd_delta",
+    "muse_rope_cos_sin", "muse_rope_cos_sin_2d", "muse_qk_norm_rope", "muse_qk_norm_rope_table",
+    "muse_gqa_attn_fwd", "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd", "muse_attn_bwd_delta",
     "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd", "muse_qk_norm_rope_bwd_workspace_size",
     "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size", "muse_validate_cu_seqlens",
     "muse_status_string", "muse_last_error", "muse_version",
@@ -68,6 +68,7 @@ _SIGS = {
     "muse_rope_cos_sin": [ctypes.c_float, _I32, _I32, _P, _P, _P],
     "muse_rope_cos_sin_2d": [ctypes.c_float, _I32, _I32, _I32, _P, _P, _P],
     "muse_qk_norm_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P],
+    "muse_qk_norm_rope_table": [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P, _P, _P, _P, _P, _P],
     "muse_gqa_attn_fwd": [_P, _P, _P, _P, _P, _P, _P, _P],
     "muse_out_norm_gate": [_P, _P, _P, _P, _P, _P, _P],
     "muse_attn_core_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P],
@@ -288,6 +289,37 @@ def muse_qk_norm_rope(params: AttnParams, layout: Layout, q, k, q_gain=None, k_g
         _ptr(sin, "sin", "fp32"), n_pos, _ptr(q_out, "q_out", "bf16"), _ptr(k_out, "k_out", "bf16"),
         _ptr(q_rstd, "q_rstd", "fp32"), _ptr(k_rstd, "k_rstd", "fp32"), _stream(stream)))
     return q_out, k_out, q_rstd, k_rstd
+
+
+def muse_qk_norm_rope_table(params: AttnParams, layout: Layout, q, k, q_gain=None, k_gain=None, *,
+                            theta: float, n_pos: int, cos_out=None, sin_out=None, q_out=None, k_out=None,
+                            q_rstd=None, k_rstd=None, want_rstd=False, stream=None):
+    """muse_qk_norm_rope that also builds the RoPE table rows of its tokens'
+    positions; returns (q_out, k_out, q_rstd, k_rstd, cos_out, sin_out)."""
+    import torch
+    like = q if q is not None else k
+    if q is not None and q_out is None:
+        q_out = torch.empty_like(q)
+    if k is not None and k_out is None:
+        k_out = torch.empty_like(k)
+    if cos_out is None:
+        cos_out = _empty((n_pos, params.head_dim // 2), torch.float32, like)
+    if sin_out is None:
+        sin_out = _empty((n_pos, params.head_dim // 2), torch.float32, like)
+    if want_rstd:
+        n = like.shape[0]
+        if q is not None and q_rstd is None:
+            q_rstd = _empty((n, params.num_heads), torch.float32, like)
+        if k is not None and k_rstd is None:
+            k_rstd = _empty((n, params.num_key_value_heads), torch.float32, like)
+    p, l = params.to_c(), layout.to_c()
+    _check(library().muse_qk_norm_rope_table(
+        ctypes.byref(p), ctypes.byref(l), _ptr(q, "q", "bf16"), _ptr(k, "k", "bf16"),
+        _ptr(q_gain, "q_gain", "fp32"), _ptr(k_gain, "k_gain", "fp32"), float(theta), int(n_pos),
+        _ptr(cos_out, "cos_out", "fp32"), _ptr(sin_out, "sin_out", "fp32"), _ptr(q_out, "q_out", "bf16"),
+        _ptr(k_out, "k_out", "bf16"), _ptr(q_rstd, "q_rstd", "fp32"), _ptr(k_rstd, "k_rstd", "fp32"),
+        _stream(stream)))
+    return q_out, k_out, q_rstd, k_rstd, cos_out, sin_out
 
 
 def muse_gqa_attn_fwd(params: AttnParams, layout: Layout, q_hat, k_hat, v, *, o=None, lse=None,

@@ -237,15 +237,21 @@ extern "C" muse_status muse_rope_cos_sin_2d(float theta, int32_t head_dim, int32
   return device_status(launch_rope_table(a, (hipStream_t)stream), "2-D rope table launch");
 }
 
-extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_layout *l, const void *q,
-                                         const void *k, const float *q_gain, const float *k_gain,
-                                         const float *cos, const float *sin, int32_t n_pos, void *q_out,
-                                         void *k_out, float *q_rstd, float *k_rstd, void *stream) {
+// muse_qk_norm_rope, and with table_out muse_qk_norm_rope_table (cos/sin are
+// then the tables to write, theta their base).
+static muse_status qk_norm_rope_impl(const muse_attn_params *p, const muse_layout *l, const void *q,
+                                     const void *k, const float *q_gain, const float *k_gain, const float *cos,
+                                     const float *sin, int32_t n_pos, void *q_out, void *k_out, float *q_rstd,
+                                     float *k_rstd, void *stream, bool table_out, float theta) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
   Geometry g;
   s = check_layout(l, p, (hipStream_t)stream, &g);
   if (s != MUSE_OK) return s;
+  if (table_out) {
+    if (!p->use_rope) return set_error(MUSE_ERR_INVALID_ARG, "the table is built only for use_rope");
+    if (!std::isfinite(theta) || theta <= 0.0f) return set_error(MUSE_ERR_INVALID_ARG, "theta must be finite and > 0");
+  }
   if ((q == nullptr) != (q_out == nullptr)) return set_error(MUSE_ERR_INVALID_ARG, "q and q_out must be given together");
   if ((k == nullptr) != (k_out == nullptr)) return set_error(MUSE_ERR_INVALID_ARG, "k and k_out must be given together");
   if (!q && !k) return set_error(MUSE_ERR_INVALID_ARG, "neither q nor k given");
@@ -257,12 +263,14 @@ extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_l
   if (s != MUSE_OK) return s;
   const int64_t N = g.n_tokens;
   const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
+  const int64_t tab_in = table_out ? 0 : tab, tab_out = table_out ? tab : 0;
   s = check_disjoint(
       {{q, bf16_bytes(N, g.hq, g.d), "q"}, {k, bf16_bytes(N, g.hkv, g.d), "k"}, {q_gain, g.d * 4, "q_gain"},
-       {k_gain, g.d * 4, "k_gain"}, {cos, tab, "cos"}, {sin, tab, "sin"}, layout_range(l, g, 0),
-       layout_range(l, g, 1)},
+       {k_gain, g.d * 4, "k_gain"}, {table_out ? nullptr : cos, tab_in, "cos"},
+       {table_out ? nullptr : sin, tab_in, "sin"}, layout_range(l, g, 0), layout_range(l, g, 1)},
       {{q_out, bf16_bytes(N, g.hq, g.d), "q_out"}, {k_out, bf16_bytes(N, g.hkv, g.d), "k_out"},
-       {q_rstd, N * g.hq * 4, "q_rstd", 4}, {k_rstd, N * g.hkv * 4, "k_rstd", 4}});
+       {q_rstd, N * g.hq * 4, "q_rstd", 4}, {k_rstd, N * g.hkv * 4, "k_rstd", 4},
+       {table_out ? cos : nullptr, tab_out, "cos_out"}, {table_out ? sin : nullptr, tab_out, "sin_out"}});
   if (s != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
   QkNormArgs a;
@@ -290,8 +298,31 @@ extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_l
   a.use_rope = p->use_rope ? 1 : 0;
   a.rope_v2 = p->upcast_rope ? 0 : 1;
   a.skip_norm = p->skip_qk_norm ? 1 : 0;
+  if (table_out) {
+    a.cos_tab = a.sin_tab = nullptr;
+    a.theta = theta;
+    a.cos_out = const_cast<float *>(cos);
+    a.sin_out = const_cast<float *>(sin);
+  }
   a.lay = token_layout(l, g);
   return device_status(launch_qk_norm_rope(g.d, a, (hipStream_t)stream), "qk_norm_rope launch");
+}
+
+extern "C" muse_status muse_qk_norm_rope(const muse_attn_params *p, const muse_layout *l, const void *q,
+                                         const void *k, const float *q_gain, const float *k_gain,
+                                         const float *cos, const float *sin, int32_t n_pos, void *q_out,
+                                         void *k_out, float *q_rstd, float *k_rstd, void *stream) {
+  return qk_norm_rope_impl(p, l, q, k, q_gain, k_gain, cos, sin, n_pos, q_out, k_out, q_rstd, k_rstd, stream,
+                           false, 0.0f);
+}
+
+extern "C" muse_status muse_qk_norm_rope_table(const muse_attn_params *p, const muse_layout *l, const void *q,
+                                               const void *k, const float *q_gain, const float *k_gain,
+                                               float theta, int32_t n_pos, float *cos_out, float *sin_out,
+                                               void *q_out, void *k_out, float *q_rstd, float *k_rstd,
+                                               void *stream) {
+  return qk_norm_rope_impl(p, l, q, k, q_gain, k_gain, cos_out, sin_out, n_pos, q_out, k_out, q_rstd, k_rstd,
+                           stream, true, theta);
 }
 
 extern "C" muse_status muse_gqa_attn_fwd(const muse_attn_params *p, const muse_layout *l, const void *q_hat,

@@ -48,6 +48,12 @@ struct QkNormArgs {
   int32_t use_rope;
   int32_t rope_v2;         // rotation in the Q/K dtype (upcast_rope == 0)
   int32_t skip_norm;       // scale/rotate only: no RMSNorm, no gain
+  // table mode (cos_out != nullptr): each block evaluates the cos/sin rows of
+  // its rows' token positions (rope_entry, as the table kernel) instead of
+  // reading cos_tab/sin_tab, uses them, and writes them to cos_out/sin_out
+  float theta;
+  float *cos_out;
+  float *sin_out;
   TokenLayout lay;
 };
 
@@ -152,6 +158,23 @@ hipError_t launch_qk_norm_rope_bwd(int head_dim, const QkNormBwdArgs &a, hipStre
 hipError_t launch_attn_bwd(int head_dim, const AttnBwdArgs &a, hipStream_t stream);
 int attn_bwd_keys_per_workgroup();
 int attn_columns_per_workgroup();  // (token, head) query columns one attention workgroup holds
+
+// One RoPE table entry: pair i of a head `width` wide at coordinate coord.
+// The inverse frequency theta^(-2i/width) and the cosine/sine are evaluated
+// in double and rounded once to binary32; the angle is the binary32 product
+// of the coordinate and that frequency.  Every kernel that forms table
+// entries calls this, so they agree bit for bit.
+__device__ __forceinline__ float rope_inv_freq(float theta, int i, int width) {
+  return (float)pow((double)theta, -2.0 * (double)i / (double)width);
+}
+__device__ __forceinline__ void rope_cos_sin(int coord, float inv, float &c, float &s) {
+  const float ang = (float)coord * inv;
+  c = (float)cos((double)ang);
+  s = (float)sin((double)ang);
+}
+__device__ __forceinline__ void rope_entry(float theta, int i, int width, int coord, float &c, float &s) {
+  rope_cos_sin(coord, rope_inv_freq(theta, i, width), c, s);
+}
 
 // Position of token t for RoPE (clamped into the table), and its segment.
 __device__ __forceinline__ int find_segment(const TokenLayout &l, int t) {

@@ -10,6 +10,14 @@
 // outstanding before it computes.  The first q_blocks blocks take Q rows
 // (row r = token * Hq + head), the others K rows, so the tensor, its gain and
 // the query scale are uniform per block.
+//
+// Table mode (TAB): a block's rows are consecutive, so they touch a short
+// run of tokens; the block first evaluates the cos/sin rows of those tokens'
+// positions (one entry per thread and pass, rope_entry's arithmetic as in the
+// table kernel, with the inverse frequencies computed once per block),
+// keeps them in LDS for its own rotations and writes them to the table, so
+// the table costs no launch of its own.  Tokens that share a position write
+// identical bits.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -23,12 +31,20 @@ constexpr int kRowsInFlight = 2;
 // ROPE: 0 no rotation, 1 FP32 rotation (upcast_rope), 2 rotation in the Q/K
 // dtype; QS: query_scale != 1 (K rows then take the exact identity scale 1,
 // which leaves their bf16 values unchanged); NORM: false skips the RMSNorm
-// and gain (the vision attention rotates un-normalised Q/K).
-template <int D, int ROPE, bool QS, bool NORM>
+// and gain (the vision attention rotates un-normalised Q/K); TAB: table mode
+// (ROPE != 0).
+template <int D, int ROPE, bool QS, bool NORM, bool TAB>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
   constexpr int LPR = D / 8;               // lanes per row
   constexpr int RPP = kThreads / LPR;      // rows per pass of the block
+  constexpr int RPB = RPP * kRowsInFlight; // rows of a block (consecutive)
+  constexpr int HALF = D / 2;
   static_assert(LPR == 8 || LPR == 16, "row_sum covers 8 or 16 lanes");
+  static_assert(!TAB || ROPE != 0, "table mode rotates");
+  // cos then sin rows of the block's tokens (at most RPB tokens), and the
+  // inverse frequencies they share
+  __shared__ __attribute__((aligned(16))) float tab[TAB ? 2 * RPB * HALF : 1];
+  __shared__ float inv_freq[TAB ? HALF : 1];
   const int c = threadIdx.x % LPR;         // chunk: elements [8c, 8c+8)
   const int rsub = threadIdx.x / LPR;
 
@@ -61,10 +77,39 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
     w[6] = a.gain_center + g1.z; w[7] = a.gain_center + g1.w;
   }
 
+  // table mode: the cos/sin rows of tokens t_first .. t_last (every row of
+  // this block has r < nrows; blocks are sized to start below nrows)
+  int t_first = 0;
+  if constexpr (TAB) {
+    const int r0 = blk * RPB;
+    const int r1 = min(r0 + RPB, nrows) - 1;
+    t_first = (int)hdiv.div((uint32_t)r0);
+    const int n = ((int)hdiv.div((uint32_t)r1) - t_first + 1) * HALF;
+    for (int i = threadIdx.x; i < HALF; i += kThreads) inv_freq[i] = rope_inv_freq(a.theta, i, D);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < n; idx += kThreads) {
+      const int t = t_first + idx / HALF;
+      const int i = idx % HALF;
+      const int p = rope_position(a.lay, t, a.n_pos);
+      float cv, sv;
+      rope_cos_sin(p, inv_freq[i], cv, sv);   // = rope_entry(a.theta, i, D, p, ...)
+      tab[idx] = cv;
+      tab[RPB * HALF + idx] = sv;
+      a.cos_out[(int64_t)p * HALF + i] = cv;
+      a.sin_out[(int64_t)p * HALF + i] = sv;
+    }
+    __syncthreads();
+  }
+
   // RoPE positions of this thread's rows (tokens increase with j; a packed
-  // layout walks its segments forward from the first row's)
+  // layout walks its segments forward from the first row's); in table mode
+  // the row's token instead (its LDS row)
   int pos[kRowsInFlight];
-  if constexpr (ROPE != 0) {
+  if constexpr (TAB) {
+#pragma unroll
+    for (int j = 0; j < kRowsInFlight; ++j)
+      pos[j] = (int)hdiv.div((uint32_t)min(base + j * RPP, nrows - 1)) - t_first;
+  } else if constexpr (ROPE != 0) {
     int seg = -1;
 #pragma unroll
     for (int j = 0; j < kRowsInFlight; ++j) {
@@ -97,8 +142,10 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
     if (r >= nrows) continue;
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (ROPE != 0) {
-      const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)pos[j] * (D / 2) + c * 4);
-      const float4 sv = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)pos[j] * (D / 2) + c * 4);
+      const float *ct = TAB ? tab + pos[j] * HALF : a.cos_tab + (int64_t)pos[j] * HALF;
+      const float *st = TAB ? tab + RPB * HALF + pos[j] * HALF : a.sin_tab + (int64_t)pos[j] * HALF;
+      const float4 cv = *reinterpret_cast<const float4 *>(ct + c * 4);
+      const float4 sv = *reinterpret_cast<const float4 *>(st + c * 4);
       cs[0] = cv.x; cs[1] = cv.y; cs[2] = cv.z; cs[3] = cv.w;
       sn[0] = sv.x; sn[1] = sv.y; sn[2] = sv.z; sn[3] = sv.w;
     }
@@ -115,12 +162,23 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
   }
 }
 
+template <int D, int ROPE, bool NORM, bool TAB>
+void launch_t(const QkNormArgs &a, dim3 grid, hipStream_t stream) {
+  if (a.q_rows > 0 && a.query_scale != 1.0f)
+    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, true, NORM, TAB>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, false, NORM, TAB>), grid, dim3(kThreads), 0, stream, a);
+}
+
 template <int D, int ROPE, bool NORM>
 void launch_r(const QkNormArgs &a, dim3 grid, hipStream_t stream) {
-  if (a.q_rows > 0 && a.query_scale != 1.0f)
-    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, true, NORM>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((qk_norm_rope_kernel<D, ROPE, false, NORM>), grid, dim3(kThreads), 0, stream, a);
+  if constexpr (ROPE != 0) {
+    if (a.cos_out) {
+      launch_t<D, ROPE, NORM, true>(a, grid, stream);
+      return;
+    }
+  }
+  launch_t<D, ROPE, NORM, false>(a, grid, stream);
 }
 
 template <int D, bool NORM>

@@ -8,9 +8,9 @@
 // row-major patch grid): the first D/4 pairs of patch (y, x) take the 1-D
 // angles of a D/2-wide head at coordinate y, the last D/4 pairs those at x.
 //
-// One thread per (position, pair).  The inverse frequency and the cosine/sine
-// are evaluated in double and rounded once to binary32; the angle itself is
-// the binary32 product of the coordinate and that frequency.
+// One thread per (position, pair); each entry is rope_entry's (inverse
+// frequency and cosine/sine in double, rounded once to binary32; the angle
+// the binary32 product of the coordinate and that frequency).
 #include "kernels.hpp"
 
 namespace muse {
@@ -28,10 +28,10 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
     coord = i < quarter ? p / a.grid_w : p % a.grid_w;
     j = i < quarter ? i : i - quarter;
   }
-  const float inv = (float)pow((double)a.theta, -2.0 * (double)j / (double)width);
-  const float ang = (float)coord * inv;
-  a.cos_out[idx] = (float)cos((double)ang);
-  a.sin_out[idx] = (float)sin((double)ang);
+  float c, s;
+  rope_entry(a.theta, j, width, coord, c, s);
+  a.cos_out[idx] = c;
+  a.sin_out[idx] = s;
 }
 
 hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t stream) {

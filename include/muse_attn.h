@@ -219,6 +219,30 @@ muse_status muse_qk_norm_rope(const muse_attn_params *params, const muse_layout 
                               float *k_rstd, void *stream);
 
 /*
+ * muse_qk_norm_rope with the 1-D RoPE table built in the same launch (layers
+ * page, MuseSparkRotaryEmbedding and _qk_norm_rope_core): instead of reading
+ * cos/sin, the call evaluates the table rows of the positions its tokens have
+ * -- every entry exactly as muse_rope_cos_sin(theta, head_dim, n_pos) writes
+ * it (same bits) -- rotates with them, and writes those rows into cos_out /
+ * sin_out, so that a following muse_attn_fused_fwd (or muse_qk_norm_rope)
+ * can read them.  Rows of positions no token has are left untouched; with
+ * implicit positions (no position_ids) every position below the longest
+ * row/segment is written.  Tokens that share a position write identical bits.
+ *
+ * theta     as muse_rope_cos_sin.
+ * n_pos     rows of cos_out / sin_out (the position rules of muse_qk_norm_rope).
+ * cos_out, sin_out  device fp32 [n_pos, D/2], written (rows as above).
+ * Other arguments as muse_qk_norm_rope.
+ * Errors: as muse_qk_norm_rope; INVALID_ARG also when use_rope is 0, theta is
+ * not finite and > 0, or cos_out / sin_out overlap each other or any input.
+ */
+muse_status muse_qk_norm_rope_table(const muse_attn_params *params, const muse_layout *layout,
+                                    const void *q, const void *k, const float *q_gain,
+                                    const float *k_gain, float theta, int32_t n_pos,
+                                    float *cos_out, float *sin_out, void *q_out, void *k_out,
+                                    float *q_rstd, float *k_rstd, void *stream);
+
+/*
  * Causal GQA softmax attention on normalised, rotated Q/K (layers page,
  * MuseSparkAttention: scaling = head_dim ** -0.5, GQA groups, sliding_window;
  * model page, _causal_mask).

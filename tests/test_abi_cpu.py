@@ -146,6 +146,29 @@ def test_qk_norm_rope_argument_rules():
     assert call(qo=FAKE + 100) == 1                        # output overlaps input
 
 
+def test_qk_norm_rope_table_argument_rules():
+    lib = m.library()
+    lay = _bshd()
+    base = dict(q=FAKE, k=FAKE + (1 << 24), qg=None, kg=None, theta=1e4, npos=16, cos=FAKE + (2 << 24),
+                sin=FAKE + (3 << 24), qo=FAKE + (4 << 24), ko=FAKE + (5 << 24), qr=None, kr=None)
+
+    def call(p=None, **over):
+        a = dict(base)
+        a.update(over)
+        return lib.muse_qk_norm_rope_table(ctypes.byref(p or _params()), ctypes.byref(lay), a["q"], a["k"],
+                                           a["qg"], a["kg"], a["theta"], a["npos"], a["cos"], a["sin"],
+                                           a["qo"], a["ko"], a["qr"], a["kr"], None)
+    assert call(p=_params(use_rope=0)) == 1                # the table is a RoPE table
+    assert call(theta=0.0) == 1
+    assert call(theta=float("nan")) == 1
+    assert call(cos=None) == 1
+    assert call(npos=8) == 1                               # table shorter than the row
+    assert call(cos=FAKE + 100) == 1                       # table output overlaps input q
+    assert call(sin=FAKE + (2 << 24) + 64) == 1            # the two tables overlap
+    assert call(ko=FAKE + (2 << 24)) == 1                  # k_out overlaps cos_out
+    assert call(q=None, qo=None, k=None, ko=None) == 1     # nothing to do
+
+
 def test_rope_table_argument_rules():
     lib = m.library()
     assert lib.muse_rope_cos_sin(0.0, 64, 4, FAKE, FAKE + 4096, None) == 1

@@ -492,6 +492,66 @@ def test_explicit_position_ids_match_oracle():
     check_bf16(f64(out), ref["out"], what="out with position_ids")
 
 
+# ---------------------------------------------------------------- table built by the Q/K pass
+
+TABLE_CASES = [
+    ("bshd_b2_s200_g4", dict(), None),
+    ("thd_g3_mixed", dict(), None),
+    ("bshd_s130_g1_d64", dict(), None),
+    ("bshd_b2_s200_g4", dict(upcast_rope=False), None),
+    ("bshd_b2_s200_g4", dict(query_scale=0.75), None),
+    ("bshd_b2_s200_g4", dict(), "posids"),
+]
+
+
+@pytest.mark.parametrize("name,kw,pos_mode", TABLE_CASES,
+                         ids=[f"{n}-{'-'.join(k) or 'base'}-{p or 'implicit'}" for n, k, p in TABLE_CASES])
+def test_qk_norm_rope_table_equals_two_launches(name, kw, pos_mode):
+    """The one-launch table mode rotates Q and K with, and writes, exactly the
+    entries muse_rope_cos_sin produces (bitwise), and leaves rows of positions
+    no token has untouched."""
+    w = next(x for x in SMALL if x.name == name)
+    case = make_case(w, **kw)
+    lay, n_pos = case.layout, case.n_pos
+    if pos_mode == "posids":
+        pos = (np.arange(w.tokens) * 7 % 300 + 11).astype(np.int32)
+        pos[3] = pos[150]       # repeated positions
+        lay = m.Layout.bshd(w.batch, w.seqlen, position_ids=torch.from_numpy(pos).cuda())
+        n_pos = 400
+    cos, sin = m.muse_rope_cos_sin(w.theta, w.head_dim, n_pos)
+    qa, ka, qra, kra = m.muse_qk_norm_rope(case.params, lay, case.q, case.k, case.q_gain, case.k_gain,
+                                           cos, sin, want_rstd=True)
+    sentinel = float("nan")
+    cos_t = torch.full_like(cos, sentinel)
+    sin_t = torch.full_like(sin, sentinel)
+    qb, kb, qrb, krb, _, _ = m.muse_qk_norm_rope_table(case.params, lay, case.q, case.k, case.q_gain,
+                                                       case.k_gain, theta=w.theta, n_pos=n_pos,
+                                                       cos_out=cos_t, sin_out=sin_t, want_rstd=True)
+    torch.cuda.synchronize()
+    assert torch.equal(qa.view(torch.int16), qb.view(torch.int16))
+    assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
+    assert torch.equal(qra, qrb) and torch.equal(kra, krb)
+    if pos_mode == "posids":
+        rows = np.unique(pos)
+    else:
+        rows = np.arange(w.max_seqlen)
+    written = np.zeros(n_pos, dtype=bool)
+    written[rows] = True
+    ct, st = cos_t.cpu(), sin_t.cpu()
+    assert torch.equal(ct[written], cos.cpu()[written]) and torch.equal(st[written], sin.cpu()[written])
+    assert torch.isnan(ct[~written]).all() and torch.isnan(st[~written]).all()
+    # K only (the attention step's form), then the fused attention reads the table
+    cos_k = torch.full_like(cos, sentinel)
+    sin_k = torch.full_like(sin, sentinel)
+    _, kc, _, _, _, _ = m.muse_qk_norm_rope_table(case.params, lay, None, case.k, None, case.k_gain,
+                                                  theta=w.theta, n_pos=n_pos, cos_out=cos_k, sin_out=sin_k)
+    o1, _ = m.muse_attn_fused_fwd(case.params, lay, case.q, ka, case.v, case.gate, case.q_gain, cos, sin)
+    o2, _ = m.muse_attn_fused_fwd(case.params, lay, case.q, kc, case.v, case.gate, case.q_gain, cos_k, sin_k)
+    torch.cuda.synchronize()
+    assert torch.equal(kc.view(torch.int16), ka.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 # ---------------------------------------------------------------- edge cases
 
 def test_empty_inputs_are_noops():
