@@ -445,13 +445,6 @@ namespace {
 constexpr size_t kWsAlign = 256;
 size_t ws_round(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-// The FP32 rotation is the only one with a backward here.
-muse_status check_bwd_params(const muse_attn_params *p) {
-  if (p->use_rope && !p->upcast_rope)
-    return set_error(MUSE_ERR_UNSUPPORTED, "the backward of the Q/K-dtype rotation (upcast_rope = 0) is not built");
-  return MUSE_OK;
-}
-
 size_t qk_bwd_partial_bytes(const Geometry &g, bool q_gain, bool k_gain) {
   int32_t qb = 0, kb = 0;
   qk_norm_bwd_blocks(g.d, g.n_tokens * g.hq, g.n_tokens * g.hkv, &qb, &kb);
@@ -599,7 +592,6 @@ extern "C" muse_status muse_qk_norm_rope_bwd(const muse_attn_params *p, const mu
                                              void *workspace, size_t workspace_bytes, void *stream) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
-  if ((s = check_bwd_params(p)) != MUSE_OK) return s;
   Geometry g;
   s = check_layout(l, p, (hipStream_t)stream, &g);
   if (s != MUSE_OK) return s;
@@ -654,6 +646,7 @@ extern "C" muse_status muse_qk_norm_rope_bwd(const muse_attn_params *p, const mu
   a.gain_center = p->gain_center;
   a.query_scale = p->query_scale;
   a.use_rope = p->use_rope ? 1 : 0;
+  a.rope_v2 = p->upcast_rope ? 0 : 1;
   a.skip_norm = p->skip_qk_norm ? 1 : 0;
   a.lay = token_layout(l, g);
   return device_status(launch_qk_norm_rope_bwd(g.d, a, (hipStream_t)stream), "qk_norm_rope_bwd launch");
@@ -680,7 +673,6 @@ extern "C" muse_status muse_attn_core_bwd(const muse_attn_params *p, const muse_
                                           size_t workspace_bytes, void *stream) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
-  if ((s = check_bwd_params(p)) != MUSE_OK) return s;
   if (p->skip_qk_norm) return set_error(MUSE_ERR_UNSUPPORTED, "the core normalises Q/K; skip_qk_norm is for muse_qk_norm_rope_bwd");
   Geometry g;
   s = check_layout(l, p, (hipStream_t)stream, &g);

@@ -199,9 +199,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) 
   bf16x8 qf[KS], dof[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const uint4 zq = make_uint4(0, 0, 0, 0);
-    qf[ks] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4 *>(a.q + qrow + ks * 16 + g * 8) : zq);
-    dof[ks] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4 *>(a.d_o + qrow + ks * 16 + g * 8) : zq);
+    // qrow always addresses a real row (row 0 of the segment for an idle
+    // column): load, then select against a constant (a select between two
+    // addresses would put the zero in scratch and make both loads flat)
+    const uint4 rq = *reinterpret_cast<const uint4 *>(a.q + qrow + ks * 16 + g * 8);
+    const uint4 ro = *reinterpret_cast<const uint4 *>(a.d_o + qrow + ks * 16 + g * 8);
+    qf[ks] = __builtin_bit_cast(bf16x8, qvalid ? rq : make_uint4(0, 0, 0, 0));
+    dof[ks] = __builtin_bit_cast(bf16x8, qvalid ? ro : make_uint4(0, 0, 0, 0));
   }
   const float lse2 = qvalid ? a.lse[lrow] * kLog2e : 0.0f;
   const float dlt = qvalid ? a.delta[lrow] : 0.0f;
@@ -366,9 +370,11 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
   bf16x8 kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    kf[ks] = __builtin_bit_cast(bf16x8, kin ? *reinterpret_cast<const uint4 *>(a.k + krow + ks * 16 + g * 8) : z);
-    vf[ks] = __builtin_bit_cast(bf16x8, kin ? *reinterpret_cast<const uint4 *>(a.v + krow + ks * 16 + g * 8) : z);
+    // krow always addresses a real row (row 0 of the segment past its end)
+    const uint4 rk = *reinterpret_cast<const uint4 *>(a.k + krow + ks * 16 + g * 8);
+    const uint4 rv = *reinterpret_cast<const uint4 *>(a.v + krow + ks * 16 + g * 8);
+    kf[ks] = __builtin_bit_cast(bf16x8, kin ? rk : make_uint4(0, 0, 0, 0));
+    vf[ks] = __builtin_bit_cast(bf16x8, kin ? rv : make_uint4(0, 0, 0, 0));
   }
   bool kpad = false;
   if constexpr (PAD) kpad = kin && a.key_valid[s0 + key] == 0;

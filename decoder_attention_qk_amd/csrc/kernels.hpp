@@ -97,6 +97,7 @@ struct QkNormBwdArgs {
   int32_t q_blocks, k_blocks;       // set by the launcher
   float eps, gain_center, query_scale;
   int32_t use_rope, skip_norm;
+  int32_t rope_v2;                  // the forward rotated with bf16 cos/sin (upcast_rope == 0)
   TokenLayout lay;
 };
 

@@ -93,8 +93,9 @@ __global__ __launch_bounds__(kThreads) void out_norm_gate_bwd_kernel(OutGateBwdA
 }
 
 // ---------------------------------------------------------------------------
-// ROPE: rotate the gradient back; QS: query_scale != 1; NORM: false for the
-// norm-free (vision) rotation.
+// ROPE: rotate the gradient back (the transpose of the forward's rotation:
+// FP32 cos/sin, or their bf16 casts after the Q/K-dtype rotation); QS:
+// query_scale != 1; NORM: false for the norm-free (vision) rotation.
 template <int D, bool ROPE, bool QS, bool NORM>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_bwd_kernel(QkNormBwdArgs a) {
   constexpr int LPR = D / 8;
@@ -150,7 +151,16 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_bwd_kernel(QkNormBwdArg
         const int p = rope_position(a.lay, t, a.n_pos);
         const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)p * (D / 2) + c * 4);
         const float4 sv = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)p * (D / 2) + c * 4);
-        const float cs[4] = {cv.x, cv.y, cv.z, cv.w}, sn[4] = {sv.x, sv.y, sv.z, sv.w};
+        float cs[4] = {cv.x, cv.y, cv.z, cv.w}, sn[4] = {sv.x, sv.y, sv.z, sv.w};
+        if (a.rope_v2) {
+          // the Q/K-dtype rotation multiplied by bf16 cos/sin; its bf16 product
+          // and sum roundings are differentiated as the identity
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            cs[i] = round_bf16(cs[i]);
+            sn[i] = round_bf16(sn[i]);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float d0 = dx[2 * i], d1 = dx[2 * i + 1];

@@ -318,8 +318,10 @@ muse_status muse_attn_fused_fwd(const muse_attn_params *params, const muse_layou
  *
  * The gradients of the forward stages above, each following autograd's
  * dtypes: a gradient of a bf16 tensor is bf16, gain gradients are fp32.
- * The rotation's backward is built for the FP32 rotation only
- * (upcast_rope = 0 with use_rope returns UNSUPPORTED).  Entry points that
+ * The rotation's backward is its transpose: by the FP32 cos/sin, or, after
+ * the Q/K-dtype rotation (upcast_rope = 0), by their bf16 casts (the bf16
+ * roundings of its products and sums differentiated as the identity).
+ * Entry points that
  * need scratch memory take a caller-owned workspace (16-byte aligned, at
  * least the size the matching *_workspace_size call reports); its contents
  * are overwritten, and calls that share a workspace must not overlap in time.
@@ -364,7 +366,8 @@ muse_status muse_gqa_attn_bwd(const muse_attn_params *params, const muse_layout 
 
 /*
  * Backward of muse_qk_norm_rope.  For each row: g = the FP32 inverse rotation
- * of the incoming gradient, (g0 C + g1 S, -g0 S + g1 C), rounded to bf16;
+ * of the incoming gradient, (g0 C + g1 S, -g0 S + g1 C), rounded to bf16
+ * (C, S = bf16(cos), bf16(sin) when upcast_rope = 0);
  * for Q, g = bf16(g * query_scale); then with x the raw input, r its rstd and
  * w = gain_center + gain (1 without a gain), u = g w:
  *   dx = bf16(r u - r^3 x mean(u x)),  dgain += g x r  (summed over all rows, fp32).
@@ -374,7 +377,7 @@ muse_status muse_gqa_attn_bwd(const muse_attn_params *params, const muse_layout 
  * [D] out, given exactly when the matching gain is (for one gain shared by
  * Q and K, its gradient is dq_gain + dk_gain); cos/sin as in the forward.
  * workspace: muse_qk_norm_rope_bwd_workspace_size bytes (gain partial sums).
- * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}, upcast_rope = 0), DEVICE.
+ * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}), DEVICE.
  */
 muse_status muse_qk_norm_rope_bwd(const muse_attn_params *params, const muse_layout *layout,
                                   const void *q, const void *k, const float *q_gain,
@@ -396,8 +399,7 @@ muse_status muse_qk_norm_rope_bwd_workspace_size(const muse_attn_params *params,
  * Outputs: dq [N, Hq, D], dk, dv [N, Hkv, D], dgate [N, Hq, D] bf16;
  * dq_gain, dk_gain fp32 [D] (given exactly when the matching gain is).
  * workspace: muse_attn_core_bwd_workspace_size bytes.
- * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}, upcast_rope = 0 with
- * use_rope, skip_qk_norm), DEVICE.
+ * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}, skip_qk_norm), DEVICE.
  */
 muse_status muse_attn_core_bwd(const muse_attn_params *params, const muse_layout *layout,
                                const void *q, const void *k, const void *v, const void *gate,

@@ -38,10 +38,15 @@ is visible to no query, and a query left with no visible key gives the zero
 row with lse = -inf; bf16 boundary on the attention output;
 sigmoid and output norm in full precision with one final cast; the vision
 2-D table gives the first half of the pairs the patch row and the second
-half the patch column.
+half the patch column; the backward (written from the chain rule of these
+definitions) takes the delta of the softmax correction from the stored bf16
+output, and differentiates the Q/K-dtype rotation as the transpose of the
+rotation by its bf16 cos/sin (its bf16 roundings as the identity).
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
-forms, library routines or brute force; none is "parity unpinned".
+Every function here is pinned by ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_bwd_pins.py`` against closed forms, library routines,
+torch autograd of an independent float64 forward, finite differences or
+brute force; none is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -577,9 +582,18 @@ def attention_bwd(q_hat, k_hat, v, d_o, segments: Segments, *, window=0, scaling
     return out + (dqa, dka, dva) if mags else out
 
 
-def rope_rotate_bwd(dy, cos, sin):
-    """Transpose of the FP32 rotation: each pair's gradient rotated back,
-    (dy0 C + dy1 S, -dy0 S + dy1 C), unrounded."""
+def rope_rotate_bwd(dy, cos, sin, upcast: bool = True):
+    """Transpose of the rotation: each pair's gradient rotated back,
+    (dy0 C + dy1 S, -dy0 S + dy1 C), unrounded.
+
+    upcast=False (the Q/K-dtype rotation): C and S are the bf16 casts the
+    forward rotates with, and the bf16 roundings of its products and sums are
+    taken as the identity (their derivative almost everywhere), so the
+    gradient is the transpose of the rotation by bf16(C), bf16(S).
+    """
+    if not upcast:
+        cos = round_bf16(np.asarray(cos, dtype=np.float64))
+        sin = round_bf16(np.asarray(sin, dtype=np.float64))
     dy = np.asarray(dy, dtype=np.float64)
     d0, d1 = dy[..., 0::2], dy[..., 1::2]
     dx = np.empty_like(dy)
@@ -610,16 +624,18 @@ def rms_norm_bwd(x, dy, eps, gain=None, gain_center=1.0):
 
 
 def qk_norm_rope_bwd(q, k, dq_hat, dk_hat, *, eps, q_gain=None, k_gain=None, gain_center=1.0,
-                     query_scale=1.0, use_rope=True, cos=None, sin=None, normalize=True, rnd=True):
-    """Gradients through _qk_norm_rope_core (FP32 rotation): returns
-    (dq, dk, dq_gain, dk_gain).  ``cos``/``sin`` are the per-token rows [N, D/2]."""
+                     query_scale=1.0, use_rope=True, cos=None, sin=None, normalize=True, rnd=True,
+                     upcast_rope=True):
+    """Gradients through _qk_norm_rope_core: returns (dq, dk, dq_gain, dk_gain).
+    ``cos``/``sin`` are the per-token rows [N, D/2]; upcast_rope as rope_rotate_bwd's
+    upcast."""
     dq1 = np.asarray(dq_hat, dtype=np.float64)
     dk1 = np.asarray(dk_hat, dtype=np.float64)
     if use_rope:
         c = np.asarray(cos, dtype=np.float64)[:, None, :]
         s = np.asarray(sin, dtype=np.float64)[:, None, :]
-        dq1 = _maybe_bf16(rope_rotate_bwd(dq1, c, s), rnd)
-        dk1 = _maybe_bf16(rope_rotate_bwd(dk1, c, s), rnd)
+        dq1 = _maybe_bf16(rope_rotate_bwd(dq1, c, s, upcast_rope), rnd)
+        dk1 = _maybe_bf16(rope_rotate_bwd(dk1, c, s, upcast_rope), rnd)
     dq1 = _maybe_bf16(dq1 * np.float64(round_f32(query_scale)), rnd)
     if not normalize:
         return dq1, dk1, None, None
@@ -630,8 +646,10 @@ def qk_norm_rope_bwd(q, k, dq_hat, dk_hat, *, eps, q_gain=None, k_gain=None, gai
 
 def attn_core_bwd(q, k, v, gate, dout, segments: Segments, *, theta, eps, out_eps, scaling,
                   window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
-                  query_scale=1.0, position_ids=None, causal=True, key_valid=None, rnd=True):
-    """The whole backward: recomputes the forward (FP32 rotation), then returns a dict
+                  query_scale=1.0, position_ids=None, causal=True, key_valid=None, rnd=True,
+                  upcast_rope=True):
+    """The whole backward: recomputes the forward (with the rotation upcast_rope
+    selects; the Q/K-dtype one differentiated as rope_rotate_bwd states), then returns a dict
     with dq, dk, dv, dgate (bf16 values when rnd), dq_gain, dk_gain, and the forward's
     o and lse, plus the intermediate d_o, dq_hat and dk_hat.
 
@@ -645,27 +663,30 @@ def attn_core_bwd(q, k, v, gate, dout, segments: Segments, *, theta, eps, out_ep
         fw = attn_core(q, k, v, gate, segments, theta=theta, eps=eps, out_eps=out_eps,
                        scaling=scaling, window=window, use_rope=use_rope, q_gain=q_gain,
                        k_gain=k_gain, gain_center=gain_center, query_scale=query_scale,
-                       position_ids=position_ids, causal=causal, key_valid=key_valid)
+                       position_ids=position_ids, causal=causal, key_valid=key_valid,
+                       upcast_rope=upcast_rope)
         q_hat, k_hat, o, lse = fw["q_hat"], fw["k_hat"], fw["o"], fw["lse"]
     else:
         q_hat, k_hat, o, lse = _exact_forward(q, k, v, segments, eps=eps, scaling=scaling,
                                               window=window, use_rope=use_rope, cos=cos, sin=sin,
                                               q_gain=q_gain, k_gain=k_gain, gain_center=gain_center,
                                               query_scale=query_scale, causal=causal,
-                                              key_valid=key_valid)
+                                              key_valid=key_valid, upcast_rope=upcast_rope)
     d_o, dgate = out_norm_gate_bwd(o, gate, dout, out_eps, rnd)
     dq_hat, dk_hat, dv = attention_bwd(q_hat, k_hat, v, d_o, segments, window=window, scaling=scaling,
                                        causal=causal, key_valid=key_valid, rnd=rnd, o=o if rnd else None)
     dq, dk, dqg, dkg = qk_norm_rope_bwd(q, k, dq_hat, dk_hat, eps=eps, q_gain=q_gain, k_gain=k_gain,
                                         gain_center=gain_center, query_scale=query_scale,
-                                        use_rope=use_rope, cos=cos, sin=sin, rnd=rnd)
+                                        use_rope=use_rope, cos=cos, sin=sin, rnd=rnd,
+                                        upcast_rope=upcast_rope)
     return dict(dq=dq, dk=dk, dv=dv, dgate=dgate, dq_gain=dqg, dk_gain=dkg, o=o, lse=lse,
                 d_o=d_o, dq_hat=dq_hat, dk_hat=dk_hat)
 
 
 def _exact_forward(q, k, v, segments, *, eps, scaling, window, use_rope, cos, sin, q_gain, k_gain,
-                   gain_center, query_scale, causal, key_valid):
-    """The forward with no rounding anywhere (for the exact-derivative mode)."""
+                   gain_center, query_scale, causal, key_valid, upcast_rope=True):
+    """The forward with no rounding anywhere (for the exact-derivative mode); the
+    Q/K-dtype rotation keeps only its bf16 cos/sin (the rotation it applies)."""
     def norm(x, gain):
         y, _ = rms_normalize(x, eps)
         if gain is not None:
@@ -675,6 +696,8 @@ def _exact_forward(q, k, v, segments, *, eps, scaling, window, use_rope, cos, si
     def rot(x):
         c = np.asarray(cos, dtype=np.float64)[:, None, :]
         s = np.asarray(sin, dtype=np.float64)[:, None, :]
+        if not upcast_rope:
+            c, s = round_bf16(c), round_bf16(s)
         y = np.empty_like(x)
         y[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
         y[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c

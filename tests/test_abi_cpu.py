@@ -240,7 +240,7 @@ def test_backward_argument_rules():
     assert core(wsb=need - 1) == 1                         # too small
     assert "workspace" in lib.muse_last_error().decode()
     assert core(ws=A[20] + 8) == 1                         # misaligned workspace
-    assert core(pp=_params(upcast_rope=0)) == 2            # no backward for the Q/K-dtype rotation
+    assert core(pp=_params(upcast_rope=0), ws=None) == 1   # the Q/K-dtype rotation passes the mode checks
     assert core(pp=_params(skip_qk_norm=1)) == 2
     # the attention backward needs every tensor
     st = lib.muse_gqa_attn_bwd(ctypes.byref(p), ctypes.byref(lay), A[0], A[1], A[2], A[3], A[4], None,

@@ -83,6 +83,9 @@ CASES = [
     dict(name="padded", bounds=[(0, 8), (8, 8)], hq=2, hkv=1, window=2, causal=True,
          valid=np.array([0, 0, 1, 1, 0, 1, 1, 1, 1, 1, 1, 0, 1, 1, 1, 1], dtype=bool), rope=True,
          gains=True, qs=1.0),
+    # the Q/K-dtype rotation: the torch side casts its own copy of the table to bf16
+    dict(name="qk_dtype_rope", bounds=[(0, 6), (6, 9)], hq=4, hkv=2, window=0, causal=True, valid=None,
+         rope=True, gains=True, qs=0.75, upcast=False),
 ]
 
 
@@ -105,7 +108,15 @@ def _inputs(case, seed, d=8):
 def _kw(case, x):
     return dict(theta=1.0e4, eps=1e-6, out_eps=1e-6, scaling=0.35, window=case["window"],
                 use_rope=case["rope"], q_gain=x["q_gain"], k_gain=x["k_gain"], query_scale=case["qs"],
-                causal=case["causal"], key_valid=case["valid"])
+                causal=case["causal"], key_valid=case["valid"], upcast_rope=case.get("upcast", True))
+
+
+def _torch_table(t, case):
+    """The table the rotation multiplies by: as given, or cast to bf16 by torch."""
+    if t is None:
+        return None
+    t = torch.tensor(t)
+    return t if case.get("upcast", True) else t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
@@ -116,8 +127,7 @@ def test_exact_backward_matches_torch_autograd(case):
          for kk, vv in x.items() if kk != "dout"}
     out = _torch_forward(t["q"], t["k"], t["v"], t["gate"], case["bounds"], eps=1e-6, out_eps=1e-6,
                          scaling=0.35, window=case["window"],
-                         cos=None if cos is None else torch.tensor(cos),
-                         sin=None if sin is None else torch.tensor(sin),
+                         cos=_torch_table(cos, case), sin=_torch_table(sin, case),
                          q_gain=t["q_gain"], k_gain=t["k_gain"], gain_center=1.0,
                          query_scale=case["qs"], causal=case["causal"], valid=case["valid"])
     (out * torch.tensor(x["dout"])).sum().backward()
@@ -130,8 +140,9 @@ def test_exact_backward_matches_torch_autograd(case):
         assert np.abs(ref[ours] - g).max() <= 1e-10 * scale, (ours, np.abs(ref[ours] - g).max(), scale)
 
 
-def test_exact_backward_matches_finite_differences():
-    case = CASES[1]
+@pytest.mark.parametrize("ci", [1, 5], ids=["fp32_rope", "qk_dtype_rope"])
+def test_exact_backward_matches_finite_differences(ci):
+    case = CASES[ci]
     x, segs, cos, sin = _inputs(case, 41)
     kw = _kw(case, x)
     ref = O.attn_core_bwd(x["q"], x["k"], x["v"], x["gate"], x["dout"], segs, rnd=False, **kw)
@@ -140,7 +151,7 @@ def test_exact_backward_matches_finite_differences():
         qh, kh, o, _ = O.muse_oracle._exact_forward(
             q, k, v, segs, eps=1e-6, scaling=0.35, window=case["window"], use_rope=True, cos=cos,
             sin=sin, q_gain=x["q_gain"], k_gain=x["k_gain"], gain_center=1.0, query_scale=case["qs"],
-            causal=True, key_valid=None)
+            causal=True, key_valid=None, upcast_rope=case.get("upcast", True))
         y, _ = O.rms_normalize(o, 1e-6)
         return float(np.sum(y / (1.0 + np.exp(-gate)) * x["dout"]))
 
@@ -231,8 +242,9 @@ def test_rope_bwd_is_the_inverse_rotation():
     np.testing.assert_array_equal(O.rope_rotate_bwd(x, c0[:, None], s0[:, None]), x)
 
 
-def test_rounded_backward_sits_near_the_exact_one():
-    case = CASES[0]
+@pytest.mark.parametrize("ci", [0, 5], ids=["fp32_rope", "qk_dtype_rope"])
+def test_rounded_backward_sits_near_the_exact_one(ci):
+    case = CASES[ci]
     x, segs, _, _ = _inputs(case, 46, d=16)
     a = O.attn_core_bwd(x["q"], x["k"], x["v"], x["gate"], x["dout"], segs, rnd=True, **_kw(case, x))
     b = O.attn_core_bwd(x["q"], x["k"], x["v"], x["gate"], x["dout"], segs, rnd=False, **_kw(case, x))

@@ -138,7 +138,21 @@ def test_attention_bwd_stage(w):
 
 @pytest.mark.parametrize("w", BWD[:5], ids=IDS[:5])
 def test_qk_norm_rope_bwd_stage(w):
-    case = make_case(w, query_scale=0.75 if w.name == "bshd_b2_s200_g4" else 1.0)
+    _qk_bwd_stage_check(make_case(w, query_scale=0.75 if w.name == "bshd_b2_s200_g4" else 1.0))
+
+
+# the Q/K-dtype rotation (upcast_rope = 0): its backward is the transpose of
+# the rotation by the bf16 cos/sin
+V2 = [BWD[1], BWD[4]]
+
+
+@pytest.mark.parametrize("w", V2, ids=[w.name for w in V2])
+def test_qk_norm_rope_bwd_stage_qk_dtype_rotation(w):
+    _qk_bwd_stage_check(make_case(w, upcast_rope=False, query_scale=0.75))
+
+
+def _qk_bwd_stage_check(case):
+    w = case.w
     dqh = dev_bf16(_grad(case, "dq_hat"))
     dkh = dev_bf16(W.draw_bf16(tuple(case.k.shape), 1.0, seed=7, workload=w.name, layer=0, tensor="dk_hat"))
     dq, dk, dqg, dkg = m.muse_qk_norm_rope_bwd(case.params, case.layout, case.q, case.k, case.q_gain,
@@ -150,7 +164,8 @@ def test_qk_norm_rope_bwd_stage(w):
         c, s = O.rope_cos_sin(w.theta, w.head_dim, case.segs.local_positions())
     rq, rk, rqg, rkg = O.qk_norm_rope_bwd(bits_f64(case.x["q"]), bits_f64(case.x["k"]), f64(dqh), f64(dkh),
                                           eps=EPS, q_gain=kw["q_gain"], k_gain=kw["k_gain"],
-                                          query_scale=kw["query_scale"], use_rope=kw["use_rope"], cos=c, sin=s)
+                                          query_scale=kw["query_scale"], use_rope=kw["use_rope"], cos=c, sin=s,
+                                          upcast_rope=kw["upcast_rope"])
     sq = check_bf16(f64(dq), rq, what="dq")
     sk = check_bf16(f64(dk), rk, what="dk")
     assert sq["exact"] > 0.99 and sk["exact"] > 0.99, (sq, sk)
@@ -161,7 +176,7 @@ def test_qk_norm_rope_bwd_stage(w):
         xn, _ = O.rms_normalize(xs, EPS)
         g = f64(dh)
         if kw["use_rope"]:
-            g = O.round_bf16(O.rope_rotate_bwd(g, c[:, None, :], s[:, None, :]))
+            g = O.round_bf16(O.rope_rotate_bwd(g, c[:, None, :], s[:, None, :], kw["upcast_rope"]))
         g = O.round_bf16(g * np.float64(np.float32(qs)))
         terms = np.abs(g * xn).reshape(-1, xs.shape[-1])
         _check_sum(f64(got), ref, terms.sum(0), "gain gradient", flip=2.0 ** -7 * terms.max(0))
@@ -169,7 +184,15 @@ def test_qk_norm_rope_bwd_stage(w):
 
 @pytest.mark.parametrize("w", BWD, ids=IDS)
 def test_core_bwd_matches_oracle(w):
-    case = make_case(w)
+    _core_bwd_check(make_case(w))
+
+
+@pytest.mark.parametrize("w", V2, ids=[w.name for w in V2])
+def test_core_bwd_qk_dtype_rotation(w):
+    _core_bwd_check(make_case(w, upcast_rope=False))
+
+
+def _core_bwd_check(case):
     dout = dev_bf16(_grad(case, "dout"))
     res = m.muse_attn_core_bwd(case.params, case.layout, case.q, case.k, case.v, case.gate, dout,
                                case.q_gain, case.k_gain, case.cos, case.sin)
@@ -183,7 +206,6 @@ def test_core_bwd_matches_oracle(w):
     for a, b in zip(res, res2):
         assert torch.equal(a, b)
     kw = case.oracle_kw()
-    kw.pop("upcast_rope")
     ref = O.attn_core_bwd(bits_f64(case.x["q"]), bits_f64(case.x["k"]), bits_f64(case.x["v"]),
                           bits_f64(case.x["gate"]), f64(dout), case.segs, **kw)
     dq, dk, dv, dgate, dqg, dkg = res
