@@ -322,8 +322,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}); this build has no "
-              "multi-GPU path", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the library has no "
+              "multi-GPU path; each GPU would run it on its own share of the KV heads", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
