@@ -187,6 +187,43 @@ __device__ __forceinline__ int find_segment(const TokenLayout &l, int t) {
   return lo;
 }
 
+// Positions of a run of consecutive tokens starting at t0 (wave-uniform, so
+// the segment search runs on scalar loads once per run): a token inside the
+// run's first segment needs no load at all; a later one walks forward from it
+// (a run crosses few boundaries).
+struct PosCursor {
+  int seg, start, next;   // packed layouts: t0's segment, its first token, the next segment's
+};
+
+__device__ __forceinline__ PosCursor pos_cursor(const TokenLayout &l, int t0) {
+  PosCursor c{0, 0, 0};
+  if (l.cu_seqlens && !l.position_ids) {
+    c.seg = find_segment(l, t0);
+    c.start = l.cu_seqlens[c.seg];
+    c.next = l.cu_seqlens[c.seg + 1];
+  }
+  return c;
+}
+
+// rope_position(l, t, n_pos) for a token t >= the cursor's t0.
+__device__ __forceinline__ int rope_position(const TokenLayout &l, const PosCursor &c, int t, int n_pos) {
+  int p;
+  if (l.position_ids) {
+    p = l.position_ids[t];
+  } else if (l.cu_seqlens) {
+    if (t < c.next) {
+      p = t - c.start;
+    } else {
+      int seg = c.seg + 1;
+      while (seg + 1 < l.num_segments && l.cu_seqlens[seg + 1] <= t) ++seg;
+      p = t - l.cu_seqlens[seg];
+    }
+  } else {
+    p = (int)l.seqlen_div.mod((uint32_t)t);
+  }
+  return p < 0 ? 0 : (p >= n_pos ? n_pos - 1 : p);
+}
+
 __device__ __forceinline__ int rope_position(const TokenLayout &l, int t, int n_pos) {
   int p;
   if (l.position_ids) {

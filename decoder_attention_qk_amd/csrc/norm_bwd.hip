@@ -141,6 +141,9 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_bwd_kernel(QkNormBwdArg
         gin[j] = *reinterpret_cast<const uint4 *>(gsrc + (int64_t)r * D + c * 8);
       }
     }
+    // the group's rows are consecutive: one segment search per group
+    PosCursor pc{0, 0, 0};
+    if constexpr (ROPE) pc = pos_cursor(a.lay, (int)hdiv.div((uint32_t)(grp * RPP)));
 #pragma unroll
     for (int j = 0; j < kQkRows; ++j) {
       const int r = (grp + j) * RPP + rsub;
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_bwd_kernel(QkNormBwdArg
       unpack8(gin[j], dx);
       if constexpr (ROPE) {
         const int t = (int)hdiv.div((uint32_t)min(r, nrows - 1));
-        const int p = rope_position(a.lay, t, a.n_pos);
+        const int p = rope_position(a.lay, pc, t, a.n_pos);
         const float4 cv = *reinterpret_cast<const float4 *>(a.cos_tab + (int64_t)p * (D / 2) + c * 4);
         const float4 sv = *reinterpret_cast<const float4 *>(a.sin_tab + (int64_t)p * (D / 2) + c * 4);
         float cs[4] = {cv.x, cv.y, cv.z, cv.w}, sn[4] = {sv.x, sv.y, sv.z, sv.w};

@@ -86,11 +86,12 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
     t_first = (int)hdiv.div((uint32_t)r0);
     const int n = ((int)hdiv.div((uint32_t)r1) - t_first + 1) * HALF;
     for (int i = threadIdx.x; i < HALF; i += kThreads) inv_freq[i] = rope_inv_freq(a.theta, i, D);
+    const PosCursor pc = pos_cursor(a.lay, t_first);
     __syncthreads();
     for (int idx = threadIdx.x; idx < n; idx += kThreads) {
       const int t = t_first + idx / HALF;
       const int i = idx % HALF;
-      const int p = rope_position(a.lay, t, a.n_pos);
+      const int p = rope_position(a.lay, pc, t, a.n_pos);
       float cv, sv;
       rope_cos_sin(p, inv_freq[i], cv, sv);   // = rope_entry(a.theta, i, D, p, ...)
       tab[idx] = cv;
@@ -101,32 +102,19 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(QkNormArgs a) {
     __syncthreads();
   }
 
-  // RoPE positions of this thread's rows (tokens increase with j; a packed
-  // layout walks its segments forward from the first row's); in table mode
-  // the row's token instead (its LDS row)
+  // RoPE positions of this thread's rows; in table mode the row's token
+  // instead (its LDS row).  The block's rows are consecutive, so a packed
+  // layout's segment search runs once per block (pos_cursor).
   int pos[kRowsInFlight];
   if constexpr (TAB) {
 #pragma unroll
     for (int j = 0; j < kRowsInFlight; ++j)
       pos[j] = (int)hdiv.div((uint32_t)min(base + j * RPP, nrows - 1)) - t_first;
   } else if constexpr (ROPE != 0) {
-    int seg = -1;
+    const PosCursor pc = pos_cursor(a.lay, (int)hdiv.div((uint32_t)(blk * RPB)));
 #pragma unroll
-    for (int j = 0; j < kRowsInFlight; ++j) {
-      const int r = min(base + j * RPP, nrows - 1);
-      const int t = (int)hdiv.div((uint32_t)r);
-      int p;
-      if (a.lay.position_ids) {
-        p = a.lay.position_ids[t];
-      } else if (a.lay.cu_seqlens) {
-        if (seg < 0) seg = find_segment(a.lay, t);
-        while (seg + 1 < a.lay.num_segments && a.lay.cu_seqlens[seg + 1] <= t) ++seg;
-        p = t - a.lay.cu_seqlens[seg];
-      } else {
-        p = (int)a.lay.seqlen_div.mod((uint32_t)t);
-      }
-      pos[j] = p < 0 ? 0 : (p >= a.n_pos ? a.n_pos - 1 : p);
-    }
+    for (int j = 0; j < kRowsInFlight; ++j)
+      pos[j] = rope_position(a.lay, pc, (int)hdiv.div((uint32_t)min(base + j * RPP, nrows - 1)), a.n_pos);
   }
 
 #pragma unroll
