@@ -26,11 +26,24 @@ FULL = [
 ]
 
 
+# sequences past the configurations' 32k: positions, window bounds, table rows
+# and tile offsets at their largest values
+LONG = {
+    "bshd_1x131072_h8kv1_d128": W.small_workload("bshd_1x131072_h8kv1_d128", num_heads=8, num_kv_heads=1,
+                                                 head_dim=128, seqlen=131072, theta=5.0e5),
+    "thd_2seg_long_h8kv2_d128_w70000": W.small_workload("thd_2seg_long_h8kv2_d128_w70000", num_heads=8,
+                                                        num_kv_heads=2, head_dim=128,
+                                                        segment_lengths=(100000, 31072), window=70000,
+                                                        theta=5.0e5),
+}
+FULL += [(n, 0) for n in LONG]
+
+
 @pytest.mark.parametrize("name,layer", FULL, ids=[f"{n}-L{l}" for n, l in FULL])
 def test_full_size_sampled_rows(name, layer):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    w = W.WORKLOADS[name]
+    w = LONG[name] if name in LONG else W.WORKLOADS[name]
     print(f"[full] {name} layer {layer}", flush=True)
     case = make_case(w, layer)
     out, k_hat, lse = m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v,
