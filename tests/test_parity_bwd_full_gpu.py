@@ -25,6 +25,14 @@ FULL = [
     ("bshd_1x32768_h64kv8_d128_mix", 0),
     ("bshd_1x32768_h64kv8_d128_mix", 3),
 ]
+# a sequence past the configurations' 32k (positions and tile offsets at their
+# largest); the window keeps the oracle's per-key and per-row sums short
+LONG = {
+    "bshd_1x131072_h8kv2_d128_w2048": W.small_workload("bshd_1x131072_h8kv2_d128_w2048", num_heads=8,
+                                                       num_kv_heads=2, head_dim=128, seqlen=131072,
+                                                       window=2048, theta=5.0e5),
+}
+FULL += [(n, 0) for n in LONG]
 
 
 def _keys(segs, window, rng, n_random=4):
@@ -46,7 +54,7 @@ def _keys(segs, window, rng, n_random=4):
 def test_full_size_attention_bwd_sampled(name, layer):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    w = W.WORKLOADS[name]
+    w = LONG[name] if name in LONG else W.WORKLOADS[name]
     print(f"[full bwd] {name} layer {layer}", flush=True)
     case = make_case(w, layer)
     p, lay = case.params, case.layout
