@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--kv-split", type=int, default=0,
+                    help="attention KV-split policy: 0 automatic, 1 never, n >= 2 n parts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage (unfused) measurements")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurements")
@@ -330,7 +332,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    import decoder_attention_qk_amd as m
     w = W.WORKLOADS[args.workload]
+    m.muse_attn_set_kv_split(args.kv_split)
     b = Bench(w)
     if args.calibrate_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=b.dev)   # 256 MiB
@@ -387,6 +391,8 @@ def main():
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "layers": [{"sliding_window": t["window"], "use_rope": bool(t["params"].use_rope)} for t in b.layers],
             "flop_per_step_causal": flop_step,
+            "share_of": W.SHARE_OF.get(w.name),
+            "kv_split_policy": args.kv_split,
         },
         "roofline": {
             "bound": "mfma", "kernel": "attn_fwd_kernel<128,fused>" if w.head_dim == 128 else "attn_fwd_kernel<64,fused>",

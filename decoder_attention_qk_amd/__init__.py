@@ -21,7 +21,7 @@ __all__ = [
     "muse_gqa_attn_fwd", "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd",
     "muse_attn_bwd_delta", "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd",
     "muse_qk_norm_rope_bwd_workspace_size", "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size",
-    "muse_validate_cu_seqlens", "muse_status_string", "muse_version",
+    "muse_validate_cu_seqlens", "muse_attn_set_kv_split", "muse_status_string", "muse_version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +35,7 @@ symbols = (
     "muse_gqa_attn_fwd", "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd", "muse_attn_bwd_delta",
     "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd", "muse_qk_norm_rope_bwd_workspace_size",
     "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size", "muse_validate_cu_seqlens",
-    "muse_status_string", "muse_last_error", "muse_version",
+    "muse_attn_set_kv_split", "muse_status_string", "muse_last_error", "muse_version",
 )
 
 
@@ -83,6 +83,7 @@ _SIGS = {
                            _P, _P, ctypes.c_size_t, _P],
     "muse_attn_core_bwd_workspace_size": [_P, _P, _P],
     "muse_validate_cu_seqlens": [_P, _I32, _I32, _I32],
+    "muse_attn_set_kv_split": [_I32],
     "muse_status_string": [ctypes.c_int],
     "muse_last_error": [],
     "muse_version": [],
@@ -126,6 +127,12 @@ def muse_status_string(status: int) -> str:
 
 def muse_version() -> str:
     return library().muse_version().decode()
+
+
+def muse_attn_set_kv_split(mode: int) -> int:
+    """Sets the attention forward's KV-split policy (0 automatic, 1 never,
+    n >= 2 n parts); returns the previous one."""
+    return int(library().muse_attn_set_kv_split(int(mode)))
 
 
 # ---------------------------------------------------------------- parameters

@@ -3,10 +3,13 @@
 // per-thread error message.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "host_util.hpp"
@@ -195,11 +198,142 @@ AttnArgs attn_args(const muse_attn_params *p, const muse_layout *l, const Geomet
   a.bidirectional = p->bidirectional ? 1 : 0;
   a.key_valid = g.thd ? nullptr : l->attention_mask;
   a.q_blocks = (g.maxlen + a.tok_per_wg - 1) / a.tok_per_wg;
+  a.kv_parts = 1;
   a.lay = token_layout(l, g);
   return a;
 }
 
 int64_t bf16_bytes(int64_t n, int h, int d) { return n * h * d * 2; }
+
+// ---- KV split of the attention forward (flash-decoding style).  A grid
+// with fewer than two work items per CU leaves CUs idle and lets its longest
+// items (the last query blocks of a causal sequence) set the kernel's length;
+// then each item's key tiles are cut into parts of kv_span tiles run by
+// separate workgroups, combined per wave by the last part to finish.  The plan
+// depends only on the shape and the device's CU count, so the fused and
+// unfused kernels take the same one (and stay bitwise equal).
+
+std::atomic<int> g_kv_split{0};   // 0 automatic, 1 never, n >= 2: n parts whenever an item has 2+ tiles
+
+int device_cus(int dev) {
+  static std::atomic<int> cache[64];
+  if (dev < 0 || dev >= 64) return 0;
+  int c = cache[dev].load();
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return 0;
+  cache[dev].store(c);
+  return c;
+}
+
+// The heaviest work item's tile count (the kernel's own tile range for each
+// query block of the longest segment).
+int max_item_tiles(const AttnArgs &a, int maxlen) {
+  const int bn = attn_keys_per_tile();
+  int best = 0;
+  for (int qb = 0; qb < a.q_blocks; ++qb) {
+    const int q0 = qb * a.tok_per_wg;
+    if (q0 >= maxlen) break;
+    const int q1 = std::min(q0 + a.tok_per_wg, maxlen);
+    const int lo = a.window > 0 && !a.bidirectional ? std::max(0, q0 - a.window + 1) : 0;
+    const int hi = (a.bidirectional ? maxlen : q1) - 1;
+    best = std::max(best, hi / bn - lo / bn + 1);
+  }
+  return best;
+}
+
+// Grow-only device buffers per (device, stream): calls on one stream run in
+// order, so they can share one; calls on different streams get their own.
+struct SplitWs {
+  int dev;
+  hipStream_t stream;
+  void *cnt = nullptr;   // arrival counters, zero between launches
+  size_t cnt_bytes = 0;
+  void *part = nullptr;  // partial O and (max, sum) rows, no initial value needed
+  size_t part_bytes = 0;
+};
+std::mutex g_ws_mu;
+std::vector<SplitWs> g_ws;
+
+muse_status split_buffers(hipStream_t stream, size_t cnt_bytes, size_t part_bytes, void **cnt, void **part) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return set_error(MUSE_ERR_DEVICE, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  SplitWs *w = nullptr;
+  for (SplitWs &x : g_ws)
+    if (x.dev == dev && x.stream == stream) w = &x;
+  if (!w) {
+    g_ws.push_back(SplitWs{dev, stream});
+    w = &g_ws.back();
+  }
+  if (w->cnt_bytes < cnt_bytes || w->part_bytes < part_bytes) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+      return set_error(MUSE_ERR_UNSUPPORTED,
+                       "the KV-split workspace of this stream must grow (%zu + %zu bytes); make one call of "
+                       "this shape outside graph capture first",
+                       cnt_bytes, part_bytes);
+    // earlier launches on this stream may still use the old buffers
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return device_status(e, "KV-split workspace");
+    if (w->cnt_bytes < cnt_bytes) {
+      if (w->cnt) (void)hipFree(w->cnt);
+      w->cnt = nullptr;
+      w->cnt_bytes = 0;
+      if ((e = hipMalloc(&w->cnt, cnt_bytes)) != hipSuccess) return device_status(e, "KV-split counters");
+      if ((e = hipMemset(w->cnt, 0, cnt_bytes)) != hipSuccess) return device_status(e, "KV-split counters");
+      w->cnt_bytes = cnt_bytes;
+    }
+    if (w->part_bytes < part_bytes) {
+      if (w->part) (void)hipFree(w->part);
+      w->part = nullptr;
+      w->part_bytes = 0;
+      if ((e = hipMalloc(&w->part, part_bytes)) != hipSuccess) return device_status(e, "KV-split partials");
+      w->part_bytes = part_bytes;
+    }
+  }
+  *cnt = w->cnt;
+  *part = w->part;
+  return MUSE_OK;
+}
+
+// Plans the split for a, and when there is one, points a at its buffers.
+muse_status attn_split(AttnArgs &a, const Geometry &g, hipStream_t stream) {
+  a.kv_parts = 1;
+  a.kv_span = 0;
+  const int mode = g_kv_split.load();
+  if (mode == 1) return MUSE_OK;
+  const int64_t items = (int64_t)a.q_blocks * g.nseg * a.hkv * a.head_chunks;
+  const int tiles = max_item_tiles(a, g.maxlen);
+  int parts = 1;
+  if (mode >= 2) {
+    parts = std::min(std::min(mode, tiles), kMaxKvParts);
+  } else {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MUSE_OK;
+    const int cus = device_cus(dev);
+    if (cus <= 0 || items >= 2 * (int64_t)cus) return MUSE_OK;
+    // about three workgroups per CU; parts of at least 4 tiles, so a part's
+    // prologue stays small beside its tile loop
+    parts = (int)std::min<int64_t>(4, (3 * (int64_t)cus + items - 1) / items);
+    parts = std::min(parts, tiles / 4);
+  }
+  if (parts < 2) return MUSE_OK;
+  const int span = (tiles + parts - 1) / parts;
+  parts = (tiles + span - 1) / span;
+  if (parts < 2) return MUSE_OK;
+  const int nw = attn_waves_per_workgroup();
+  const size_t slots = (size_t)items * parts * nw;
+  // per slot and lane: the wave's O fragment (D/32 tiles of 16) plus reference and sum
+  const size_t slot_bytes = (size_t)(g.d / 32 * 16 + 2) * 64 * sizeof(float);
+  void *cnt = nullptr, *part = nullptr;
+  muse_status s = split_buffers(stream, (size_t)items * nw * sizeof(uint32_t), slots * slot_bytes, &cnt, &part);
+  if (s != MUSE_OK) return s;
+  a.kv_parts = parts;
+  a.kv_span = span;
+  a.part_cnt = (uint32_t *)cnt;
+  a.part_o = (float *)part;
+  return MUSE_OK;
+}
 
 }  // namespace
 }  // namespace muse
@@ -325,6 +459,11 @@ extern "C" muse_status muse_qk_norm_rope_table(const muse_attn_params *p, const 
                            stream, true, theta);
 }
 
+extern "C" int32_t muse_attn_set_kv_split(int32_t mode) {
+  if (mode < 0) return -1;
+  return g_kv_split.exchange(mode);
+}
+
 extern "C" muse_status muse_gqa_attn_fwd(const muse_attn_params *p, const muse_layout *l, const void *q_hat,
                                          const void *k_hat, const void *v, void *o, float *lse, void *stream) {
   muse_status s = check_params(p);
@@ -347,6 +486,7 @@ extern "C" muse_status muse_gqa_attn_fwd(const muse_attn_params *p, const muse_l
   a.v = (const uint16_t *)v;
   a.o = (uint16_t *)o;
   a.lse = lse;
+  if ((s = attn_split(a, g, (hipStream_t)stream)) != MUSE_OK) return s;
   return device_status(launch_attn_fwd(g.d, false, a, (hipStream_t)stream), "attention launch");
 }
 
@@ -401,6 +541,7 @@ extern "C" muse_status muse_attn_fused_fwd(const muse_attn_params *p, const muse
   a.cos_tab = cos;
   a.sin_tab = sin;
   a.n_pos = n_pos;
+  if ((s = attn_split(a, g, (hipStream_t)stream)) != MUSE_OK) return s;
   return device_status(launch_attn_fwd(g.d, true, a, (hipStream_t)stream), "fused attention launch");
 }
 

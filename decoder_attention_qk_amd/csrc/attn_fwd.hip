@@ -87,16 +87,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   const int g = lane >> 5;
 
   // ---- work item: segment-major, then query blocks in descending order
-  // (longest first), then (kv head, head chunk).  Consecutive workgroups
-  // take consecutive kv heads, so with the round-robin dispatch over the
-  // XCDs each XCD works on one (segment, kv head) pair at a time and its K/V
-  // stays in that XCD's L2.
-  const int per_seg = a.q_blocks * a.hkv * a.head_chunks;
+  // (longest first), then KV part, then (kv head, head chunk).  Consecutive
+  // workgroups take consecutive kv heads, so with the round-robin dispatch
+  // over the XCDs each XCD works on one (segment, kv head) pair at a time and
+  // its K/V stays in that XCD's L2.
+  const int heads_items = a.hkv * a.head_chunks;
+  const int per_seg = a.q_blocks * a.kv_parts * heads_items;
   const int b = blockIdx.x;
   const int seg = b / per_seg;
   int rest = b % per_seg;
-  const int qb = a.q_blocks - 1 - rest / (a.hkv * a.head_chunks);
-  rest %= a.hkv * a.head_chunks;
+  const int qb = a.q_blocks - 1 - rest / (a.kv_parts * heads_items);
+  rest %= a.kv_parts * heads_items;
+  const int part = rest / heads_items;
+  rest %= heads_items;
   const int hc = rest % a.head_chunks;
   const int kvh = rest / a.head_chunks;
 
@@ -412,8 +415,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   const int kt_lo = lo / BN;
   const int kt_hi = ((bidir ? L : q1) - 1) / BN;
   const int ntiles = kt_hi - kt_lo + 1;
+  // KV split: this part takes tiles kt_hi - it for it in [it0, it1); parts
+  // past the item's last tile have nothing to do (uniform per workgroup).
+  // The last launched part takes any remainder, so every item's parts are
+  // all launched whatever its length.
+  const int span = a.kv_parts > 1 ? a.kv_span : ntiles;
+  const int nparts = min((ntiles + span - 1) / span, a.kv_parts);
+  if (part >= nparts) return;
+  const int it0 = part * span;
+  const int it1 = part == nparts - 1 ? ntiles : it0 + span;
 
-  issue_dma(kt_hi, 0);
+  issue_dma(kt_hi - it0, 0);
   load_q();
   // The gate fragments of the epilogue (qrow always addresses a real row).
   // At D = 128 they are fetched now, so their latency is long hidden when
@@ -431,22 +443,80 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   if constexpr (FUSED && kGateEarly) load_gate();
   vmem_wait_all();
   __syncthreads();
-  for (int it = 0;;) {
+  for (int it = it0;;) {
     take_mask();
-    if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 1);
+    if (it + 1 < it1) issue_dma(kt_hi - it - 1, 1);
     compute(kt_hi - it, 0);
     vmem_wait_all();
     __syncthreads();
-    if (++it >= ntiles) break;
+    if (++it >= it1) break;
     take_mask();
-    if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 0);
+    if (it + 1 < it1) issue_dma(kt_hi - it - 1, 0);
     compute(kt_hi - it, 1);
     vmem_wait_all();
     __syncthreads();
-    if (++it >= ntiles) break;
+    if (++it >= it1) break;
   }
 
   if (!wave_active) return;
+  if (nparts > 1) {
+    // Each part publishes its wave's unnormalised O fragment and per-lane
+    // (reference, partial sum); the wave of the last part to arrive combines
+    // all parts in part order, so the result does not depend on which
+    // arrives last.  No wave waits for another.  Slot layout (floats):
+    // [O element e][lane], then [reference, sum][lane].
+    const int64_t item = (((int64_t)seg * a.q_blocks + qb) * a.hkv + kvh) * a.head_chunks + hc;
+    constexpr int SLOT = (DT * 16 + 2) * 64;
+    auto slot = [&](int p) __attribute__((always_inline)) {
+      return a.part_o + ((item * a.kv_parts + p) * NW + wave) * SLOT + lane;
+    };
+    // The slots are written and read with device-coherent (device-scope
+    // atomic) stores and loads, and a store completes only once it is visible
+    // device-wide, so waiting for this wave's stores before arriving orders
+    // them before the arrival.  Release/acquire fences would instead write
+    // back and invalidate the whole L2 of the XCD, which its other workgroups
+    // pay for in K/V refetches.
+    auto st = [&](float *p, float v) __attribute__((always_inline)) {
+      __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    {
+      float *dst = slot(part);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st(dst + (dt * 16 + i) * 64, oacc[dt][i]);
+      st(dst + DT * 16 * 64, m_run);
+      st(dst + (DT * 16 + 1) * 64, l_run);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    uint32_t prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(a.part_cnt + item * NW + wave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != (uint32_t)(nparts - 1)) return;
+    if (lane == 0) a.part_cnt[item * NW + wave] = 0u;   // zero again for the next launch
+    auto ld = [&](const float *p) __attribute__((always_inline)) {
+      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    float m_all = -INFINITY;
+    for (int p = 0; p < nparts; ++p) m_all = fmaxf(m_all, ld(slot(p) + DT * 16 * 64));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+    float l_all = 0.0f;
+    for (int p = 0; p < nparts; ++p) {
+      const float *src = slot(p);
+      const float mp = ld(src + DT * 16 * 64);
+      // a part without a reference saw no key: l = 0, O = 0
+      const float sc = mp == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mp - m_all) * c2);
+      l_all = __builtin_fmaf(sc, ld(src + (DT * 16 + 1) * 64), l_all);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] = __builtin_fmaf(sc, ld(src + (dt * 16 + i) * 64), oacc[dt][i]);
+    }
+    m_run = m_all;
+    l_run = l_all;
+  }
   if constexpr (FUSED && !kGateEarly) load_gate();
   float l_lo, l_hi;
   swap32(l_run, l_lo, l_hi);
@@ -525,10 +595,14 @@ hipError_t launch_one(const AttnArgs &a, dim3 grid, hipStream_t stream) {
 }  // namespace
 
 int attn_columns_per_workgroup() { return COLS; }
+int attn_waves_per_workgroup() { return NW; }
+int attn_keys_per_tile() { return BN; }
 
 hipError_t launch_attn_fwd(int head_dim, bool fused, const AttnArgs &a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.q_blocks * a.lay.num_segments * a.hkv * a.head_chunks;
+  const int64_t blocks = (int64_t)a.q_blocks * a.lay.num_segments * a.hkv * a.head_chunks * a.kv_parts;
   if (blocks == 0) return hipSuccess;
+  if (a.kv_parts < 1 || a.kv_parts > kMaxKvParts || (a.kv_parts > 1 && (a.kv_span < 1 || !a.part_o || !a.part_cnt)))
+    return hipErrorInvalidConfiguration;
   if (a.heads_per_wg < 1 || a.heads_per_wg > COLS || a.tok_per_wg < 1 || a.tok_per_wg * a.heads_per_wg > COLS)
     return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);

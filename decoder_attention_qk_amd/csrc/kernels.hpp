@@ -127,8 +127,17 @@ struct AttnArgs {
   int32_t bidirectional;   // every key of the segment is visible (no causal order, no window)
   const uint8_t *key_valid;  // BSHD [batch, seqlen] token validity (0 = padded key) or nullptr
   int32_t q_blocks;        // ceil(max segment length / tok_per_wg)
+  // KV split: a work item's key tiles are cut into parts of kv_span tiles,
+  // each run by its own workgroup; per wave, the last part to arrive combines
+  // them (kv_parts == 1: no split, the pointers below are unused).
+  int32_t kv_parts;        // 1 .. kMaxKvParts
+  int32_t kv_span;
+  float *part_o;           // [items][kv_parts][waves] slots: O fragment, reference, sum (per lane)
+  uint32_t *part_cnt;      // [items][waves] arrivals; zero between launches
   TokenLayout lay;
 };
+
+constexpr int kMaxKvParts = 8;
 
 // Attention backward (dQ kernel and dK/dV kernel).
 struct AttnBwdArgs {
@@ -159,6 +168,8 @@ hipError_t launch_qk_norm_rope_bwd(int head_dim, const QkNormBwdArgs &a, hipStre
 hipError_t launch_attn_bwd(int head_dim, const AttnBwdArgs &a, hipStream_t stream);
 int attn_bwd_keys_per_workgroup();
 int attn_columns_per_workgroup();  // (token, head) query columns one attention workgroup holds
+int attn_waves_per_workgroup();
+int attn_keys_per_tile();
 
 // One RoPE table entry: pair i of a head `width` wide at coordinate coord.
 // The inverse frequency theta^(-2i/width) and the cosine/sine are evaluated

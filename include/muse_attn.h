@@ -256,6 +256,16 @@ muse_status muse_qk_norm_rope_table(const muse_attn_params *params, const muse_l
  *
  * q_hat [N, Hq, D], k_hat [N, Hkv, D], v [N, Hkv, D]: bf16 in.
  * o     [N, Hq, D] bf16 out.  lse: optional fp32 [N, Hq] out (natural log).
+ *
+ * Small grids (fewer than two work items of 128 query columns per CU, e.g.
+ * one GPU's share of a head-sharded layer) split each item's keys into parts
+ * that run side by side and are combined in a fixed order (see
+ * muse_attn_set_kv_split).  Those calls use a device buffer the library keeps
+ * per (device, stream), allocated (and its counters zeroed) on the first call
+ * of a shape that needs more than it holds; that call synchronises the stream
+ * and must not be under graph capture (UNSUPPORTED).  A captured graph that
+ * takes the split path uses its capturing stream's buffer: do not replay it
+ * concurrently with other calls on that stream.
  * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}), DEVICE.
  */
 muse_status muse_gqa_attn_fwd(const muse_attn_params *params, const muse_layout *layout,
@@ -419,6 +429,20 @@ muse_status muse_attn_core_bwd_workspace_size(const muse_attn_params *params,
  */
 muse_status muse_validate_cu_seqlens(const int32_t *cu_seqlens_host, int32_t num_segments,
                                      int32_t total_tokens, int32_t max_seqlen);
+
+/*
+ * Attention-forward KV split policy (process-wide; muse_gqa_attn_fwd,
+ * muse_attn_fused_fwd, muse_attn_core_fwd and the recomputing backward):
+ *   0  automatic (default): split only grids with fewer than two work items
+ *      per CU, into at most 4 parts of at least 4 key tiles;
+ *   1  never split;
+ *   n >= 2  split every work item with two or more 64-key tiles into
+ *      min(n, 8) parts (a tuning and testing aid).
+ * Splitting reorders the sums (results move within rounding); a given policy
+ * and shape always give the same bits, fused and unfused alike.
+ * Returns the previous policy, or -1 (nothing changed) when mode < 0.
+ */
+int32_t muse_attn_set_kv_split(int32_t mode);
 
 /* Static name of a status code. */
 const char *muse_status_string(muse_status status);

@@ -24,6 +24,7 @@ FULL = [
     ("thd_16seg_h40kv8_d128", 0),
     ("bshd_1x32768_h64kv8_d128_mix", 0),
     ("bshd_1x32768_h64kv8_d128_mix", 3),
+    ("bshd_2x4096_h4kv1_d128", 0),   # one GPU's share; its forward takes the KV split
 ]
 # a sequence past the configurations' 32k (positions and tile offsets at their
 # largest); the window keeps the oracle's per-key and per-row sums short

@@ -23,6 +23,11 @@ FULL = [
     ("bshd_1x32768_h64kv8_d128_mix", 1),
     ("bshd_1x32768_h64kv8_d128_mix", 2),
     ("bshd_1x32768_h64kv8_d128_mix", 3),
+    # one GPU's share of the head-sharded layers (the 2x4096 share takes the KV split)
+    ("bshd_2x4096_h4kv1_d128", 0),
+    ("bshd_1x16384_h4kv1_d128_w4096", 0),
+    ("thd_16seg_h5kv1_d128", 0),
+    ("bshd_1x32768_h8kv1_d128_mix", 3),
 ]
 
 

@@ -1,0 +1,176 @@
+"""GPU parity of the attention forward's KV split (a work item's key tiles cut
+into parts run by separate workgroups and combined per wave in part order).
+Forced splits of small cases against the oracle, fused == unfused bitwise
+under the split, repeat runs bitwise equal (the arrival counters return to
+zero), every output row written, and the automatic split of a grid too small
+to fill the device."""
+
+import numpy as np
+import pytest
+import torch
+
+import decoder_attention_qk_amd as m
+import oracle as O
+import workloads as W
+from gpu_util import bits_f64, check_bf16, check_fp32, dev_bf16, f64, make_case
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    W.small_workload("split_bshd_b2_s700_g4", num_heads=8, num_kv_heads=2, head_dim=128, batch=2, seqlen=700),
+    W.small_workload("split_bshd_s900_g5_w300", num_heads=5, num_kv_heads=1, head_dim=128, seqlen=900,
+                     window=300),
+    W.small_workload("split_bshd_s520_g1_d64", num_heads=2, num_kv_heads=2, head_dim=64, seqlen=520),
+    W.small_workload("split_thd_g3_mixed", num_heads=6, num_kv_heads=2, head_dim=128,
+                     segment_lengths=(1, 77, 0, 600, 64, 385)),
+    W.small_workload("split_bshd_g16_d64", num_heads=16, num_kv_heads=1, head_dim=64, seqlen=450),
+]
+IDS = [w.name for w in CASES]
+MODES = [2, 3, 8]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.library()
+
+
+@pytest.fixture
+def split_mode():
+    """Sets a KV-split policy for one test and restores automatic afterwards."""
+    def set_mode(mode):
+        m.muse_attn_set_kv_split(mode)
+    yield set_mode
+    m.muse_attn_set_kv_split(0)
+
+
+def _sentinel_like(t):
+    # bf16 NaN bits: a row the kernel never writes stays NaN
+    return torch.full(t.shape, 0x7FC0, dtype=torch.int16, device=t.device).view(torch.bfloat16)
+
+
+def _q_k_hat(case, layout=None):
+    lay = layout if layout is not None else case.layout
+    q_hat, k_hat, _, _ = m.muse_qk_norm_rope(case.params, lay, case.q, case.k, case.q_gain, case.k_gain,
+                                             case.cos, case.sin)
+    return q_hat, k_hat
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_split_attention_stage(w, mode, split_mode):
+    case = make_case(w)
+    q_hat, k_hat = _q_k_hat(case)
+    split_mode(mode)
+    print(f"[split] {w.name} mode {mode}", flush=True)
+    o = _sentinel_like(q_hat)
+    o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, o=o, want_lse=True)
+    o2, lse2 = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o.float()).any()
+    ro, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs,
+                         window=case.x["window"], scaling=case.scaling)
+    check_bf16(f64(o), ro, what=f"o split {mode}")
+    check_fp32(f64(lse), rl, floor=1.0, what=f"lse split {mode}")
+    # a second call reads counters the first left at zero: the same bits
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_split_fused_core(w, mode, split_mode):
+    case = make_case(w)
+    split_mode(mode)
+    print(f"[split fused] {w.name} mode {mode}", flush=True)
+    out = _sentinel_like(case.q)
+    out, k_hat_f, lse_f = m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v, case.gate,
+                                               case.q_gain, case.k_gain, case.cos, case.sin, out=out,
+                                               want_lse=True)
+    q_hat, k_hat = _q_k_hat(case)
+    o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    out_u, _ = m.muse_out_norm_gate(case.params, case.layout, o, case.gate)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any()
+    ref = O.attn_core(bits_f64(case.x["q"]), bits_f64(case.x["k"]), bits_f64(case.x["v"]),
+                      bits_f64(case.x["gate"]), case.segs, **case.oracle_kw())
+    check_bf16(f64(out), ref["out"], what=f"fused out split {mode}")
+    assert torch.equal(out.view(torch.int16), out_u.view(torch.int16))
+    assert torch.equal(lse_f, lse)
+
+
+def test_split_padded_keys_and_empty_rows(split_mode):
+    """Key padding under a split: parts that see only padded keys carry no
+    reference; a query with no valid key still gives the zero row."""
+    w = W.small_workload("split_pad_b2_s640", num_heads=4, num_kv_heads=1, head_dim=128, batch=2, seqlen=640)
+    case = make_case(w)
+    valid = np.ones((2, 640), dtype=np.uint8)
+    valid[0, :300] = 0          # left padding: the first 300 queries of row 0 see no key
+    valid[1, 500:] = 0          # right padding
+    valid[1, 64:192] = 0        # two whole padded tiles inside the row
+    lay = m.Layout.bshd(2, 640, attention_mask=torch.from_numpy(valid).cuda())
+    q_hat, k_hat = _q_k_hat(case, lay)
+    split_mode(4)
+    o, lse = m.muse_gqa_attn_fwd(case.params, lay, q_hat, k_hat, case.v, want_lse=True)
+    out, _, lse_f = m.muse_attn_core_fwd(case.params, lay, case.q, case.k, case.v, case.gate, case.q_gain,
+                                         case.k_gain, case.cos, case.sin, want_lse=True)
+    out_u, _ = m.muse_out_norm_gate(case.params, lay, o, case.gate)
+    torch.cuda.synchronize()
+    ro, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs, window=0,
+                         scaling=case.scaling, key_valid=valid.reshape(-1))
+    check_bf16(f64(o), ro, what="o padded split")
+    fin = np.isfinite(rl)
+    assert (~fin).any()
+    check_fp32(f64(lse)[fin], rl[fin], floor=1.0, what="lse padded split")
+    assert torch.isneginf(lse.cpu()[torch.from_numpy(~fin)]).all()
+    assert not f64(o)[~fin].any()
+    assert torch.equal(out.view(torch.int16), out_u.view(torch.int16))
+    assert torch.equal(lse_f, lse)
+
+
+def test_split_bidirectional(split_mode):
+    w = W.small_workload("split_bidir_thd", num_heads=4, num_kv_heads=2, head_dim=128,
+                         segment_lengths=(300, 900, 5), use_rope=False)
+    case = make_case(w, bidirectional=True)
+    q_hat, k_hat = _q_k_hat(case)
+    split_mode(3)
+    o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs, window=0,
+                         scaling=case.scaling, causal=False)
+    check_bf16(f64(o), ro, what="o bidirectional split")
+    check_fp32(f64(lse), rl, floor=1.0, what="lse bidirectional split")
+
+
+def test_automatic_split_of_a_small_grid(split_mode):
+    """One KV head of a 2048-token sequence: 64 work items, far fewer than two
+    per CU, so the automatic policy splits them; compared with the oracle on
+    every element, and with the never-split policy within rounding."""
+    w = W.small_workload("split_auto_s2048_h4kv1", num_heads=4, num_kv_heads=1, head_dim=128, seqlen=2048,
+                         theta=5.0e5)
+    case = make_case(w)
+    q_hat, k_hat = _q_k_hat(case)
+    split_mode(0)
+    o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    split_mode(1)
+    o1, lse1 = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs, window=0,
+                         scaling=case.scaling)
+    check_bf16(f64(o), ro, what="o automatic split")
+    check_bf16(f64(o1), ro, what="o unsplit")
+    check_fp32(f64(lse), rl, floor=1.0, what="lse automatic split")
+    # the split reorders sums: the two differ, by rounding only
+    assert not torch.equal(o.view(torch.int16), o1.view(torch.int16))
+    assert float((lse - lse1).abs().max()) < 1e-5 * max(1.0, float(lse1.abs().max()))
+
+
+def test_policy_setter_returns_previous():
+    prev = m.muse_attn_set_kv_split(1)
+    try:
+        assert m.muse_attn_set_kv_split(5) == 1
+        assert m.muse_attn_set_kv_split(-3) == -1
+        assert m.muse_attn_set_kv_split(0) == 5
+    finally:
+        m.muse_attn_set_kv_split(prev)

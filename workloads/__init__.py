@@ -81,6 +81,19 @@ WORKLOADS = {
         layers=((8192, True), (8192, True), (8192, True), (0, False)), gate_std=4.0),
 }
 
+# One GPU's share of the four large workloads when their KV heads are split over
+# eight GPUs (one KV head and its query heads per GPU; the heads of a KV group
+# need nothing from other groups): the same sequences at 1/8 of the heads.
+for _full, _share, _hq in (("bshd_2x4096_h32kv8_d128", "bshd_2x4096_h4kv1_d128", 4),
+                           ("bshd_1x16384_h32kv8_d128_w4096", "bshd_1x16384_h4kv1_d128_w4096", 4),
+                           ("thd_16seg_h40kv8_d128", "thd_16seg_h5kv1_d128", 5),
+                           ("bshd_1x32768_h64kv8_d128_mix", "bshd_1x32768_h8kv1_d128_mix", 8)):
+    WORKLOADS[_share] = dataclasses.replace(WORKLOADS[_full], name=_share, num_heads=_hq, num_kv_heads=1)
+SHARE_OF = {"bshd_2x4096_h4kv1_d128": "bshd_2x4096_h32kv8_d128",
+            "bshd_1x16384_h4kv1_d128_w4096": "bshd_1x16384_h32kv8_d128_w4096",
+            "thd_16seg_h5kv1_d128": "thd_16seg_h40kv8_d128",
+            "bshd_1x32768_h8kv1_d128_mix": "bshd_1x32768_h64kv8_d128_mix"}
+
 
 def small_workload(name, *, num_heads, num_kv_heads, head_dim, batch=1, seqlen=0,
                    segment_lengths=(), window=0, use_rope=True, theta=1.0e4, gate_std=1.0,
