@@ -11,7 +11,10 @@
 // workgroup of NW = 4 waves owns 32*NW query columns; a column is a (token,
 // head) pair of the KV group, token-major, so any group size fills the
 // columns (G = 5 uses 25 tokens x 5 heads + 3 idle columns).  K and V tiles
-// of BN = 64 keys are shared by all columns through LDS.
+// of BN = 64 keys are shared by all columns through LDS.  A grid too small to
+// fill the device may cut each item's key tiles into parts (KV split): each
+// part runs its tiles and publishes per wave its unnormalised O, reference and
+// sums; the last part of a wave to arrive combines them in part order.
 //
 // Registers (v_mfma_f32_32x32x16_bf16, 64 lanes): each wave computes
 // S^T = K Q^T, so lane l owns query column n = l % 32 and key rows
