@@ -225,20 +225,50 @@ int device_cus(int dev) {
   return c;
 }
 
-// The heaviest work item's tile count (the kernel's own tile range for each
-// query block of the longest segment).
-int max_item_tiles(const AttnArgs &a, int maxlen) {
+// The heaviest query block's key-tile count (the attention kernels' own tile
+// range for each query block of the longest segment).
+int max_item_tiles(int q_blocks, int tok_per_wg, int window, bool bidir, int maxlen) {
   const int bn = attn_keys_per_tile();
   int best = 0;
-  for (int qb = 0; qb < a.q_blocks; ++qb) {
-    const int q0 = qb * a.tok_per_wg;
+  for (int qb = 0; qb < q_blocks; ++qb) {
+    const int q0 = qb * tok_per_wg;
     if (q0 >= maxlen) break;
-    const int q1 = std::min(q0 + a.tok_per_wg, maxlen);
-    const int lo = a.window > 0 && !a.bidirectional ? std::max(0, q0 - a.window + 1) : 0;
-    const int hi = (a.bidirectional ? maxlen : q1) - 1;
+    const int q1 = std::min(q0 + tok_per_wg, maxlen);
+    const int lo = window > 0 && !bidir ? std::max(0, q0 - window + 1) : 0;
+    const int hi = (bidir ? maxlen : q1) - 1;
     best = std::max(best, hi / bn - lo / bn + 1);
   }
   return best;
+}
+
+// Parts and span (steps per part) of a grid of `items` work items whose
+// heaviest takes `steps` tile steps, with `per_cu` workgroups resident per CU;
+// the automatic policy aims at `fill_x2` / 2 workgroups per resident slot.
+void split_plan(int64_t items, int steps, int per_cu, int max_auto, int fill_x2, int *parts, int *span) {
+  *parts = 1;
+  *span = 0;
+  const int mode = g_kv_split.load();
+  if (mode == 1 || steps < 2) return;
+  int n;
+  if (mode >= 2) {
+    n = std::min(std::min(mode, steps), kMaxKvParts);
+  } else {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    const int cus = device_cus(dev);
+    const int64_t slots = (int64_t)cus * per_cu;
+    if (cus <= 0 || items >= slots) return;
+    // parts of at least 4 steps, so a part's prologue stays small beside its
+    // tile loop
+    n = (int)std::min<int64_t>(max_auto, (fill_x2 * slots + 2 * items - 1) / (2 * items));
+    n = std::min(n, steps / 4);
+  }
+  if (n < 2) return;
+  const int sp = (steps + n - 1) / n;
+  n = (steps + sp - 1) / sp;
+  if (n < 2) return;
+  *parts = n;
+  *span = sp;
 }
 
 // Grow-only device buffers per (device, stream): calls on one stream run in
@@ -300,26 +330,10 @@ muse_status split_buffers(hipStream_t stream, size_t cnt_bytes, size_t part_byte
 muse_status attn_split(AttnArgs &a, const Geometry &g, hipStream_t stream) {
   a.kv_parts = 1;
   a.kv_span = 0;
-  const int mode = g_kv_split.load();
-  if (mode == 1) return MUSE_OK;
   const int64_t items = (int64_t)a.q_blocks * g.nseg * a.hkv * a.head_chunks;
-  const int tiles = max_item_tiles(a, g.maxlen);
-  int parts = 1;
-  if (mode >= 2) {
-    parts = std::min(std::min(mode, tiles), kMaxKvParts);
-  } else {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return MUSE_OK;
-    const int cus = device_cus(dev);
-    if (cus <= 0 || items >= 2 * (int64_t)cus) return MUSE_OK;
-    // about three workgroups per CU; parts of at least 4 tiles, so a part's
-    // prologue stays small beside its tile loop
-    parts = (int)std::min<int64_t>(4, (3 * (int64_t)cus + items - 1) / items);
-    parts = std::min(parts, tiles / 4);
-  }
-  if (parts < 2) return MUSE_OK;
-  const int span = (tiles + parts - 1) / parts;
-  parts = (tiles + span - 1) / span;
+  int parts, span;
+  split_plan(items, max_item_tiles(a.q_blocks, a.tok_per_wg, a.window, a.bidirectional != 0, g.maxlen), 2, 4, 3,
+             &parts, &span);
   if (parts < 2) return MUSE_OK;
   const int nw = attn_waves_per_workgroup();
   const size_t slots = (size_t)items * parts * nw;
@@ -332,6 +346,53 @@ muse_status attn_split(AttnArgs &a, const Geometry &g, hipStream_t stream) {
   a.kv_span = span;
   a.part_cnt = (uint32_t *)cnt;
   a.part_o = (float *)part;
+  return MUSE_OK;
+}
+
+// The heaviest 128-key block's (query tile, head) steps in the dK/dV kernel.
+int max_dkv_steps(const AttnBwdArgs &a, int maxlen) {
+  const int kpw = attn_bwd_keys_per_workgroup(), bn = attn_keys_per_tile();
+  int best = 0;
+  for (int kb = 0; kb < a.k_blocks; ++kb) {
+    const int kb0 = kb * kpw;
+    if (kb0 >= maxlen) break;
+    const int qlo = a.bidirectional ? 0 : kb0;
+    const int qhi = a.bidirectional || a.window <= 0
+                        ? maxlen - 1
+                        : std::min(maxlen - 1, std::min(kb0 + kpw - 1, maxlen - 1) + a.window - 1);
+    best = std::max(best, (qhi / bn - qlo / bn + 1) * a.group);
+  }
+  return best;
+}
+
+// Splits of the two attention-backward kernels (the dQ kernel as the forward,
+// the dK/dV kernel over its query steps), sharing one set of buffers.
+muse_status attn_bwd_split(AttnBwdArgs &a, const Geometry &g, hipStream_t stream) {
+  a.dq_parts = a.dkv_parts = 1;
+  a.dq_span = a.dkv_span = 0;
+  const int64_t items_q = (int64_t)a.q_blocks * g.nseg * a.hkv * a.head_chunks;
+  const int64_t items_k = (int64_t)a.k_blocks * g.nseg * a.hkv;
+  int qp, qs, kp, ks;
+  split_plan(items_q, max_item_tiles(a.q_blocks, a.tok_per_wg, a.window, a.bidirectional != 0, g.maxlen), 2, 4, 3,
+             &qp, &qs);
+  // the D = 128 dK/dV kernel runs one workgroup per CU; one round of them
+  // (a 1.5-round split of the 16k/window-4096 share was 2 % slower than none)
+  split_plan(items_k, max_dkv_steps(a, g.maxlen), g.d == 128 ? 1 : 2, kMaxKvParts, 2, &kp, &ks);
+  if (qp < 2 && kp < 2) return MUSE_OK;
+  const int nw = attn_waves_per_workgroup();
+  const size_t acc_bytes = (size_t)32 * g.d * sizeof(float);   // one D x 32 fp32 accumulator per wave
+  const size_t need = std::max(qp > 1 ? (size_t)items_q * qp * nw * acc_bytes : 0,
+                               kp > 1 ? (size_t)items_k * kp * nw * 2 * acc_bytes : 0);
+  const size_t cnt = (size_t)std::max(qp > 1 ? items_q : 0, kp > 1 ? items_k : 0) * nw * sizeof(uint32_t);
+  void *c = nullptr, *part = nullptr;
+  muse_status s = split_buffers(stream, cnt, need, &c, &part);
+  if (s != MUSE_OK) return s;
+  a.dq_parts = qp;
+  a.dq_span = qs;
+  a.dkv_parts = kp;
+  a.dkv_span = ks;
+  a.part_acc = (float *)part;
+  a.part_cnt = (uint32_t *)c;
   return MUSE_OK;
 }
 
@@ -637,6 +698,7 @@ AttnBwdArgs attn_bwd_args(const muse_attn_params *p, const muse_layout *l, const
   a.q_blocks = (g.maxlen + a.tok_per_wg - 1) / a.tok_per_wg;
   const int kpw = attn_bwd_keys_per_workgroup();
   a.k_blocks = (g.maxlen + kpw - 1) / kpw;
+  a.dq_parts = a.dkv_parts = 1;
   a.lay = token_layout(l, g);
   return a;
 }
@@ -710,6 +772,7 @@ extern "C" muse_status muse_gqa_attn_bwd(const muse_attn_params *p, const muse_l
   a.dq = (uint16_t *)dq_hat;
   a.dk = (uint16_t *)dk_hat;
   a.dv = (uint16_t *)dv;
+  if ((s = attn_bwd_split(a, g, (hipStream_t)stream)) != MUSE_OK) return s;
   return device_status(launch_attn_bwd(g.d, a, (hipStream_t)stream), "attention backward launch");
 }
 

@@ -165,12 +165,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) 
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  // work item: as the forward (segment-major, longest query blocks first, kv head)
-  const int per_seg = a.q_blocks * a.hkv * a.head_chunks;
+  // work item: as the forward (segment-major, longest query blocks first,
+  // part, kv head)
+  const int heads_items = a.hkv * a.head_chunks;
+  const int per_seg = a.q_blocks * a.dq_parts * heads_items;
   const int b = blockIdx.x;
   const int seg = b / per_seg;
   int rest = b % per_seg;
-  const int qb = a.q_blocks - 1 - rest / (a.hkv * a.head_chunks);
+  const int qb = a.q_blocks - 1 - rest / (a.dq_parts * heads_items);
+  rest %= a.dq_parts * heads_items;
+  const int part = rest / heads_items;
   rest %= a.hkv * a.head_chunks;
   const int hc = rest % a.head_chunks;
   const int kvh = rest / a.head_chunks;
@@ -246,7 +250,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) 
     }
   };
 
-  f32x16 dqacc[DT];
+  f32x16 dqv[1][DT];
+  f32x16 (&dqacc)[DT] = dqv[0];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dqacc[dt] = f32x16{};
 
@@ -296,25 +301,40 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) 
   const int kt_lo = lo / BN;
   const int kt_hi = ((bidir ? L : q1) - 1) / BN;
   const int ntiles = kt_hi - kt_lo + 1;
+  // split: this part takes tiles kt_hi - it for it in [it0, it1) (the last
+  // launched part takes any remainder)
+  const int span = a.dq_parts > 1 ? a.dq_span : ntiles;
+  const int nparts = min((ntiles + span - 1) / span, a.dq_parts);
+  if (part >= nparts) return;
+  const int it0 = part * span;
+  const int it1 = part == nparts - 1 ? ntiles : it0 + span;
 
-  issue_dma(kt_hi, 0);
+  issue_dma(kt_hi - it0, 0);
   vmem_wait_all();
   __syncthreads();
-  for (int it = 0;;) {
+  for (int it = it0;;) {
     take_mask();
-    if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 1);
+    if (it + 1 < it1) issue_dma(kt_hi - it - 1, 1);
     compute(kt_hi - it, 0);
     vmem_wait_all();
     __syncthreads();
-    if (++it >= ntiles) break;
+    if (++it >= it1) break;
     take_mask();
-    if (it + 1 < ntiles) issue_dma(kt_hi - it - 1, 0);
+    if (it + 1 < it1) issue_dma(kt_hi - it - 1, 0);
     compute(kt_hi - it, 1);
     vmem_wait_all();
     __syncthreads();
-    if (++it >= ntiles) break;
+    if (++it >= it1) break;
   }
-  if (!wave_active || !qvalid) return;
+  if (!wave_active) return;
+  if (nparts > 1) {
+    const int64_t item = (((int64_t)seg * a.q_blocks + qb) * a.hkv + kvh) * a.head_chunks + hc;
+    constexpr int SLOT = DT * 16 * 64;
+    if (!split_sum(dqv, a.part_acc + (item * a.dq_parts * NW + wave) * SLOT, (int64_t)NW * SLOT, part, nparts,
+                   a.part_cnt + item * NW + wave))
+      return;
+  }
+  if (!qvalid) return;
   store_cols<D>(a.dq + qrow, dqacc, a.scaling, g, false);
 }
 
@@ -350,11 +370,13 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
   // work item: segment-major, key blocks ascending (the most queries first),
   // then kv head -- consecutive workgroups take consecutive kv heads, so each
   // XCD keeps one head group's Q/dO rows in its L2.
-  const int per_seg = a.k_blocks * a.hkv;
+  const int per_seg = a.k_blocks * a.dkv_parts * a.hkv;
   const int b = blockIdx.x;
   const int seg = b / per_seg;
-  const int rest = b % per_seg;
-  const int kb = rest / a.hkv;
+  int rest = b % per_seg;
+  const int kb = rest / (a.dkv_parts * a.hkv);
+  rest %= a.dkv_parts * a.hkv;
+  const int part = rest / a.hkv;
   const int kvh = rest % a.hkv;
   int s0, L;
   segment_bounds(a.lay, seg, s0, L);
@@ -393,6 +415,12 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
   const int qt_lo = qlo / BN;
   const int nqt = qhi / BN - qt_lo + 1;
   const int ntiles = nqt * a.group;
+  // split: this part takes steps [it0, it1) (the last launched part takes any remainder)
+  const int span = a.dkv_parts > 1 ? a.dkv_span : ntiles;
+  const int nparts = min((ntiles + span - 1) / span, a.dkv_parts);
+  if (part >= nparts) return;
+  const int it0 = part * span;
+  const int it1 = part == nparts - 1 ? ntiles : it0 + span;
 
   const int64_t q_stride = (int64_t)a.hq * D;
   int off[DMA_PER_WAVE];
@@ -429,7 +457,9 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
     }
   };
 
-  f32x16 dkacc[DT], dvacc[DT];
+  f32x16 dkv[2][DT];
+  f32x16 (&dkacc)[DT] = dkv[0];
+  f32x16 (&dvacc)[DT] = dkv[1];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
 
@@ -475,20 +505,28 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
     }
   };
 
-  issue_dma(0, 0);
+  issue_dma(it0, 0);
   vmem_wait_all();
   __syncthreads();
-  for (int it = 0;;) {
-    if (it + 1 < ntiles) issue_dma(it + 1, 1);
+  for (int it = it0;;) {
+    if (it + 1 < it1) issue_dma(it + 1, 1);
     compute(it, 0);
     vmem_wait_all();
     __syncthreads();
-    if (++it >= ntiles) break;
-    if (it + 1 < ntiles) issue_dma(it + 1, 0);
+    if (++it >= it1) break;
+    if (it + 1 < it1) issue_dma(it + 1, 0);
     compute(it, 1);
     vmem_wait_all();
     __syncthreads();
-    if (++it >= ntiles) break;
+    if (++it >= it1) break;
+  }
+  if (!wave_active) return;
+  if (nparts > 1) {
+    const int64_t item = ((int64_t)seg * a.k_blocks + kb) * a.hkv + kvh;
+    constexpr int SLOT = 2 * DT * 16 * 64;
+    if (!split_sum(dkv, a.part_acc + (item * a.dkv_parts * NW + wave) * SLOT, (int64_t)NW * SLOT, part, nparts,
+                   a.part_cnt + item * NW + wave))
+      return;
   }
   if (!kin) return;
   // a padded key is seen by no query: its gradients are zero
@@ -499,8 +537,8 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
 template <int D, bool PAD>
 hipError_t launch_d(const AttnBwdArgs &a, hipStream_t stream) {
   const int64_t nseg = a.lay.num_segments;
-  const int64_t dq_blocks = (int64_t)a.q_blocks * nseg * a.hkv * a.head_chunks;
-  const int64_t kv_blocks = (int64_t)a.k_blocks * nseg * a.hkv;
+  const int64_t dq_blocks = (int64_t)a.q_blocks * nseg * a.hkv * a.head_chunks * a.dq_parts;
+  const int64_t kv_blocks = (int64_t)a.k_blocks * nseg * a.hkv * a.dkv_parts;
   if (dq_blocks > 0)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, PAD>), dim3((unsigned)dq_blocks), dim3(64 * NW), 0, stream, a);
   hipError_t e = hipGetLastError();
@@ -516,6 +554,11 @@ int attn_bwd_keys_per_workgroup() { return COLS; }
 
 hipError_t launch_attn_bwd(int head_dim, const AttnBwdArgs &a, hipStream_t stream) {
   if (a.heads_per_wg < 1 || a.heads_per_wg > COLS || a.tok_per_wg < 1 || a.tok_per_wg * a.heads_per_wg > COLS)
+    return hipErrorInvalidConfiguration;
+  for (const int parts : {a.dq_parts, a.dkv_parts})
+    if (parts < 1 || parts > kMaxKvParts) return hipErrorInvalidConfiguration;
+  if ((a.dq_parts > 1 && a.dq_span < 1) || (a.dkv_parts > 1 && a.dkv_span < 1) ||
+      ((a.dq_parts > 1 || a.dkv_parts > 1) && (!a.part_acc || !a.part_cnt)))
     return hipErrorInvalidConfiguration;
   const bool pad = a.key_valid != nullptr;
   if (head_dim == 128) return pad ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);

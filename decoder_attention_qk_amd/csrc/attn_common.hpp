@@ -37,6 +37,52 @@ __device__ __forceinline__ void vmem_wait_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
 }
 
+// Sum of per-wave accumulators over the parts of one split work item.  Each
+// part stores this wave's R x C accumulators to its slot (floats, [element]
+// [lane]) with device-coherent stores -- a store completes only once it is
+// visible device-wide, so waiting for them orders them before the arrival --
+// and counts its arrival; the wave that arrives last resets the counter to
+// zero, replaces acc by the sum of every part's slot in part order (the same
+// bits whichever part arrives last) and returns true.  No wave waits for
+// another.  Release/acquire fences would write back and invalidate the XCD's
+// whole L2 instead, which its other workgroups pay for in refetches.
+template <int R, int C>
+__device__ __forceinline__ bool split_sum(f32x16 (&acc)[R][C], float *slot0, int64_t part_stride, int part,
+                                          int nparts, uint32_t *cnt) {
+  const int lane = threadIdx.x & 63;
+  float *mine = slot0 + part * part_stride + lane;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        __hip_atomic_store(mine + ((r * C + c) * 16 + i) * 64, acc[r][c][i], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  uint32_t prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != (uint32_t)(nparts - 1)) return false;
+  if (lane == 0) *cnt = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[r][c] = f32x16{};
+  for (int p = 0; p < nparts; ++p) {
+    const float *src = slot0 + p * part_stride + lane;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[r][c][i] += __hip_atomic_load(src + ((r * C + c) * 16 + i) * 64, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return true;
+}
+
 // LDS layout of a tile of 64 rows of D bf16 values with its 16-byte chunks
 // XOR-swizzled per row (the swizzle is applied on the DMA source side).
 template <int D>

@@ -154,6 +154,14 @@ struct AttnBwdArgs {
   const uint8_t *key_valid;    // BSHD token validity or nullptr
   int32_t q_blocks;            // dQ kernel: query blocks per segment
   int32_t k_blocks;            // dK/dV kernel: 128-key blocks per segment
+  // Splits of small grids (1: none): the dQ kernel's key tiles and the dK/dV
+  // kernel's (query tile, head) steps are cut into parts whose fp32 sums the
+  // last part of each wave adds up in part order.  The kernels run one after
+  // the other, so they share the slots and counters.
+  int32_t dq_parts, dq_span;
+  int32_t dkv_parts, dkv_span;
+  float *part_acc;             // [items][parts][waves] slots of R x C x 16 x 64 floats
+  uint32_t *part_cnt;          // [items][waves] arrivals; zero between launches
   TokenLayout lay;
 };
 

@@ -431,15 +431,20 @@ muse_status muse_validate_cu_seqlens(const int32_t *cu_seqlens_host, int32_t num
                                      int32_t total_tokens, int32_t max_seqlen);
 
 /*
- * Attention-forward KV split policy (process-wide; muse_gqa_attn_fwd,
- * muse_attn_fused_fwd, muse_attn_core_fwd and the recomputing backward):
- *   0  automatic (default): split only grids with fewer than two work items
- *      per CU, into at most 4 parts of at least 4 key tiles;
+ * Split policy of the attention kernels for small grids (process-wide): the
+ * forward (muse_gqa_attn_fwd, muse_attn_fused_fwd, muse_attn_core_fwd) and
+ * the backward's dQ kernel split a work item's key tiles; the backward's
+ * dK/dV kernel (muse_gqa_attn_bwd, muse_attn_core_bwd) splits a key block's
+ * (query tile, head) steps.
+ *   0  automatic (default): split only grids with fewer work items than
+ *      resident workgroup slots (two per CU; one for the D = 128 dK/dV
+ *      kernel), into parts of at least 4 steps (at most 4 parts; 8 for dK/dV);
  *   1  never split;
- *   n >= 2  split every work item with two or more 64-key tiles into
- *      min(n, 8) parts (a tuning and testing aid).
+ *   n >= 2  split every work item with two or more steps into min(n, 8)
+ *      parts (a tuning and testing aid).
  * Splitting reorders the sums (results move within rounding); a given policy
- * and shape always give the same bits, fused and unfused alike.
+ * and shape always give the same bits, fused and unfused alike.  The backward
+ * split uses the same per-(device, stream) buffer as the forward's.
  * Returns the previous policy, or -1 (nothing changed) when mode < 0.
  */
 int32_t muse_attn_set_kv_split(int32_t mode);

@@ -174,3 +174,57 @@ def test_policy_setter_returns_previous():
         assert m.muse_attn_set_kv_split(0) == 5
     finally:
         m.muse_attn_set_kv_split(prev)
+
+
+# ---------------------------------------------------------------- backward
+# The dQ kernel splits its key tiles as the forward does; the dK/dV kernel
+# splits each key block's (query tile, head) steps; each sums its parts' fp32
+# accumulators in part order.
+BWD_CASES = [CASES[0], CASES[1], CASES[3], CASES[4]]
+
+
+def _bwd_inputs(case, layout=None):
+    lay = layout if layout is not None else case.layout
+    q_hat, k_hat = _q_k_hat(case, lay)
+    o, lse = m.muse_gqa_attn_fwd(case.params, lay, q_hat, k_hat, case.v, want_lse=True)
+    d_o = dev_bf16(W.draw_bf16(tuple(case.q.shape), 1.0, seed=11, workload=case.w.name, layer=0, tensor="d_o"))
+    delta = m.muse_attn_bwd_delta(case.params, lay, o, d_o)
+    return q_hat, k_hat, o, lse, d_o, delta
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3, 8])
+@pytest.mark.parametrize("w", BWD_CASES, ids=[w.name for w in BWD_CASES])
+def test_split_attention_bwd(w, mode, split_mode):
+    case = make_case(w)
+    q_hat, k_hat, o, lse, d_o, delta = _bwd_inputs(case)
+    split_mode(mode)
+    print(f"[split bwd] {w.name} mode {mode}", flush=True)
+    got = m.muse_gqa_attn_bwd(case.params, case.layout, q_hat, k_hat, case.v, d_o, lse, delta)
+    again = m.muse_gqa_attn_bwd(case.params, case.layout, q_hat, k_hat, case.v, d_o, lse, delta)
+    torch.cuda.synchronize()
+    ref = O.attention_bwd(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), f64(d_o), case.segs,
+                          window=case.x["window"], scaling=case.scaling, o=f64(o))
+    for name, g_, a_, r in zip(("dq_hat", "dk_hat", "dv"), got, again, ref):
+        check_bf16(f64(g_), r, what=f"{name} split {mode}")
+        assert torch.equal(g_.view(torch.int16), a_.view(torch.int16)), name
+
+
+def test_split_attention_bwd_padded_keys(split_mode):
+    w = W.small_workload("split_bwd_pad_b2_s640", num_heads=8, num_kv_heads=2, head_dim=128, batch=2, seqlen=640)
+    case = make_case(w)
+    valid = np.ones((2, 640), dtype=np.uint8)
+    valid[0, :300] = 0
+    valid[1, 64:192] = 0
+    valid[1, 500:] = 0
+    lay = m.Layout.bshd(2, 640, attention_mask=torch.from_numpy(valid).cuda())
+    q_hat, k_hat, o, lse, d_o, delta = _bwd_inputs(case, lay)
+    split_mode(4)
+    dq, dk, dv = m.muse_gqa_attn_bwd(case.params, lay, q_hat, k_hat, case.v, d_o, lse, delta)
+    torch.cuda.synchronize()
+    rq, rk, rv = O.attention_bwd(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), f64(d_o), case.segs, window=0,
+                                 scaling=case.scaling, o=f64(o), key_valid=valid.reshape(-1).astype(bool))
+    check_bf16(f64(dq), rq, what="dq_hat padded split")
+    check_bf16(f64(dk), rk, what="dk_hat padded split")
+    check_bf16(f64(dv), rv, what="dv padded split")
+    flat = torch.from_numpy(valid.reshape(-1) == 0).cuda()
+    assert torch.all(dk[flat] == 0) and torch.all(dv[flat] == 0)
