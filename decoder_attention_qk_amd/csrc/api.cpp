@@ -310,7 +310,8 @@ muse_status split_buffers(hipStream_t stream, size_t cnt_bytes, size_t part_byte
       w->cnt = nullptr;
       w->cnt_bytes = 0;
       if ((e = hipMalloc(&w->cnt, cnt_bytes)) != hipSuccess) return device_status(e, "KV-split counters");
-      if ((e = hipMemset(w->cnt, 0, cnt_bytes)) != hipSuccess) return device_status(e, "KV-split counters");
+      // ordered on the caller's stream (a non-blocking stream does not wait for the null stream)
+      if ((e = hipMemsetAsync(w->cnt, 0, cnt_bytes, stream)) != hipSuccess) return device_status(e, "KV-split counters");
       w->cnt_bytes = cnt_bytes;
     }
     if (w->part_bytes < part_bytes) {

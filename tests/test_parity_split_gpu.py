@@ -228,3 +228,21 @@ def test_split_attention_bwd_padded_keys(split_mode):
     check_bf16(f64(dv), rv, what="dv padded split")
     flat = torch.from_numpy(valid.reshape(-1) == 0).cuda()
     assert torch.all(dk[flat] == 0) and torch.all(dv[flat] == 0)
+
+
+def test_split_on_a_side_stream_matches_the_default_stream(split_mode):
+    """A torch side stream (non-blocking) gets its own split buffer, zeroed in
+    its own stream order: the first call on it equals the default stream's."""
+    w = W.small_workload("split_side_stream_s1100", num_heads=8, num_kv_heads=2, head_dim=128, seqlen=1100)
+    case = make_case(w)
+    q_hat, k_hat = _q_k_hat(case)
+    split_mode(3)
+    o_ref, lse_ref = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(lse, lse_ref)
