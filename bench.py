@@ -4,12 +4,16 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 for each layer of the workload the key norm/RoPE pass (the first rotating
 layer's pass also builds the FP32 RoPE table, in the same launch) and the
 fused attention kernel (query norm/RoPE prologue, causal GQA flash attention,
-output norm x sigmoid gate epilogue).  Inputs are resident in
-HBM before the timed region.  Prints one JSON line.  Besides the step it
-reports the unfused stages (flushed caches) and the backward entry points of
-layer 0 (--no-stages, --no-backward skip them).
+output norm x sigmoid gate epilogue).  The default workload is the 32k-token
+four-layer mix (three layers with a 8192-key window and RoPE, one full-causal
+layer without RoPE; 64 query heads, 8 KV heads, D = 128).  Inputs are resident
+in HBM before the timed region.  Prints one JSON line.  Besides the step it
+reports the unfused stages of layer 0 (flushed caches), the other workloads'
+fused kernel and flushed norm stages, the backward entry points of layer 0,
+and the CPU oracle's rate on a sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --summarize-pmc DIR [DIR ...]   # rocprofv3 counter summary (text)
 """
 
 from __future__ import annotations
@@ -29,10 +33,12 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 METRIC = "attention TFLOP/s (causal-adjusted) + norm/RoPE/gate GB/s, % of roofline"
-DEFAULT_WORKLOAD = "bshd_2x4096_h32kv8_d128"
+DEFAULT_WORKLOAD = "bshd_1x32768_h64kv8_d128_mix"
+# the five configurations; the other four get a sub-record each
+CONFIGS = ["bshd_1x128_h4kv1_d64", "bshd_2x4096_h32kv8_d128", "bshd_1x16384_h32kv8_d128_w4096",
+           "thd_16seg_h40kv8_d128", "bshd_1x32768_h64kv8_d128_mix"]
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
-EVENT_EVERY = 4                # timed steps between two steps with per-launch events
 EPS = 1e-6
 
 
@@ -51,22 +57,25 @@ def layer_flop(w: W.Workload, window: int) -> int:
     return 4 * w.head_dim * w.num_heads * sum(visible_pairs(n, window) for n in seq_lengths(w))
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU raises its clocks over the first ~30 ms of sustained work, so the
-    # default warmup runs 100 steps before the timed region
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    # a 32k-mix step is ~38 ms, so five warmup steps already cover the ~30 ms
+    # the clocks need to settle from idle
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
     ap.add_argument("--kv-split", type=int, default=0,
-                    help="attention KV-split policy: 0 automatic, 1 never, n >= 2 n parts")
+                    help="attention KV-split policy (params.kv_split): 0 automatic, 1 never, n >= 2 n parts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage (unfused) measurements")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurements")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the other configurations' sub-records")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (reference kernel for HBM counters)")
-    return ap.parse_args()
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print a text summary of rocprofv3 --pmc result directories and exit")
+    return ap.parse_args(argv)
 
 
 def kernel_source_digest() -> str:
@@ -101,7 +110,10 @@ def measured_traffic(workload: str, launches: int):
 
 
 class Bench:
-    def __init__(self, w: W.Workload):
+    """A workload's layers resident on the GPU, with every buffer the step
+    needs (outputs, K-hat, the RoPE table, split workspaces) allocated once."""
+
+    def __init__(self, w: W.Workload, kv_split: int = 0):
         import torch
 
         import decoder_attention_qk_amd as m
@@ -112,24 +124,26 @@ class Bench:
         def bf(a):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
+        if w.is_thd:
+            cu = torch.from_numpy(w.cu_seqlens()).to(dev)
+            self.layout = m.Layout.thd(cu, w.max_seqlen, total_tokens=w.tokens)
+        else:
+            self.layout = m.Layout.bshd(w.batch, w.seqlen)
         self.layers = []
         for li in range(len(w.layers)):
             x = W.make_layer_inputs(w, li)
             p = m.AttnParams(head_dim=w.head_dim, num_heads=w.num_heads,
                              num_key_value_heads=w.num_kv_heads, sliding_window=x["window"],
                              use_rope=x["use_rope"], scaling=float(np.float32(w.head_dim ** -0.5)),
-                             qk_eps=EPS, out_eps=EPS)
+                             qk_eps=EPS, out_eps=EPS, kv_split=kv_split)
             t = dict(params=p, q=bf(x["q"]), k=bf(x["k"]), v=bf(x["v"]), gate=bf(x["gate"]),
                      q_gain=torch.from_numpy(x["q_gain"]).to(dev),
                      k_gain=torch.from_numpy(x["k_gain"]).to(dev), window=x["window"])
             t["k_hat"] = torch.empty_like(t["k"])
             t["out"] = torch.empty_like(t["q"])
+            ws = m.muse_attn_fwd_workspace_size(p, self.layout)
+            t["ws"] = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
             self.layers.append(t)
-        if w.is_thd:
-            cu = torch.from_numpy(w.cu_seqlens()).to(dev)
-            self.layout = m.Layout.thd(cu, w.max_seqlen, total_tokens=w.tokens)
-        else:
-            self.layout = m.Layout.bshd(w.batch, w.seqlen)
         self.n_pos = max(1, w.max_seqlen)
         self.cos = torch.empty((self.n_pos, w.head_dim // 2), dtype=torch.float32, device=dev)
         self.sin = torch.empty_like(self.cos)
@@ -158,23 +172,74 @@ class Bench:
             if ev is not None:
                 ev[2 + 3 * li].record()
             m.muse_attn_fused_fwd(t["params"], self.layout, t["q"], t["k_hat"], t["v"], t["gate"],
-                                  t["q_gain"], cos, sin, out=t["out"])
+                                  t["q_gain"], cos, sin, out=t["out"], workspace=t["ws"])
             if ev is not None:
                 ev[3 + 3 * li].record()
 
     def n_events(self):
         return 1 + 3 * len(self.layers)
 
+    def free(self):
+        self.layers.clear()
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
 
-def measure_stages(b: Bench, iters: int = 5) -> dict:
-    """Unfused stages, each timed alone after reading a 512 MiB buffer, which
-    refills the 256 MB Infinity Cache with clean unrelated lines, so the
-    HBM-bound kernels are charged HBM traffic (a write-based flush would leave
-    dirty lines for the measured kernel to write back)."""
+
+def time_steps(b: Bench, steps: int, warmup: int) -> dict:
+    """Warmup, then `steps` timed steps bracketed by device synchronisation,
+    with events around every launch (a step holds few long launches, so the
+    marker packets cost well under 1 %)."""
+    torch = b.torch
+    for _ in range(warmup):
+        b.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(b.n_events())] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        b.step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nl = len(b.layers)
+    attn = np.array([[evs[i][2 + 3 * li].elapsed_time(evs[i][3 + 3 * li]) * 1e-3 for li in range(nl)]
+                     for i in range(steps)])
+    kpass = np.array([[evs[i][1 + 3 * li].elapsed_time(evs[i][2 + 3 * li]) * 1e-3 for li in range(nl)]
+                      for i in range(steps)])
+    flop_layers = [layer_flop(b.w, t["window"]) for t in b.layers]
+    return dict(step_s=wall / steps, attn_s=attn, kpass_s=kpass, flop_layers=flop_layers)
+
+
+def kernel_record(b: Bench, t: dict) -> dict:
+    """The fused attention kernel's roofline record: algorithmic flop per
+    launch averaged over the step's launches / the average launch duration."""
+    flop = np.array(t["flop_layers"], dtype=np.float64)
+    attn = t["attn_s"]
+    achieved = float(flop.sum() / attn.mean(axis=0).sum()) / 1e12
+    kb = b.layers[0]["k"].numel() * 2
+    kp = float(t["kpass_s"].mean())
+    return {
+        "kernel": f"attn_fwd_kernel<{b.w.head_dim},fused>",
+        "achieved": round(achieved, 3), "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "launch_us": round(float(attn.mean()) * 1e6, 2),
+        "launch_us_per_layer": [round(float(x) * 1e6, 2) for x in attn.mean(axis=0)],
+        "k_norm_rope": {"launch_us": round(kp * 1e6, 2), "GBps": round(2 * kb / kp / 1e9, 1),
+                        "frac_hbm": round(2 * kb / kp / 1e9 / PEAK_HBM_GBPS, 4)},
+    }
+
+
+def measure_stages(b: Bench, iters: int = 5, which=("qk_norm_rope", "gqa_attn_fwd", "out_norm_gate",
+                                                    "k_norm_rope", "attn_fused_fwd_flushed")) -> dict:
+    """Unfused stages of layer 0, each timed alone after reading a 512 MiB
+    buffer, which refills the 256 MB Infinity Cache with clean unrelated
+    lines, so the HBM-bound kernels are charged HBM traffic (a write-based
+    flush would leave dirty lines for the measured kernel to write back)."""
     torch, m, w = b.torch, b.m, b.w
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=b.dev)
     t = b.layers[0]
-    cos, sin = (b.cos, b.sin) if t["params"].use_rope else (None, None)
+    p = t["params"]
+    cos, sin = (b.cos, b.sin) if p.use_rope else (None, None)
+    if p.use_rope:
+        m.muse_rope_cos_sin(w.theta, w.head_dim, b.n_pos, b.cos, b.sin)
     q_hat, k_hat = torch.empty_like(t["q"]), torch.empty_like(t["k"])
     o = torch.empty_like(t["q"])
     out = torch.empty_like(t["q"])
@@ -193,20 +258,29 @@ def measure_stages(b: Bench, iters: int = 5) -> dict:
 
     qb = t["q"].numel() * 2
     kb = t["k"].numel() * 2
+    flop = layer_flop(w, t["window"])
+    m.muse_qk_norm_rope(p, b.layout, t["q"], t["k"], t["q_gain"], t["k_gain"], cos, sin, q_out=q_hat,
+                        k_out=k_hat)
+    m.muse_gqa_attn_fwd(p, b.layout, q_hat, k_hat, t["v"], o=o, workspace=t["ws"])
     res = {}
-    s = timed(lambda: m.muse_qk_norm_rope(t["params"], b.layout, t["q"], t["k"], t["q_gain"], t["k_gain"],
-                                          cos, sin, q_out=q_hat, k_out=k_hat))
-    res["qk_norm_rope"] = dict(us=s * 1e6, GBps=2 * (qb + kb) / s / 1e9)
-    s = timed(lambda: m.muse_gqa_attn_fwd(t["params"], b.layout, q_hat, k_hat, t["v"], o=o))
-    res["gqa_attn_fwd"] = dict(us=s * 1e6, TFLOPs=layer_flop(w, t["window"]) / s / 1e12)
-    s = timed(lambda: m.muse_out_norm_gate(t["params"], b.layout, o, t["gate"], out=out))
-    res["out_norm_gate"] = dict(us=s * 1e6, GBps=3 * qb / s / 1e9)
-    s = timed(lambda: m.muse_qk_norm_rope(t["params"], b.layout, None, t["k"], None, t["k_gain"], cos, sin,
-                                          k_out=k_hat))
-    res["k_norm_rope"] = dict(us=s * 1e6, GBps=2 * kb / s / 1e9)
-    s = timed(lambda: m.muse_attn_fused_fwd(t["params"], b.layout, t["q"], k_hat, t["v"], t["gate"],
-                                            t["q_gain"], cos, sin, out=out))
-    res["attn_fused_fwd_flushed"] = dict(us=s * 1e6, TFLOPs=layer_flop(w, t["window"]) / s / 1e12)
+    if "qk_norm_rope" in which:
+        s = timed(lambda: m.muse_qk_norm_rope(p, b.layout, t["q"], t["k"], t["q_gain"], t["k_gain"], cos, sin,
+                                              q_out=q_hat, k_out=k_hat))
+        res["qk_norm_rope"] = dict(us=s * 1e6, GBps=2 * (qb + kb) / s / 1e9)
+    if "gqa_attn_fwd" in which:
+        s = timed(lambda: m.muse_gqa_attn_fwd(p, b.layout, q_hat, k_hat, t["v"], o=o, workspace=t["ws"]))
+        res["gqa_attn_fwd"] = dict(us=s * 1e6, TFLOPs=flop / s / 1e12)
+    if "out_norm_gate" in which:
+        s = timed(lambda: m.muse_out_norm_gate(p, b.layout, o, t["gate"], out=out))
+        res["out_norm_gate"] = dict(us=s * 1e6, GBps=3 * qb / s / 1e9)
+    if "k_norm_rope" in which:
+        s = timed(lambda: m.muse_qk_norm_rope(p, b.layout, None, t["k"], None, t["k_gain"], cos, sin,
+                                              k_out=k_hat))
+        res["k_norm_rope"] = dict(us=s * 1e6, GBps=2 * kb / s / 1e9)
+    if "attn_fused_fwd_flushed" in which:
+        s = timed(lambda: m.muse_attn_fused_fwd(p, b.layout, t["q"], k_hat, t["v"], t["gate"], t["q_gain"], cos,
+                                                sin, out=out, workspace=t["ws"]))
+        res["attn_fused_fwd_flushed"] = dict(us=s * 1e6, TFLOPs=flop / s / 1e12)
     for v in res.values():
         if "GBps" in v:
             v["frac_hbm"] = v["GBps"] / PEAK_HBM_GBPS
@@ -218,7 +292,7 @@ def measure_stages(b: Bench, iters: int = 5) -> dict:
     return res
 
 
-def measure_backward(b: Bench, warmup: int = 20, iters: int = 50) -> dict:
+def measure_backward(b: Bench, warmup: int = 5, iters: int = 20) -> dict:
     """The backward of layer 0 (warm clocks, back-to-back launches, events
     around each entry point): output norm/gate backward, attention backward
     (dQ kernel + dK/dV kernel), Q/K norm/RoPE backward, and the whole
@@ -229,32 +303,39 @@ def measure_backward(b: Bench, warmup: int = 20, iters: int = 50) -> dict:
     t = b.layers[0]
     p, lay = t["params"], b.layout
     cos, sin = (b.cos, b.sin) if p.use_rope else (None, None)
-    m.muse_rope_cos_sin(w.theta, w.head_dim, b.n_pos, b.cos, b.sin)
+    if p.use_rope:
+        m.muse_rope_cos_sin(w.theta, w.head_dim, b.n_pos, b.cos, b.sin)
     q_hat, k_hat, _, _ = m.muse_qk_norm_rope(p, lay, t["q"], t["k"], t["q_gain"], t["k_gain"], cos, sin)
-    o, lse = m.muse_gqa_attn_fwd(p, lay, q_hat, k_hat, t["v"], want_lse=True)
+    o, lse = m.muse_gqa_attn_fwd(p, lay, q_hat, k_hat, t["v"], want_lse=True, workspace=t["ws"])
     g = torch.Generator(device=b.dev)
     g.manual_seed(7)
     dout = torch.randn(t["q"].shape, generator=g, device=b.dev).to(torch.bfloat16)
-    d_o, dgate, delta = m.muse_out_norm_gate_bwd(p, lay, o, t["gate"], dout)
-    dq_hat, dk_hat, dv = m.muse_gqa_attn_bwd(p, lay, q_hat, k_hat, t["v"], d_o, lse, delta)
-    dq, dk, dqg, dkg = m.muse_qk_norm_rope_bwd(p, lay, t["q"], t["k"], t["q_gain"], t["k_gain"], cos, sin,
-                                               dq_hat, dk_hat)
-    res_core = m.muse_attn_core_bwd(p, lay, t["q"], t["k"], t["v"], t["gate"], dout, t["q_gain"], t["k_gain"],
-                                    cos, sin, o=o, lse=lse)
+
+    def ws(n):
+        return torch.empty(max(1, n), dtype=torch.uint8, device=b.dev)
+    ws_attn = ws(m.muse_gqa_attn_bwd_workspace_size(p, lay))
     size = ctypes.c_size_t(0)
     pc, lc = p.to_c(), lay.to_c()
+    m.library().muse_qk_norm_rope_bwd_workspace_size(ctypes.byref(pc), ctypes.byref(lc), ctypes.byref(size))
+    ws_qk = ws(size.value)
     m.library().muse_attn_core_bwd_workspace_size(ctypes.byref(pc), ctypes.byref(lc), ctypes.byref(size))
-    ws = torch.empty(size.value, dtype=torch.uint8, device=b.dev)
+    ws_core = ws(size.value)
+    d_o, dgate, delta = m.muse_out_norm_gate_bwd(p, lay, o, t["gate"], dout)
+    dq_hat, dk_hat, dv = m.muse_gqa_attn_bwd(p, lay, q_hat, k_hat, t["v"], d_o, lse, delta, workspace=ws_attn)
+    dq, dk, dqg, dkg = m.muse_qk_norm_rope_bwd(p, lay, t["q"], t["k"], t["q_gain"], t["k_gain"], cos, sin,
+                                               dq_hat, dk_hat, workspace=ws_qk)
+    res_core = m.muse_attn_core_bwd(p, lay, t["q"], t["k"], t["v"], t["gate"], dout, t["q_gain"], t["k_gain"],
+                                    cos, sin, o=o, lse=lse, workspace=ws_core)
     calls = [
         lambda: m.muse_out_norm_gate_bwd(p, lay, o, t["gate"], dout, d_o=d_o, dgate=dgate, delta=delta),
         lambda: m.muse_gqa_attn_bwd(p, lay, q_hat, k_hat, t["v"], d_o, lse, delta, dq_hat=dq_hat,
-                                    dk_hat=dk_hat, dv=dv),
+                                    dk_hat=dk_hat, dv=dv, workspace=ws_attn),
         lambda: m.muse_qk_norm_rope_bwd(p, lay, t["q"], t["k"], t["q_gain"], t["k_gain"], cos, sin, dq_hat,
-                                        dk_hat, dq=dq, dk=dk, dq_gain=dqg, dk_gain=dkg),
+                                        dk_hat, dq=dq, dk=dk, dq_gain=dqg, dk_gain=dkg, workspace=ws_qk),
         lambda: m.muse_attn_core_bwd(p, lay, t["q"], t["k"], t["v"], t["gate"], dout, t["q_gain"],
                                      t["k_gain"], cos, sin, o=o, lse=lse, dq=res_core[0], dk=res_core[1],
                                      dv=res_core[2], dgate=res_core[3], dq_gain=res_core[4],
-                                     dk_gain=res_core[5], workspace=ws),
+                                     dk_gain=res_core[5], workspace=ws_core),
     ]
     for _ in range(warmup):
         for c in calls:
@@ -271,6 +352,7 @@ def measure_backward(b: Bench, warmup: int = 20, iters: int = 50) -> dict:
     qb, kb = t["q"].numel() * 2, t["k"].numel() * 2
     flop = 2.5 * layer_flop(w, t["window"])
     return {
+        "layer": 0,
         "out_norm_gate_bwd": {"us": round(us[0], 2), "GBps": round(5 * qb / us[0] / 1e3, 1),
                               "frac_hbm": round(5 * qb / us[0] / 1e3 / PEAK_HBM_GBPS, 4)},
         "gqa_attn_bwd": {"us": round(us[1], 2), "TFLOPs": round(flop / us[1] / 1e6, 2),
@@ -282,46 +364,141 @@ def measure_backward(b: Bench, warmup: int = 20, iters: int = 50) -> dict:
     }
 
 
-def cpu_baseline(w: W.Workload, budget_s: float = 12.0) -> dict:
-    """The FP64 oracle, as it stands, on whole (sequence, KV group) units of
-    the same workload until about `budget_s` seconds of CPU work are done."""
+def measure_workload(name: str, kv_split: int, steps: int = 10, warmup: int = 5) -> dict:
+    """Sub-record of another configuration: its step, the fused kernel's
+    roofline fraction and the flushed Q/K norm+RoPE and output norm/gate stages."""
+    w = W.WORKLOADS[name]
+    b = Bench(w, kv_split)
+    t = time_steps(b, steps, warmup)
+    rec = kernel_record(b, t)
+    flop_step = sum(t["flop_layers"])
+    st = measure_stages(b, which=("qk_norm_rope", "out_norm_gate"))
+    out = {"step_ms": round(t["step_s"] * 1e3, 4), "TFLOPs_step": round(flop_step / t["step_s"] / 1e12, 3),
+           "fused_kernel": rec, "qk_norm_rope_flushed": st["qk_norm_rope"],
+           "out_norm_gate_flushed": st["out_norm_gate"]}
+    b.free()
+    return out
+
+
+def cpu_baseline(w: W.Workload, budget_s: float = 20.0) -> dict:
+    """The FP64 oracle, as it stands, on a sample of the same workload: per
+    layer its key-side work (norm + RoPE of every key) once, and the full path
+    (query norm/RoPE, attention, norm-gate) of sampled (token, head) rows; the
+    step time is extrapolated from the measured key-side time and the rows'
+    time per visible (query, key) pair, over every row of every layer."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
-    except Exception:
-        threads = 0
-    threads = threads or 1
-    x = W.make_layer_inputs(w, 0)
-    window, use_rope = x["window"], x["use_rope"]
-    g = w.num_heads // w.num_kv_heads
-    starts = np.concatenate([[0], np.cumsum(seq_lengths(w))])[:-1]
-    units = [(int(s), int(n), kv) for s, n in zip(starts, seq_lengths(w)) for kv in range(w.num_kv_heads)]
-    units.sort(key=lambda u: -u[1])
-    flop = 0
-    done = 0
-    t0 = time.perf_counter()
-    for s0, n, kv in units:
-        sl = slice(s0, s0 + n)
-        hs = slice(kv * g, (kv + 1) * g)
-        O.attn_core(O.bf16_bits_to_f64(x["q"][sl, hs]), O.bf16_bits_to_f64(x["k"][sl, kv:kv + 1]),
-                    O.bf16_bits_to_f64(x["v"][sl, kv:kv + 1]), O.bf16_bits_to_f64(x["gate"][sl, hs]),
-                    O.Segments.bshd(1, n), theta=w.theta, eps=EPS, out_eps=EPS,
-                    scaling=float(np.float32(w.head_dim ** -0.5)), window=window, use_rope=use_rope,
-                    q_gain=x["q_gain"].astype(np.float64), k_gain=x["k_gain"].astype(np.float64))
-        flop += 4 * w.head_dim * g * visible_pairs(n, window)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(units)} (sequence, kv-group) units of layer 0 ({g} query heads each), "
-                      f"full oracle path (norm, RoPE, attention, norm-gate) in {el:.1f} s; "
-                      f"BLAS threads {threads}, elementwise numpy single-threaded"}
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    segs = O.Segments.thd(w.cu_seqlens()) if w.is_thd else O.Segments.bshd(w.batch, w.seqlen)
+    pos = segs.local_positions()
+    kw = dict(theta=w.theta, eps=EPS, out_eps=EPS, scaling=float(np.float32(w.head_dim ** -0.5)))
+    # layers with the same (window, rope) share one measurement
+    kinds = {}
+    for li, (win, rope) in enumerate(w.layers):
+        kinds.setdefault((win, rope), li)
+    per_layer_budget = budget_s / len(kinds)
+    total_s = 0.0
+    sample_rows = 0
+    sample_s = 0.0
+    meas = {}
+    for (win, rope), li in kinds.items():
+        x = W.make_layer_inputs(w, li)
+        qg, kg = x["q_gain"].astype(np.float64), x["k_gain"].astype(np.float64)
+        k64, v64 = O.bf16_bits_to_f64(x["k"]), O.bf16_bits_to_f64(x["v"])
+
+        def run(rows):
+            tok = np.array([r[0] for r in rows])
+            hd = np.array([r[1] for r in rows])
+            t0 = time.perf_counter()
+            O.attn_core_rows(O.bf16_bits_to_f64(x["q"][tok, hd]), k64, v64, O.bf16_bits_to_f64(x["gate"][tok, hd]),
+                             segs, rows, num_heads=w.num_heads, window=win, use_rope=rope, q_gain=qg,
+                             k_gain=kg, **kw)
+            return time.perf_counter() - t0
+
+        def pairs_of(rows):
+            return sum(min(int(pos[t]) + 1, win) if win > 0 else int(pos[t]) + 1 for t, _ in rows)
+
+        def draw(n):
+            return [(int(rng.integers(w.tokens)), int(rng.integers(w.num_heads))) for _ in range(n)]
+        one = draw(1)
+        t1 = run(one)
+        n = 16
+        rows = draw(n)
+        tn = run(rows)
+        # grow the sample until it takes about the layer's share of the budget
+        while tn < 0.5 * per_layer_budget and n < 65536:
+            n = min(65536, int(n * max(2.0, 0.6 * per_layer_budget / max(tn, 1e-3))))
+            rows = draw(n)
+            tn = run(rows)
+        p1, pn = pairs_of(one), pairs_of(rows)
+        per_pair = max(tn - t1, 1e-9) / max(pn - p1, 1)
+        key_side = max(t1 - p1 * per_pair, 0.0)
+        meas[(win, rope)] = (key_side, per_pair)
+        sample_rows += n + 1
+        sample_s += t1 + tn
+    flop_step = 0
+    for win, rope in w.layers:
+        key_side, per_pair = meas[(win, rope)]
+        pairs = w.num_heads * sum(visible_pairs(L, win) for L in seq_lengths(w))
+        total_s += key_side + per_pair * pairs
+        flop_step += 4 * w.head_dim * pairs
+    return {"value": round(flop_step / total_s / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "extrapolated": True,
+            "sample": f"{sample_rows} (token, head) rows over {len(kinds)} layer kinds in {sample_s:.1f} s of "
+                      f"oracle time (full path per row: query norm/RoPE, attention, norm-gate; plus every key's "
+                      f"norm/RoPE per layer); the step's {total_s:.0f} s is extrapolated from the key-side time "
+                      f"and the time per visible (query, key) pair; BLAS threads as numpy sets them on "
+                      f"{cores} cores, elementwise numpy single-threaded"}
 
 
-def main():
-    args = parse()
+def summarize_pmc(dirs: list[str]) -> str:
+    """Text summary of rocprofv3 --pmc result databases: per kernel, the mean
+    of each counter per dispatch and the ratios the attention kernel's
+    analysis uses."""
+    import collections
+    import glob
+    import sqlite3
+    lines = []
+    for d in dirs:
+        for db in sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True)):
+            con = sqlite3.connect(db)
+            rows = con.execute("select dispatch_id, kernel_name, counter_name, sum(value), avg(duration) "
+                               "from counters_collection group by dispatch_id, counter_name").fetchall()
+            per = collections.defaultdict(lambda: collections.defaultdict(float))
+            n = collections.Counter()
+            seen = set()
+            for did, kname, cname, val, dur in rows:
+                kname = kname.replace("(anonymous namespace)::", "").split("(")[0]
+                per[kname][cname] += val
+                if did not in seen:
+                    seen.add(did)
+                    n[kname] += 1
+                    per[kname]["duration_ns"] += dur
+            lines.append(f"## {os.path.relpath(db, ROOT) if db.startswith(ROOT) else db}")
+            for kname in sorted(per, key=lambda k: -per[k]["duration_ns"]):
+                c = {k: v / n[kname] for k, v in per[kname].items()}
+                lines.append(f"- `{kname}`: {n[kname]} dispatches; per dispatch: "
+                             + ", ".join(f"{k} {v:.6g}" for k, v in sorted(c.items())))
+                mf = c.get("SQ_INSTS_MFMA", 0.0)
+                if mf:
+                    r = []
+                    if "SQ_INSTS_VALU" in c:
+                        r.append(f"non-MFMA VALU per MFMA {(c['SQ_INSTS_VALU'] - mf) / mf:.3f}")
+                    for k in ("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+                        if k in c:
+                            r.append(f"{k} per MFMA {c[k] / mf:.3f}")
+                    lines.append("  - " + "; ".join(r))
+                if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and c.get("SQ_VALU_MFMA_COEXEC_CYCLES") is not None:
+                    lines.append(f"  - VALU co-executed with MFMA in "
+                                 f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.3f} of MFMA-busy cycles")
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the library has no "
@@ -332,54 +509,27 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
-    import decoder_attention_qk_amd as m
     w = W.WORKLOADS[args.workload]
-    m.muse_attn_set_kv_split(args.kv_split)
-    b = Bench(w)
+    b = Bench(w, args.kv_split)
     if args.calibrate_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=b.dev)   # 256 MiB
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        b.step()
-    torch.cuda.synchronize()
-
-    # Per-launch events on every EVENT_EVERY-th timed step only: each timed
-    # event is a marker packet between dependent kernels, and four of them
-    # per step add ~13 us (4 %) to the step; sampled steps keep the kernel
-    # timing live inside the timed region at ~1 % cost.
-    sampled = list(range(0, args.steps, EVENT_EVERY))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(b.n_events())] for i in sampled}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        b.step(evs.get(i))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    nl = len(b.layers)
-    attn_s = np.array([[evs[i][2 + 3 * li].elapsed_time(evs[i][3 + 3 * li]) * 1e-3 for li in range(nl)]
-                       for i in sampled])
-    kpass_s = np.array([[evs[i][1 + 3 * li].elapsed_time(evs[i][2 + 3 * li]) * 1e-3 for li in range(nl)]
-                        for i in sampled])
-    flop_layers = [layer_flop(w, t["window"]) for t in b.layers]
-    flop_step = sum(flop_layers)
-    step_s = wall / args.steps
-    # dominant kernel: the fused attention kernel; achieved = algorithmic flop
-    # per launch / mean launch duration, over all its launches in the timed region
-    achieved = float(np.mean([flop_layers[li] / attn_s[:, li].mean() for li in range(nl)])) / 1e12
+    t = time_steps(b, args.steps, args.warmup)
+    rec = kernel_record(b, t)
+    flop_step = sum(t["flop_layers"])
     kb = b.layers[0]["k"].numel() * 2
     qb = b.layers[0]["q"].numel() * 2
     line = {
         "metric": METRIC,
-        "value": round(flop_step / step_s / 1e12, 3),
+        "value": round(flop_step / t["step_s"] / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 4),
+        "ms_per_step": round(t["step_s"] * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -389,28 +539,33 @@ def main():
             "workload": w.name, "tokens": w.tokens, "batch": w.batch if not w.is_thd else 1,
             "seq_len": w.max_seqlen, "segments": len(seq_lengths(w)), "num_heads": w.num_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-            "layers": [{"sliding_window": t["window"], "use_rope": bool(t["params"].use_rope)} for t in b.layers],
+            "layers": [{"sliding_window": t_["window"], "use_rope": bool(t_["params"].use_rope)}
+                       for t_ in b.layers],
             "flop_per_step_causal": flop_step,
             "share_of": W.SHARE_OF.get(w.name),
             "kv_split_policy": args.kv_split,
         },
         "roofline": {
-            "bound": "mfma", "kernel": "attn_fwd_kernel<128,fused>" if w.head_dim == 128 else "attn_fwd_kernel<64,fused>",
-            "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(w.name, nl),
-            "launch_us": round(float(attn_s.mean()) * 1e6, 2),
+            "bound": "mfma", "kernel": rec["kernel"],
+            "achieved": rec["achieved"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": rec["frac"], "traffic": measured_traffic(w.name, len(b.layers)),
+            "launch_us": rec["launch_us"], "launch_us_per_layer": rec["launch_us_per_layer"],
+            "kernel_source_digest": kernel_source_digest(),
         },
-        "k_norm_rope": {
-            "launch_us": round(float(kpass_s.mean()) * 1e6, 2),
-            "GBps": round(2 * kb / float(kpass_s.mean()) / 1e9, 1),
-            "frac_hbm": round(2 * kb / float(kpass_s.mean()) / 1e9 / PEAK_HBM_GBPS, 4),
-        },
+        "k_norm_rope": rec["k_norm_rope"],
         "fused_bytes_per_layer": 3 * qb + 2 * kb,
     }
     if not args.no_stages:
         line["stages_flushed"] = measure_stages(b)
     if not args.no_backward:
         line["backward"] = measure_backward(b)
+    b.free()
+    del b
+    if not args.no_workloads and w.name in CONFIGS:
+        line["workloads"] = {}
+        for name in CONFIGS:
+            if name != w.name:
+                line["workloads"][name] = measure_workload(name, args.kv_split)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -21,7 +21,8 @@ __all__ = [
     "muse_gqa_attn_fwd", "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd",
     "muse_attn_bwd_delta", "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd",
     "muse_qk_norm_rope_bwd_workspace_size", "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size",
-    "muse_validate_cu_seqlens", "muse_attn_set_kv_split", "muse_status_string", "muse_version",
+    "muse_attn_fwd_workspace_size", "muse_gqa_attn_bwd_workspace_size",
+    "muse_validate_cu_seqlens", "muse_status_string", "muse_version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,8 +35,9 @@ symbols = (
     "muse_rope_cos_sin", "muse_rope_cos_sin_2d", "muse_qk_norm_rope", "muse_qk_norm_rope_table",
     "muse_gqa_attn_fwd", "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd", "muse_attn_bwd_delta",
     "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd", "muse_qk_norm_rope_bwd_workspace_size",
-    "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size", "muse_validate_cu_seqlens",
-    "muse_attn_set_kv_split", "muse_status_string", "muse_last_error", "muse_version",
+    "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size", "muse_attn_fwd_workspace_size",
+    "muse_gqa_attn_bwd_workspace_size", "muse_validate_cu_seqlens",
+    "muse_status_string", "muse_last_error", "muse_version",
 )
 
 
@@ -52,7 +54,7 @@ class c_params(ctypes.Structure):
                 ("scaling", ctypes.c_float), ("query_scale", ctypes.c_float),
                 ("qk_eps", ctypes.c_float), ("out_eps", ctypes.c_float),
                 ("gain_center", ctypes.c_float), ("bidirectional", ctypes.c_int32),
-                ("skip_qk_norm", ctypes.c_int32)]
+                ("skip_qk_norm", ctypes.c_int32), ("kv_split", ctypes.c_int32)]
 
 
 class c_layout(ctypes.Structure):
@@ -69,13 +71,15 @@ _SIGS = {
     "muse_rope_cos_sin_2d": [ctypes.c_float, _I32, _I32, _I32, _P, _P, _P],
     "muse_qk_norm_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P],
     "muse_qk_norm_rope_table": [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P, _P, _P, _P, _P, _P],
-    "muse_gqa_attn_fwd": [_P, _P, _P, _P, _P, _P, _P, _P],
+    "muse_gqa_attn_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "muse_attn_fwd_workspace_size": [_P, _P, _P],
     "muse_out_norm_gate": [_P, _P, _P, _P, _P, _P, _P],
-    "muse_attn_core_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P],
-    "muse_attn_fused_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
+    "muse_attn_core_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "muse_attn_fused_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
     "muse_out_norm_gate_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P],
     "muse_attn_bwd_delta": [_P, _P, _P, _P, _P, _P],
-    "muse_gqa_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "muse_gqa_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "muse_gqa_attn_bwd_workspace_size": [_P, _P, _P],
     "muse_qk_norm_rope_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
                               ctypes.c_size_t, _P],
     "muse_qk_norm_rope_bwd_workspace_size": [_P, _P, _P],
@@ -83,7 +87,6 @@ _SIGS = {
                            _P, _P, ctypes.c_size_t, _P],
     "muse_attn_core_bwd_workspace_size": [_P, _P, _P],
     "muse_validate_cu_seqlens": [_P, _I32, _I32, _I32],
-    "muse_attn_set_kv_split": [_I32],
     "muse_status_string": [ctypes.c_int],
     "muse_last_error": [],
     "muse_version": [],
@@ -129,12 +132,6 @@ def muse_version() -> str:
     return library().muse_version().decode()
 
 
-def muse_attn_set_kv_split(mode: int) -> int:
-    """Sets the attention forward's KV-split policy (0 automatic, 1 never,
-    n >= 2 n parts); returns the previous one."""
-    return int(library().muse_attn_set_kv_split(int(mode)))
-
-
 # ---------------------------------------------------------------- parameters
 
 @dataclasses.dataclass
@@ -154,6 +151,7 @@ class AttnParams:
     gain_center: float = 1.0
     bidirectional: bool = False           # packed bidirectional attention (no causal order)
     skip_qk_norm: bool = False            # muse_qk_norm_rope: scale/rotate only (vision attention)
+    kv_split: int = 0                     # attention split policy: 0 automatic, 1 never, n >= 2 n parts
 
     def to_c(self) -> c_params:
         scale = self.head_dim ** -0.5 if self.scaling is None else self.scaling
@@ -161,7 +159,7 @@ class AttnParams:
                         int(self.sliding_window or 0), int(bool(self.use_rope)),
                         int(bool(self.upcast_rope)), scale, self.query_scale, self.qk_eps,
                         self.out_eps, self.gain_center, int(bool(self.bidirectional)),
-                        int(bool(self.skip_qk_norm)))
+                        int(bool(self.skip_qk_norm)), int(self.kv_split))
 
 
 @dataclasses.dataclass
@@ -240,6 +238,31 @@ def _stream(stream):
 def _empty(shape, dtype, like):
     import torch
     return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def _workspace_size(fn, params, layout) -> int:
+    size = ctypes.c_size_t(0)
+    p, l = params.to_c(), layout.to_c()
+    _check(fn(ctypes.byref(p), ctypes.byref(l), ctypes.byref(size)))
+    return size.value
+
+
+def _ws_ptr(ws):
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise TypeError("workspace: expected a contiguous GPU tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def _fwd_workspace(params, layout, workspace, like):
+    """(pointer, bytes) of the caller's forward workspace, or of a fresh one
+    when the call needs one and none was given (None, 0 when it needs none)."""
+    import torch
+    if workspace is not None:
+        return _ws_ptr(workspace)
+    size = _workspace_size(library().muse_attn_fwd_workspace_size, params, layout)
+    if size == 0:
+        return None, 0
+    return _ws_ptr(torch.empty(size, dtype=torch.uint8, device=like.device))
 
 
 def muse_rope_cos_sin(theta, head_dim, n_pos, cos_out=None, sin_out=None, *, device=None, stream=None):
@@ -329,18 +352,24 @@ def muse_qk_norm_rope_table(params: AttnParams, layout: Layout, q, k, q_gain=Non
     return q_out, k_out, q_rstd, k_rstd, cos_out, sin_out
 
 
+def muse_attn_fwd_workspace_size(params: AttnParams, layout: Layout) -> int:
+    """Workspace bytes of the attention forward (the KV split's; 0 without one)."""
+    return _workspace_size(library().muse_attn_fwd_workspace_size, params, layout)
+
+
 def muse_gqa_attn_fwd(params: AttnParams, layout: Layout, q_hat, k_hat, v, *, o=None, lse=None,
-                      want_lse=False, stream=None):
+                      want_lse=False, workspace=None, stream=None):
     """Causal GQA attention; returns (o, lse)."""
     import torch
     if o is None:
         o = torch.empty_like(q_hat)
     if want_lse and lse is None:
         lse = _empty(q_hat.shape[:2], torch.float32, q_hat)
+    wp, wb = _fwd_workspace(params, layout, workspace, q_hat)
     p, l = params.to_c(), layout.to_c()
     _check(library().muse_gqa_attn_fwd(
         ctypes.byref(p), ctypes.byref(l), _ptr(q_hat, "q_hat", "bf16"), _ptr(k_hat, "k_hat", "bf16"),
-        _ptr(v, "v", "bf16"), _ptr(o, "o", "bf16"), _ptr(lse, "lse", "fp32"), _stream(stream)))
+        _ptr(v, "v", "bf16"), _ptr(o, "o", "bf16"), _ptr(lse, "lse", "fp32"), wp, wb, _stream(stream)))
     return o, lse
 
 
@@ -361,7 +390,7 @@ def muse_out_norm_gate(params: AttnParams, layout: Layout, o, gate, *, out=None,
 
 def muse_attn_core_fwd(params: AttnParams, layout: Layout, q, k, v, gate, q_gain=None, k_gain=None,
                        cos=None, sin=None, *, k_hat_out=None, out=None, lse=None, want_lse=False,
-                       stream=None):
+                       workspace=None, stream=None):
     """The fused core; returns (out, k_hat_out, lse)."""
     import torch
     if out is None:
@@ -371,18 +400,19 @@ def muse_attn_core_fwd(params: AttnParams, layout: Layout, q, k, v, gate, q_gain
     if want_lse and lse is None:
         lse = _empty(q.shape[:2], torch.float32, q)
     n_pos = cos.shape[0] if cos is not None else 0
+    wp, wb = _fwd_workspace(params, layout, workspace, q)
     p, l = params.to_c(), layout.to_c()
     _check(library().muse_attn_core_fwd(
         ctypes.byref(p), ctypes.byref(l), _ptr(q, "q", "bf16"), _ptr(k, "k", "bf16"),
         _ptr(v, "v", "bf16"), _ptr(gate, "gate", "bf16"), _ptr(q_gain, "q_gain", "fp32"),
         _ptr(k_gain, "k_gain", "fp32"), _ptr(cos, "cos", "fp32"), _ptr(sin, "sin", "fp32"), n_pos,
         _ptr(k_hat_out, "k_hat_out", "bf16"), _ptr(out, "out", "bf16"), _ptr(lse, "lse", "fp32"),
-        _stream(stream)))
+        wp, wb, _stream(stream)))
     return out, k_hat_out, lse
 
 
 def muse_attn_fused_fwd(params: AttnParams, layout: Layout, q, k_hat, v, gate, q_gain=None, cos=None,
-                        sin=None, *, out=None, lse=None, want_lse=False, stream=None):
+                        sin=None, *, out=None, lse=None, want_lse=False, workspace=None, stream=None):
     """Fused attention on already-normalised keys; returns (out, lse)."""
     import torch
     if out is None:
@@ -390,12 +420,13 @@ def muse_attn_fused_fwd(params: AttnParams, layout: Layout, q, k_hat, v, gate, q
     if want_lse and lse is None:
         lse = _empty(q.shape[:2], torch.float32, q)
     n_pos = cos.shape[0] if cos is not None else 0
+    wp, wb = _fwd_workspace(params, layout, workspace, q)
     p, l = params.to_c(), layout.to_c()
     _check(library().muse_attn_fused_fwd(
         ctypes.byref(p), ctypes.byref(l), _ptr(q, "q", "bf16"), _ptr(k_hat, "k_hat", "bf16"),
         _ptr(v, "v", "bf16"), _ptr(gate, "gate", "bf16"), _ptr(q_gain, "q_gain", "fp32"),
         _ptr(cos, "cos", "fp32"), _ptr(sin, "sin", "fp32"), n_pos, _ptr(out, "out", "bf16"),
-        _ptr(lse, "lse", "fp32"), _stream(stream)))
+        _ptr(lse, "lse", "fp32"), wp, wb, _stream(stream)))
     return out, lse
 
 
@@ -404,18 +435,10 @@ def muse_attn_fused_fwd(params: AttnParams, layout: Layout, q, k_hat, v, gate, q
 def _workspace(fn, params, layout, workspace, like):
     """A caller's workspace, or a fresh one of the size the library reports."""
     import torch
-    size = ctypes.c_size_t(0)
-    p, l = params.to_c(), layout.to_c()
-    _check(fn(ctypes.byref(p), ctypes.byref(l), ctypes.byref(size)))
+    size = _workspace_size(fn, params, layout)
     if workspace is None:
-        workspace = torch.empty(max(1, size.value), dtype=torch.uint8, device=like.device)
-    return workspace, size.value
-
-
-def _ws_ptr(ws):
-    if not ws.is_cuda or not ws.is_contiguous():
-        raise TypeError("workspace: expected a contiguous GPU tensor")
-    return ws.data_ptr(), ws.numel() * ws.element_size()
+        workspace = torch.empty(max(1, size), dtype=torch.uint8, device=like.device)
+    return workspace, size
 
 
 def muse_out_norm_gate_bwd(params: AttnParams, layout: Layout, o, gate, dout, *, d_o=None, dgate=None,
@@ -444,19 +467,26 @@ def muse_attn_bwd_delta(params: AttnParams, layout: Layout, o, d_o, *, delta=Non
     return delta
 
 
+def muse_gqa_attn_bwd_workspace_size(params: AttnParams, layout: Layout) -> int:
+    """Workspace bytes of the attention backward (its splits'; 0 without one)."""
+    return _workspace_size(library().muse_gqa_attn_bwd_workspace_size, params, layout)
+
+
 def muse_gqa_attn_bwd(params: AttnParams, layout: Layout, q_hat, k_hat, v, d_o, lse, delta, *,
-                      dq_hat=None, dk_hat=None, dv=None, stream=None):
+                      dq_hat=None, dk_hat=None, dv=None, workspace=None, stream=None):
     """Attention backward; returns (dq_hat, dk_hat, dv)."""
     import torch
     dq_hat = torch.empty_like(q_hat) if dq_hat is None else dq_hat
     dk_hat = torch.empty_like(k_hat) if dk_hat is None else dk_hat
     dv = torch.empty_like(v) if dv is None else dv
+    workspace, _ = _workspace(library().muse_gqa_attn_bwd_workspace_size, params, layout, workspace, q_hat)
+    wp, wb = _ws_ptr(workspace)
     p, l = params.to_c(), layout.to_c()
     _check(library().muse_gqa_attn_bwd(
         ctypes.byref(p), ctypes.byref(l), _ptr(q_hat, "q_hat", "bf16"), _ptr(k_hat, "k_hat", "bf16"),
         _ptr(v, "v", "bf16"), _ptr(d_o, "d_o", "bf16"), _ptr(lse, "lse", "fp32"),
         _ptr(delta, "delta", "fp32"), _ptr(dq_hat, "dq_hat", "bf16"), _ptr(dk_hat, "dk_hat", "bf16"),
-        _ptr(dv, "dv", "bf16"), _stream(stream)))
+        _ptr(dv, "dv", "bf16"), wp, wb, _stream(stream)))
     return dq_hat, dk_hat, dv
 
 

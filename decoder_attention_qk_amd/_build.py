@@ -15,7 +15,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmuseattn.so")
 
 SOURCES = ["rope_table.hip", "qk_norm_rope.hip", "out_norm_gate.hip", "attn_fwd.hip", "norm_bwd.hip",
-           "attn_bwd.hip", "api.cpp", "validate.cpp"]
+           "attn_bwd.hip", "api.cpp", "validate.cpp", "debug_check.cpp"]
 # Per-source extra flags.  The attention kernel never forms a NaN score (masked
 # scores are -inf, never NaN), so max() needs no NaN quieting; infinities stay
 # honoured.

@@ -1,15 +1,14 @@
 // C ABI of libmuseattn: argument validation on the host, then kernel launches
-// on the caller's stream.  No allocation, no global state besides the
-// per-thread error message.
+// on the caller's stream.  No allocation (scratch memory is the caller's
+// workspace), no synchronisation (the opt-in debug checks of debug_check.cpp
+// aside), no state besides the per-thread error message.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
 #include <vector>
 
 #include "host_util.hpp"
@@ -78,18 +77,17 @@ muse_status check_params(const muse_attn_params *p) {
   if (!finite(p->gain_center)) return set_error(MUSE_ERR_INVALID_ARG, "gain_center must be finite");
   if (p->bidirectional && p->sliding_window > 0)
     return set_error(MUSE_ERR_INVALID_ARG, "a sliding window applies to causal attention only");
+  if (p->kv_split < 0) return set_error(MUSE_ERR_INVALID_ARG, "kv_split %d must be >= 0", p->kv_split);
   if (p->head_dim != 64 && p->head_dim != 128)
     return set_error(MUSE_ERR_UNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", p->head_dim);
   return MUSE_OK;
 }
 
-bool debug_validate() {
-  const char *e = std::getenv("MUSE_DEBUG_VALIDATE");
-  return e && e[0] == '1';
-}
-
-muse_status check_layout(const muse_layout *l, const muse_attn_params *p, hipStream_t stream,
-                         Geometry *g) {
+// Checks the layout and fills g.  With MUSE_DEBUG_VALIDATE=1 and `device_check`
+// the device cu_seqlens is copied back and validated (that synchronises the
+// stream).
+muse_status check_layout(const muse_layout *l, const muse_attn_params *p, hipStream_t stream, Geometry *g,
+                         bool device_check = true) {
   if (!l) return set_error(MUSE_ERR_INVALID_ARG, "layout is NULL");
   g->d = p->head_dim;
   g->hq = p->num_heads;
@@ -109,13 +107,8 @@ muse_status check_layout(const muse_layout *l, const muse_attn_params *p, hipStr
     g->n_tokens = l->total_tokens;
     g->nseg = l->num_segments;
     g->maxlen = l->max_seqlen;
-    if (debug_validate() && l->num_segments < (1 << 26)) {
-      std::vector<int32_t> host((size_t)l->num_segments + 1);
-      if (hipMemcpyAsync(host.data(), l->cu_seqlens, host.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
-                         stream) != hipSuccess ||
-          hipStreamSynchronize(stream) != hipSuccess)
-        return set_error(MUSE_ERR_DEVICE, "copying cu_seqlens for validation failed");
-      const muse_status s = muse_validate_cu_seqlens(host.data(), l->num_segments, l->total_tokens, l->max_seqlen);
+    if (device_check && debug_validate_enabled()) {
+      const muse_status s = debug_check_cu_seqlens(l, stream);
       if (s != MUSE_OK) return s;
     }
   } else {
@@ -149,14 +142,18 @@ Range layout_range(const muse_layout *l, const Geometry &g, int which) {
   return Range{l->position_ids, g.n_tokens * 4, "position_ids", 4};
 }
 
+// The RoPE table rules; with MUSE_DEBUG_VALIDATE=1 explicit position_ids are
+// copied back and checked against [0, n_pos) (that synchronises the stream).
 muse_status check_rope_table(const muse_attn_params *p, const muse_layout *l, const Geometry &g,
-                             const float *cos, const float *sin, int32_t n_pos) {
+                             const float *cos, const float *sin, int32_t n_pos, hipStream_t stream) {
   if (!p->use_rope || g.n_tokens == 0) return MUSE_OK;
   if (!cos || !sin) return set_error(MUSE_ERR_INVALID_ARG, "use_rope needs the cos and sin tables");
   if (n_pos < 1) return set_error(MUSE_ERR_INVALID_ARG, "n_pos %d < 1", n_pos);
   if (!l->position_ids && n_pos < g.maxlen)
     return set_error(MUSE_ERR_INVALID_ARG, "cos/sin table has %d positions, the layout needs %d", n_pos,
                      g.maxlen);
+  if (l->position_ids && ((uintptr_t)l->position_ids % 4) == 0 && debug_validate_enabled())
+    return debug_check_positions(l->position_ids, g.n_tokens, n_pos, stream);
   return MUSE_OK;
 }
 
@@ -210,19 +207,19 @@ int64_t bf16_bytes(int64_t n, int h, int d) { return n * h * d * 2; }
 // items (the last query blocks of a causal sequence) set the kernel's length;
 // then each item's key tiles are cut into parts of kv_span tiles run by
 // separate workgroups, combined per wave by the last part to finish.  The plan
-// depends only on the shape and the device's CU count, so the fused and
-// unfused kernels take the same one (and stay bitwise equal).
+// depends only on the params, the shape and the device's CU count, so the
+// fused and unfused kernels take the same one (and stay bitwise equal).  Its
+// partial slots and arrival counters live in the caller's workspace:
+// [counters, padded to kWsAlign][slots].
 
-std::atomic<int> g_kv_split{0};   // 0 automatic, 1 never, n >= 2: n parts whenever an item has 2+ tiles
+constexpr size_t kWsAlign = 256;
+size_t ws_round(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-int device_cus(int dev) {
-  static std::atomic<int> cache[64];
-  if (dev < 0 || dev >= 64) return 0;
-  int c = cache[dev].load();
-  if (c > 0) return c;
-  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return 0;
-  cache[dev].store(c);
-  return c;
+int current_device_cus() {
+  int dev = 0, c = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return c > 0 ? c : 0;
 }
 
 // The heaviest query block's key-tile count (the attention kernels' own tile
@@ -244,18 +241,16 @@ int max_item_tiles(int q_blocks, int tok_per_wg, int window, bool bidir, int max
 // Parts and span (steps per part) of a grid of `items` work items whose
 // heaviest takes `steps` tile steps, with `per_cu` workgroups resident per CU;
 // the automatic policy aims at `fill_x2` / 2 workgroups per resident slot.
-void split_plan(int64_t items, int steps, int per_cu, int max_auto, int fill_x2, int *parts, int *span) {
+void split_plan(int policy, int64_t items, int steps, int per_cu, int max_auto, int fill_x2, int *parts,
+                int *span) {
   *parts = 1;
   *span = 0;
-  const int mode = g_kv_split.load();
-  if (mode == 1 || steps < 2) return;
+  if (policy == 1 || steps < 2) return;
   int n;
-  if (mode >= 2) {
-    n = std::min(std::min(mode, steps), kMaxKvParts);
+  if (policy >= 2) {
+    n = std::min(std::min(policy, steps), kMaxKvParts);
   } else {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return;
-    const int cus = device_cus(dev);
+    const int cus = current_device_cus();
     const int64_t slots = (int64_t)cus * per_cu;
     if (cus <= 0 || items >= slots) return;
     // parts of at least 4 steps, so a part's prologue stays small beside its
@@ -271,83 +266,26 @@ void split_plan(int64_t items, int steps, int per_cu, int max_auto, int fill_x2,
   *span = sp;
 }
 
-// Grow-only device buffers per (device, stream): calls on one stream run in
-// order, so they can share one; calls on different streams get their own.
-struct SplitWs {
-  int dev;
-  hipStream_t stream;
-  void *cnt = nullptr;   // arrival counters, zero between launches
-  size_t cnt_bytes = 0;
-  void *part = nullptr;  // partial O and (max, sum) rows, no initial value needed
-  size_t part_bytes = 0;
+// A split's plan and the workspace it needs: counters first, then slots.
+struct SplitNeed {
+  int parts = 1, span = 0;
+  int64_t counters = 0;   // uint32 arrival counters (items x waves)
+  size_t slot_bytes = 0;  // partial slots
+  size_t bytes() const { return parts > 1 ? ws_round((size_t)counters * 4) + slot_bytes : 0; }
 };
-std::mutex g_ws_mu;
-std::vector<SplitWs> g_ws;
 
-muse_status split_buffers(hipStream_t stream, size_t cnt_bytes, size_t part_bytes, void **cnt, void **part) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return set_error(MUSE_ERR_DEVICE, "hipGetDevice failed");
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  SplitWs *w = nullptr;
-  for (SplitWs &x : g_ws)
-    if (x.dev == dev && x.stream == stream) w = &x;
-  if (!w) {
-    g_ws.push_back(SplitWs{dev, stream});
-    w = &g_ws.back();
-  }
-  if (w->cnt_bytes < cnt_bytes || w->part_bytes < part_bytes) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
-      return set_error(MUSE_ERR_UNSUPPORTED,
-                       "the KV-split workspace of this stream must grow (%zu + %zu bytes); make one call of "
-                       "this shape outside graph capture first",
-                       cnt_bytes, part_bytes);
-    // earlier launches on this stream may still use the old buffers
-    hipError_t e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return device_status(e, "KV-split workspace");
-    if (w->cnt_bytes < cnt_bytes) {
-      if (w->cnt) (void)hipFree(w->cnt);
-      w->cnt = nullptr;
-      w->cnt_bytes = 0;
-      if ((e = hipMalloc(&w->cnt, cnt_bytes)) != hipSuccess) return device_status(e, "KV-split counters");
-      // ordered on the caller's stream (a non-blocking stream does not wait for the null stream)
-      if ((e = hipMemsetAsync(w->cnt, 0, cnt_bytes, stream)) != hipSuccess) return device_status(e, "KV-split counters");
-      w->cnt_bytes = cnt_bytes;
-    }
-    if (w->part_bytes < part_bytes) {
-      if (w->part) (void)hipFree(w->part);
-      w->part = nullptr;
-      w->part_bytes = 0;
-      if ((e = hipMalloc(&w->part, part_bytes)) != hipSuccess) return device_status(e, "KV-split partials");
-      w->part_bytes = part_bytes;
-    }
-  }
-  *cnt = w->cnt;
-  *part = w->part;
-  return MUSE_OK;
-}
-
-// Plans the split for a, and when there is one, points a at its buffers.
-muse_status attn_split(AttnArgs &a, const Geometry &g, hipStream_t stream) {
-  a.kv_parts = 1;
-  a.kv_span = 0;
+SplitNeed fwd_split_need(const AttnArgs &a, const Geometry &g, int policy) {
+  SplitNeed n;
   const int64_t items = (int64_t)a.q_blocks * g.nseg * a.hkv * a.head_chunks;
-  int parts, span;
-  split_plan(items, max_item_tiles(a.q_blocks, a.tok_per_wg, a.window, a.bidirectional != 0, g.maxlen), 2, 4, 3,
-             &parts, &span);
-  if (parts < 2) return MUSE_OK;
+  split_plan(policy, items, max_item_tiles(a.q_blocks, a.tok_per_wg, a.window, a.bidirectional != 0, g.maxlen), 2,
+             4, 3, &n.parts, &n.span);
+  if (n.parts < 2) return n;
   const int nw = attn_waves_per_workgroup();
-  const size_t slots = (size_t)items * parts * nw;
   // per slot and lane: the wave's O fragment (D/32 tiles of 16) plus reference and sum
-  const size_t slot_bytes = (size_t)(g.d / 32 * 16 + 2) * 64 * sizeof(float);
-  void *cnt = nullptr, *part = nullptr;
-  muse_status s = split_buffers(stream, (size_t)items * nw * sizeof(uint32_t), slots * slot_bytes, &cnt, &part);
-  if (s != MUSE_OK) return s;
-  a.kv_parts = parts;
-  a.kv_span = span;
-  a.part_cnt = (uint32_t *)cnt;
-  a.part_o = (float *)part;
-  return MUSE_OK;
+  const size_t slot = (size_t)(g.d / 32 * 16 + 2) * 64 * sizeof(float);
+  n.counters = items * nw;
+  n.slot_bytes = (size_t)items * n.parts * nw * slot;
+  return n;
 }
 
 // The heaviest 128-key block's (query tile, head) steps in the dK/dV kernel.
@@ -367,33 +305,38 @@ int max_dkv_steps(const AttnBwdArgs &a, int maxlen) {
 }
 
 // Splits of the two attention-backward kernels (the dQ kernel as the forward,
-// the dK/dV kernel over its query steps), sharing one set of buffers.
-muse_status attn_bwd_split(AttnBwdArgs &a, const Geometry &g, hipStream_t stream) {
-  a.dq_parts = a.dkv_parts = 1;
-  a.dq_span = a.dkv_span = 0;
+// the dK/dV kernel over its query steps); they run one after the other and
+// share one set of slots and counters.
+struct BwdSplitNeed {
+  SplitNeed q, kv;
+  int64_t counters = 0;
+  size_t slot_bytes = 0;
+  size_t bytes() const { return (q.parts > 1 || kv.parts > 1) ? ws_round((size_t)counters * 4) + slot_bytes : 0; }
+};
+
+BwdSplitNeed bwd_split_need(const AttnBwdArgs &a, const Geometry &g, int policy) {
+  BwdSplitNeed n;
   const int64_t items_q = (int64_t)a.q_blocks * g.nseg * a.hkv * a.head_chunks;
   const int64_t items_k = (int64_t)a.k_blocks * g.nseg * a.hkv;
-  int qp, qs, kp, ks;
-  split_plan(items_q, max_item_tiles(a.q_blocks, a.tok_per_wg, a.window, a.bidirectional != 0, g.maxlen), 2, 4, 3,
-             &qp, &qs);
+  split_plan(policy, items_q, max_item_tiles(a.q_blocks, a.tok_per_wg, a.window, a.bidirectional != 0, g.maxlen),
+             2, 4, 3, &n.q.parts, &n.q.span);
   // the D = 128 dK/dV kernel runs one workgroup per CU; one round of them
   // (a 1.5-round split of the 16k/window-4096 share was 2 % slower than none)
-  split_plan(items_k, max_dkv_steps(a, g.maxlen), g.d == 128 ? 1 : 2, kMaxKvParts, 2, &kp, &ks);
-  if (qp < 2 && kp < 2) return MUSE_OK;
+  split_plan(policy, items_k, max_dkv_steps(a, g.maxlen), g.d == 128 ? 1 : 2, kMaxKvParts, 2, &n.kv.parts,
+             &n.kv.span);
   const int nw = attn_waves_per_workgroup();
   const size_t acc_bytes = (size_t)32 * g.d * sizeof(float);   // one D x 32 fp32 accumulator per wave
-  const size_t need = std::max(qp > 1 ? (size_t)items_q * qp * nw * acc_bytes : 0,
-                               kp > 1 ? (size_t)items_k * kp * nw * 2 * acc_bytes : 0);
-  const size_t cnt = (size_t)std::max(qp > 1 ? items_q : 0, kp > 1 ? items_k : 0) * nw * sizeof(uint32_t);
-  void *c = nullptr, *part = nullptr;
-  muse_status s = split_buffers(stream, cnt, need, &c, &part);
-  if (s != MUSE_OK) return s;
-  a.dq_parts = qp;
-  a.dq_span = qs;
-  a.dkv_parts = kp;
-  a.dkv_span = ks;
-  a.part_acc = (float *)part;
-  a.part_cnt = (uint32_t *)c;
+  n.slot_bytes = std::max(n.q.parts > 1 ? (size_t)items_q * n.q.parts * nw * acc_bytes : 0,
+                          n.kv.parts > 1 ? (size_t)items_k * n.kv.parts * nw * 2 * acc_bytes : 0);
+  n.counters = std::max(n.q.parts > 1 ? items_q : 0, n.kv.parts > 1 ? items_k : 0) * nw;
+  return n;
+}
+
+muse_status check_workspace(void *ws, size_t have, size_t need) {
+  if (need == 0) return MUSE_OK;
+  if (!ws) return set_error(MUSE_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", need);
+  if ((uintptr_t)ws % 16) return set_error(MUSE_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (have < need) return set_error(MUSE_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed", have, need);
   return MUSE_OK;
 }
 
@@ -455,7 +398,7 @@ static muse_status qk_norm_rope_impl(const muse_attn_params *p, const muse_layou
   if (!k && k_rstd) return set_error(MUSE_ERR_INVALID_ARG, "k_rstd given without k");
   if (p->skip_qk_norm && (q_gain || k_gain || q_rstd || k_rstd))
     return set_error(MUSE_ERR_INVALID_ARG, "skip_qk_norm takes no gains and no rstd outputs");
-  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  s = check_rope_table(p, l, g, cos, sin, n_pos, (hipStream_t)stream);
   if (s != MUSE_OK) return s;
   const int64_t N = g.n_tokens;
   const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
@@ -521,13 +464,34 @@ extern "C" muse_status muse_qk_norm_rope_table(const muse_attn_params *p, const 
                            stream, true, theta);
 }
 
-extern "C" int32_t muse_attn_set_kv_split(int32_t mode) {
-  if (mode < 0) return -1;
-  return g_kv_split.exchange(mode);
+// Points a at the forward split's slots in the workspace and zeroes the
+// arrival counters on the stream (a workspace reused for another shape may
+// hold old slot values where this call's counters sit).
+static muse_status bind_fwd_split(AttnArgs &a, const SplitNeed &n, void *ws, hipStream_t stream) {
+  a.kv_parts = n.parts;
+  a.kv_span = n.span;
+  if (n.parts < 2) return MUSE_OK;
+  a.part_cnt = (uint32_t *)ws;
+  a.part_o = (float *)((char *)ws + ws_round((size_t)n.counters * 4));
+  return device_status(launch_zero_u32(a.part_cnt, n.counters, stream), "KV-split counter reset");
+}
+
+extern "C" muse_status muse_attn_fwd_workspace_size(const muse_attn_params *p, const muse_layout *l,
+                                                    size_t *bytes) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, nullptr, &g, false);
+  if (s != MUSE_OK) return s;
+  if (!bytes) return set_error(MUSE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = g.n_tokens == 0 ? 0 : fwd_split_need(attn_args(p, l, g), g, p->kv_split).bytes();
+  clear_error();
+  return MUSE_OK;
 }
 
 extern "C" muse_status muse_gqa_attn_fwd(const muse_attn_params *p, const muse_layout *l, const void *q_hat,
-                                         const void *k_hat, const void *v, void *o, float *lse, void *stream) {
+                                         const void *k_hat, const void *v, void *o, float *lse, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
   Geometry g;
@@ -536,19 +500,22 @@ extern "C" muse_status muse_gqa_attn_fwd(const muse_attn_params *p, const muse_l
   const int64_t N = g.n_tokens;
   if (N > 0 && (!q_hat || !k_hat || !v || !o))
     return set_error(MUSE_ERR_INVALID_ARG, "q_hat, k_hat, v and o are required");
+  AttnArgs a = attn_args(p, l, g);
+  const SplitNeed split = N > 0 ? fwd_split_need(a, g, p->kv_split) : SplitNeed{};
   s = check_disjoint({{q_hat, bf16_bytes(N, g.hq, g.d), "q_hat"}, {k_hat, bf16_bytes(N, g.hkv, g.d), "k_hat"},
                       {v, bf16_bytes(N, g.hkv, g.d), "v"}, layout_range(l, g, 0), layout_range(l, g, 1),
                       layout_range(l, g, 2)},
-                     {{o, bf16_bytes(N, g.hq, g.d), "o"}, {lse, N * g.hq * 4, "lse", 4}});
+                     {{o, bf16_bytes(N, g.hq, g.d), "o"}, {lse, N * g.hq * 4, "lse", 4},
+                      {split.bytes() ? workspace : nullptr, (int64_t)split.bytes(), "workspace"}});
   if (s != MUSE_OK) return s;
+  if ((s = check_workspace(workspace, workspace_bytes, split.bytes())) != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
-  AttnArgs a = attn_args(p, l, g);
   a.q = (const uint16_t *)q_hat;
   a.k = (const uint16_t *)k_hat;
   a.v = (const uint16_t *)v;
   a.o = (uint16_t *)o;
   a.lse = lse;
-  if ((s = attn_split(a, g, (hipStream_t)stream)) != MUSE_OK) return s;
+  if ((s = bind_fwd_split(a, split, workspace, (hipStream_t)stream)) != MUSE_OK) return s;
   return device_status(launch_attn_fwd(g.d, false, a, (hipStream_t)stream), "attention launch");
 }
 
@@ -572,7 +539,8 @@ extern "C" muse_status muse_out_norm_gate(const muse_attn_params *p, const muse_
 extern "C" muse_status muse_attn_fused_fwd(const muse_attn_params *p, const muse_layout *l, const void *q,
                                            const void *k_hat, const void *v, const void *gate,
                                            const float *q_gain, const float *cos, const float *sin,
-                                           int32_t n_pos, void *out, float *lse, void *stream) {
+                                           int32_t n_pos, void *out, float *lse, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
   if (p->skip_qk_norm) return set_error(MUSE_ERR_UNSUPPORTED, "the fused core normalises Q; skip_qk_norm is for muse_qk_norm_rope");
@@ -582,17 +550,20 @@ extern "C" muse_status muse_attn_fused_fwd(const muse_attn_params *p, const muse
   const int64_t N = g.n_tokens;
   if (N > 0 && (!q || !k_hat || !v || !gate || !out))
     return set_error(MUSE_ERR_INVALID_ARG, "q, k_hat, v, gate and out are required");
-  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  s = check_rope_table(p, l, g, cos, sin, n_pos, (hipStream_t)stream);
   if (s != MUSE_OK) return s;
+  AttnArgs a = attn_args(p, l, g);
+  const SplitNeed split = N > 0 ? fwd_split_need(a, g, p->kv_split) : SplitNeed{};
   const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
   s = check_disjoint({{q, bf16_bytes(N, g.hq, g.d), "q"}, {k_hat, bf16_bytes(N, g.hkv, g.d), "k_hat"},
                       {v, bf16_bytes(N, g.hkv, g.d), "v"}, {gate, bf16_bytes(N, g.hq, g.d), "gate"},
                       {q_gain, g.d * 4, "q_gain"}, {cos, tab, "cos"}, {sin, tab, "sin"},
                       layout_range(l, g, 0), layout_range(l, g, 1), layout_range(l, g, 2)},
-                     {{out, bf16_bytes(N, g.hq, g.d), "out"}, {lse, N * g.hq * 4, "lse", 4}});
+                     {{out, bf16_bytes(N, g.hq, g.d), "out"}, {lse, N * g.hq * 4, "lse", 4},
+                      {split.bytes() ? workspace : nullptr, (int64_t)split.bytes(), "workspace"}});
   if (s != MUSE_OK) return s;
+  if ((s = check_workspace(workspace, workspace_bytes, split.bytes())) != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
-  AttnArgs a = attn_args(p, l, g);
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k_hat;
   a.v = (const uint16_t *)v;
@@ -603,14 +574,15 @@ extern "C" muse_status muse_attn_fused_fwd(const muse_attn_params *p, const muse
   a.cos_tab = cos;
   a.sin_tab = sin;
   a.n_pos = n_pos;
-  if ((s = attn_split(a, g, (hipStream_t)stream)) != MUSE_OK) return s;
+  if ((s = bind_fwd_split(a, split, workspace, (hipStream_t)stream)) != MUSE_OK) return s;
   return device_status(launch_attn_fwd(g.d, true, a, (hipStream_t)stream), "fused attention launch");
 }
 
 extern "C" muse_status muse_attn_core_fwd(const muse_attn_params *p, const muse_layout *l, const void *q,
                                           const void *k, const void *v, const void *gate, const float *q_gain,
                                           const float *k_gain, const float *cos, const float *sin, int32_t n_pos,
-                                          void *k_hat_out, void *out, float *lse, void *stream) {
+                                          void *k_hat_out, void *out, float *lse, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
   if (p->skip_qk_norm) return set_error(MUSE_ERR_UNSUPPORTED, "the fused core normalises Q/K; skip_qk_norm is for muse_qk_norm_rope");
@@ -620,24 +592,27 @@ extern "C" muse_status muse_attn_core_fwd(const muse_attn_params *p, const muse_
   const int64_t N = g.n_tokens;
   if (N > 0 && (!q || !k || !v || !gate || !k_hat_out || !out))
     return set_error(MUSE_ERR_INVALID_ARG, "q, k, v, gate, k_hat_out and out are required");
-  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  s = check_rope_table(p, l, g, cos, sin, n_pos, (hipStream_t)stream);
   if (s != MUSE_OK) return s;
   const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
+  const size_t split_bytes = N > 0 ? fwd_split_need(attn_args(p, l, g), g, p->kv_split).bytes() : 0;
   s = check_disjoint(
       {{q, bf16_bytes(N, g.hq, g.d), "q"}, {k, bf16_bytes(N, g.hkv, g.d), "k"}, {v, bf16_bytes(N, g.hkv, g.d), "v"},
        {gate, bf16_bytes(N, g.hq, g.d), "gate"}, {q_gain, g.d * 4, "q_gain"}, {k_gain, g.d * 4, "k_gain"},
        {cos, tab, "cos"}, {sin, tab, "sin"}, layout_range(l, g, 0), layout_range(l, g, 1),
        layout_range(l, g, 2)},
       {{k_hat_out, bf16_bytes(N, g.hkv, g.d), "k_hat_out"}, {out, bf16_bytes(N, g.hq, g.d), "out"},
-       {lse, N * g.hq * 4, "lse", 4}});
+       {lse, N * g.hq * 4, "lse", 4}, {split_bytes ? workspace : nullptr, (int64_t)split_bytes, "workspace"}});
   if (s != MUSE_OK) return s;
+  if ((s = check_workspace(workspace, workspace_bytes, split_bytes)) != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
   // keys: norm + gain + RoPE once per key (the K-only pass of the Q/K kernel),
   // then attention with the query prologue and the norm/gate epilogue fused.
   s = muse_qk_norm_rope(p, l, nullptr, k, nullptr, k_gain, cos, sin, n_pos, nullptr, k_hat_out, nullptr,
                         nullptr, stream);
   if (s != MUSE_OK) return s;
-  return muse_attn_fused_fwd(p, l, q, k_hat_out, v, gate, q_gain, cos, sin, n_pos, out, lse, stream);
+  return muse_attn_fused_fwd(p, l, q, k_hat_out, v, gate, q_gain, cos, sin, n_pos, out, lse, workspace,
+                             workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- backward
@@ -645,24 +620,24 @@ extern "C" muse_status muse_attn_core_fwd(const muse_attn_params *p, const muse_
 namespace muse {
 namespace {
 
-constexpr size_t kWsAlign = 256;
-size_t ws_round(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
-
 size_t qk_bwd_partial_bytes(const Geometry &g, bool q_gain, bool k_gain) {
   int32_t qb = 0, kb = 0;
   qk_norm_bwd_blocks(g.d, g.n_tokens * g.hq, g.n_tokens * g.hkv, &qb, &kb);
   return ws_round((size_t)(q_gain ? qb : 0) * g.d * 4) + ws_round((size_t)(k_gain ? kb : 0) * g.d * 4);
 }
 
-// Core workspace: q_hat, k_hat, o, lse, d_o, delta, dq_hat, dk_hat, gain partials.
+// Core workspace: the attention splits' region (the recomputed forward's
+// and the attention backward's, used one after the other), then q_hat, k_hat,
+// o, lse, d_o, delta, dq_hat, dk_hat and the gain partials.
 struct CoreWs {
-  size_t q_hat, k_hat, o, lse, d_o, delta, dq_hat, dk_hat, part, total;
+  size_t split, q_hat, k_hat, o, lse, d_o, delta, dq_hat, dk_hat, part, total;
 };
-CoreWs core_ws(const Geometry &g) {
+CoreWs core_ws(const Geometry &g, size_t split_bytes) {
   CoreWs w;
   const size_t nq = (size_t)g.n_tokens * g.hq, nk = (size_t)g.n_tokens * g.hkv;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off += ws_round(bytes); return at; };
+  w.split = take(split_bytes);
   w.q_hat = take(nq * g.d * 2);
   w.k_hat = take(nk * g.d * 2);
   w.o = take(nq * g.d * 2);
@@ -674,14 +649,6 @@ CoreWs core_ws(const Geometry &g) {
   w.part = take(qk_bwd_partial_bytes(g, true, true));
   w.total = off;
   return w;
-}
-
-muse_status check_workspace(void *ws, size_t have, size_t need) {
-  if (need == 0) return MUSE_OK;
-  if (!ws) return set_error(MUSE_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", need);
-  if ((uintptr_t)ws % 16) return set_error(MUSE_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-  if (have < need) return set_error(MUSE_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed", have, need);
-  return MUSE_OK;
 }
 
 AttnBwdArgs attn_bwd_args(const muse_attn_params *p, const muse_layout *l, const Geometry &g) {
@@ -702,6 +669,27 @@ AttnBwdArgs attn_bwd_args(const muse_attn_params *p, const muse_layout *l, const
   a.dq_parts = a.dkv_parts = 1;
   a.lay = token_layout(l, g);
   return a;
+}
+
+// Split region of muse_attn_core_bwd: its forward recompute (when O and LSE
+// are not given) and its attention backward take turns in it.
+size_t core_split_bytes(const muse_attn_params *p, const muse_layout *l, const Geometry &g) {
+  if (g.n_tokens == 0) return 0;
+  return std::max(fwd_split_need(attn_args(p, l, g), g, p->kv_split).bytes(),
+                  bwd_split_need(attn_bwd_args(p, l, g), g, p->kv_split).bytes());
+}
+
+// Points a at the backward split's slots and zeroes its arrival counters on
+// the stream.
+muse_status bind_bwd_split(AttnBwdArgs &a, const BwdSplitNeed &n, void *ws, hipStream_t stream) {
+  a.dq_parts = n.q.parts;
+  a.dq_span = n.q.span;
+  a.dkv_parts = n.kv.parts;
+  a.dkv_span = n.kv.span;
+  if (n.bytes() == 0) return MUSE_OK;
+  a.part_cnt = (uint32_t *)ws;
+  a.part_acc = (float *)((char *)ws + ws_round((size_t)n.counters * 4));
+  return device_status(launch_zero_u32(a.part_cnt, n.counters, stream), "attention-backward split counter reset");
 }
 
 }  // namespace
@@ -745,9 +733,23 @@ extern "C" muse_status muse_attn_bwd_delta(const muse_attn_params *p, const muse
   return device_status(launch_out_norm_gate_bwd(g.d, a, (hipStream_t)stream), "attention delta launch");
 }
 
+extern "C" muse_status muse_gqa_attn_bwd_workspace_size(const muse_attn_params *p, const muse_layout *l,
+                                                        size_t *bytes) {
+  muse_status s = check_params(p);
+  if (s != MUSE_OK) return s;
+  Geometry g;
+  s = check_layout(l, p, nullptr, &g, false);
+  if (s != MUSE_OK) return s;
+  if (!bytes) return set_error(MUSE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = g.n_tokens == 0 ? 0 : bwd_split_need(attn_bwd_args(p, l, g), g, p->kv_split).bytes();
+  clear_error();
+  return MUSE_OK;
+}
+
 extern "C" muse_status muse_gqa_attn_bwd(const muse_attn_params *p, const muse_layout *l, const void *q_hat,
                                          const void *k_hat, const void *v, const void *d_o, const float *lse,
-                                         const float *delta, void *dq_hat, void *dk_hat, void *dv, void *stream) {
+                                         const float *delta, void *dq_hat, void *dk_hat, void *dv, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
   Geometry g;
@@ -756,14 +758,17 @@ extern "C" muse_status muse_gqa_attn_bwd(const muse_attn_params *p, const muse_l
   const int64_t N = g.n_tokens;
   if (N > 0 && (!q_hat || !k_hat || !v || !d_o || !lse || !delta || !dq_hat || !dk_hat || !dv))
     return set_error(MUSE_ERR_INVALID_ARG, "every tensor of the attention backward is required");
+  AttnBwdArgs a = attn_bwd_args(p, l, g);
+  const BwdSplitNeed split = N > 0 ? bwd_split_need(a, g, p->kv_split) : BwdSplitNeed{};
   const int64_t qb = bf16_bytes(N, g.hq, g.d), kb = bf16_bytes(N, g.hkv, g.d);
   s = check_disjoint({{q_hat, qb, "q_hat"}, {k_hat, kb, "k_hat"}, {v, kb, "v"}, {d_o, qb, "d_o"},
                       {lse, N * g.hq * 4, "lse", 4}, {delta, N * g.hq * 4, "delta", 4}, layout_range(l, g, 0),
                       layout_range(l, g, 1), layout_range(l, g, 2)},
-                     {{dq_hat, qb, "dq_hat"}, {dk_hat, kb, "dk_hat"}, {dv, kb, "dv"}});
+                     {{dq_hat, qb, "dq_hat"}, {dk_hat, kb, "dk_hat"}, {dv, kb, "dv"},
+                      {split.bytes() ? workspace : nullptr, (int64_t)split.bytes(), "workspace"}});
   if (s != MUSE_OK) return s;
+  if ((s = check_workspace(workspace, workspace_bytes, split.bytes())) != MUSE_OK) return s;
   if (N == 0) { clear_error(); return MUSE_OK; }
-  AttnBwdArgs a = attn_bwd_args(p, l, g);
   a.q = (const uint16_t *)q_hat;
   a.k = (const uint16_t *)k_hat;
   a.v = (const uint16_t *)v;
@@ -773,7 +778,7 @@ extern "C" muse_status muse_gqa_attn_bwd(const muse_attn_params *p, const muse_l
   a.dq = (uint16_t *)dq_hat;
   a.dk = (uint16_t *)dk_hat;
   a.dv = (uint16_t *)dv;
-  if ((s = attn_bwd_split(a, g, (hipStream_t)stream)) != MUSE_OK) return s;
+  if ((s = bind_bwd_split(a, split, workspace, (hipStream_t)stream)) != MUSE_OK) return s;
   return device_status(launch_attn_bwd(g.d, a, (hipStream_t)stream), "attention backward launch");
 }
 
@@ -782,7 +787,7 @@ extern "C" muse_status muse_qk_norm_rope_bwd_workspace_size(const muse_attn_para
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
   Geometry g;
-  s = check_layout(l, p, nullptr, &g);
+  s = check_layout(l, p, nullptr, &g, false);
   if (s != MUSE_OK) return s;
   if (!bytes) return set_error(MUSE_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = p->skip_qk_norm ? 0 : qk_bwd_partial_bytes(g, true, true);
@@ -810,7 +815,7 @@ extern "C" muse_status muse_qk_norm_rope_bwd(const muse_attn_params *p, const mu
     return set_error(MUSE_ERR_INVALID_ARG, "a gain is given without its tensor");
   if (p->skip_qk_norm && (q_gain || k_gain))
     return set_error(MUSE_ERR_INVALID_ARG, "skip_qk_norm takes no gains");
-  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  s = check_rope_table(p, l, g, cos, sin, n_pos, (hipStream_t)stream);
   if (s != MUSE_OK) return s;
   const int64_t N = g.n_tokens;
   const int64_t qb = bf16_bytes(N, g.hq, g.d), kb = bf16_bytes(N, g.hkv, g.d);
@@ -857,15 +862,16 @@ extern "C" muse_status muse_qk_norm_rope_bwd(const muse_attn_params *p, const mu
   return device_status(launch_qk_norm_rope_bwd(g.d, a, (hipStream_t)stream), "qk_norm_rope_bwd launch");
 }
 
+
 extern "C" muse_status muse_attn_core_bwd_workspace_size(const muse_attn_params *p, const muse_layout *l,
                                                          size_t *bytes) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
   Geometry g;
-  s = check_layout(l, p, nullptr, &g);
+  s = check_layout(l, p, nullptr, &g, false);
   if (s != MUSE_OK) return s;
   if (!bytes) return set_error(MUSE_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = core_ws(g).total;
+  *bytes = core_ws(g, core_split_bytes(p, l, g)).total;
   clear_error();
   return MUSE_OK;
 }
@@ -889,9 +895,9 @@ extern "C" muse_status muse_attn_core_bwd(const muse_attn_params *p, const muse_
     return set_error(MUSE_ERR_INVALID_ARG, "o and lse are given together (or both recomputed)");
   if ((q_gain != nullptr) != (dq_gain != nullptr) || (k_gain != nullptr) != (dk_gain != nullptr))
     return set_error(MUSE_ERR_INVALID_ARG, "a gain gradient is given exactly when its gain is");
-  s = check_rope_table(p, l, g, cos, sin, n_pos);
+  s = check_rope_table(p, l, g, cos, sin, n_pos, (hipStream_t)stream);
   if (s != MUSE_OK) return s;
-  const CoreWs w = core_ws(g);
+  const CoreWs w = core_ws(g, core_split_bytes(p, l, g));
   const int64_t qb = bf16_bytes(N, g.hq, g.d), kb = bf16_bytes(N, g.hkv, g.d);
   const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
   s = check_disjoint({{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {gate, qb, "gate"}, {q_gain, g.d * 4, "q_gain"},
@@ -912,14 +918,16 @@ extern "C" muse_status muse_attn_core_bwd(const muse_attn_params *p, const muse_
   if (!o) {
     o = ws + w.o;
     lse = (const float *)(ws + w.lse);
-    s = muse_gqa_attn_fwd(p, l, q_hat, k_hat, v, (void *)o, (float *)lse, stream);
+    s = muse_gqa_attn_fwd(p, l, q_hat, k_hat, v, (void *)o, (float *)lse, ws + w.split, w.q_hat - w.split,
+                          stream);
     if (s != MUSE_OK) return s;
   }
   void *d_o = ws + w.d_o, *dq_hat = ws + w.dq_hat, *dk_hat = ws + w.dk_hat;
   float *delta = (float *)(ws + w.delta);
   s = muse_out_norm_gate_bwd(p, l, o, gate, dout, d_o, dgate, delta, stream);
   if (s != MUSE_OK) return s;
-  s = muse_gqa_attn_bwd(p, l, q_hat, k_hat, v, d_o, lse, delta, dq_hat, dk_hat, dv, stream);
+  s = muse_gqa_attn_bwd(p, l, q_hat, k_hat, v, d_o, lse, delta, dq_hat, dk_hat, dv, ws + w.split,
+                        w.q_hat - w.split, stream);
   if (s != MUSE_OK) return s;
   return muse_qk_norm_rope_bwd(p, l, q, k, q_gain, k_gain, cos, sin, n_pos, dq_hat, dk_hat, dq, dk, dq_gain,
                                dk_gain, ws + w.part, w.total - w.part, stream);

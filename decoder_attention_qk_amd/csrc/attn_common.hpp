@@ -59,10 +59,14 @@ __device__ __forceinline__ bool split_sum(f32x16 (&acc)[R][C], float *slot0, int
       for (int i = 0; i < 16; ++i)
         __hip_atomic_store(mine + ((r * C + c) * 16 + i) * 64, acc[r][c][i], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+  // the signal fences keep the compiler from moving the relaxed atomics to
+  // other addresses across the wait (they emit no instruction)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   uint32_t prev = 0;
   if (lane == 0) prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __builtin_amdgcn_readfirstlane(prev);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   if (prev != (uint32_t)(nparts - 1)) return false;
   if (lane == 0) *cnt = 0u;
 #pragma unroll

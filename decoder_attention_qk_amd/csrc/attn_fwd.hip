@@ -49,6 +49,7 @@
 // padded keys of a BSHD batch (model page, MuseSparkTextModel.forward
 // attention_mask) are masked per tile, and a query left with no key gives
 // the zero row.
+#include <algorithm>
 #include <cmath>
 
 #include "attn_common.hpp"
@@ -491,11 +492,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       st(dst + DT * 16 * 64, m_run);
       st(dst + (DT * 16 + 1) * 64, l_run);
     }
+    // compiler-only fences: the relaxed atomics to other addresses stay on
+    // their side of the wait
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     uint32_t prev = 0;
     if (lane == 0)
       prev = __hip_atomic_fetch_add(a.part_cnt + item * NW + wave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __builtin_amdgcn_readfirstlane(prev);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (prev != (uint32_t)(nparts - 1)) return;
     if (lane == 0) a.part_cnt[item * NW + wave] = 0u;   // zero again for the next launch
     auto ld = [&](const float *p) __attribute__((always_inline)) {
@@ -595,7 +600,18 @@ hipError_t launch_one(const AttnArgs &a, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 int attn_columns_per_workgroup() { return COLS; }
 int attn_waves_per_workgroup() { return NW; }

@@ -10,4 +10,10 @@ muse_status set_error(muse_status s, const char *fmt, ...) __attribute__((format
 void clear_error();
 const char *last_error();
 
+// MUSE_DEBUG_VALIDATE=1 checks of device layout arrays (debug_check.cpp):
+// each copies its array to the host, synchronising `stream` (a hipStream_t).
+bool debug_validate_enabled();
+muse_status debug_check_cu_seqlens(const muse_layout *layout, void *stream);
+muse_status debug_check_positions(const int32_t *position_ids, int64_t n_tokens, int32_t n_pos, void *stream);
+
 }  // namespace muse

@@ -133,7 +133,7 @@ struct AttnArgs {
   int32_t kv_parts;        // 1 .. kMaxKvParts
   int32_t kv_span;
   float *part_o;           // [items][kv_parts][waves] slots: O fragment, reference, sum (per lane)
-  uint32_t *part_cnt;      // [items][waves] arrivals; zero between launches
+  uint32_t *part_cnt;      // [items][waves] arrivals; zeroed before the launch, zero after it
   TokenLayout lay;
 };
 
@@ -161,7 +161,7 @@ struct AttnBwdArgs {
   int32_t dq_parts, dq_span;
   int32_t dkv_parts, dkv_span;
   float *part_acc;             // [items][parts][waves] slots of R x C x 16 x 64 floats
-  uint32_t *part_cnt;          // [items][waves] arrivals; zero between launches
+  uint32_t *part_cnt;          // [items][waves] arrivals; zeroed before the launch, zero after it
   TokenLayout lay;
 };
 
@@ -169,6 +169,8 @@ hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t stream);
 hipError_t launch_qk_norm_rope(int head_dim, const QkNormArgs &a, hipStream_t stream);
 hipError_t launch_out_norm_gate(int head_dim, const OutGateArgs &a, hipStream_t stream);
 hipError_t launch_attn_fwd(int head_dim, bool fused, const AttnArgs &a, hipStream_t stream);
+// zeroes n 32-bit words (the splits' arrival counters) in stream order
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t stream);
 hipError_t launch_out_norm_gate_bwd(int head_dim, const OutGateBwdArgs &a, hipStream_t stream);
 // blocks the Q/K backward uses for q_rows / k_rows rows (the partial buffers' first dimension)
 void qk_norm_bwd_blocks(int head_dim, int64_t q_rows, int64_t k_rows, int32_t *q_blocks, int32_t *k_blocks);

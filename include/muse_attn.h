@@ -32,17 +32,26 @@
  *   are rejected with MUSE_ERR_INVALID_ARG.
  * - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
  *   only enqueues work on that stream and returns without synchronising.
- * - The caller owns every buffer.  The library allocates no memory, keeps no
- *   state between calls and is reentrant.  Outputs must not overlap any input
- *   or other output of the same call (the pages return independent tensors);
+ * - The caller owns every buffer, scratch memory included: entry points that
+ *   need scratch take a caller workspace (`workspace`, `workspace_bytes`) of
+ *   at least the size the matching *_workspace_size query reports for the
+ *   same params, layout and current device (0 bytes: NULL is accepted).  A
+ *   workspace is 16-byte aligned, needs no initial contents, is overwritten
+ *   by the call, and must not overlap any input or output; calls that share
+ *   one must not overlap in time (stream order suffices).  The library
+ *   allocates no device or pinned memory, keeps no state between calls (a
+ *   thread's last error message aside) and is reentrant.  Outputs must not overlap any input or
+ *   other output of the same call (the pages return independent tensors);
  *   overlapping ranges are rejected with MUSE_ERR_INVALID_ARG.
  * - Arguments are validated on the host before anything is enqueued.  An
  *   error leaves every output untouched.  muse_last_error() gives a message.
- * - Setting MUSE_DEBUG_VALIDATE=1 in the environment makes THD calls copy
- *   cu_seqlens to the host (synchronising the stream) and check it with
- *   muse_validate_cu_seqlens; without it, a malformed cu_seqlens gives
- *   unspecified results but every memory access stays inside the buffers
- *   implied by the host-visible sizes.
+ * - Setting MUSE_DEBUG_VALIDATE=1 in the environment makes calls copy the
+ *   device layout arrays to the host -- synchronising the stream, the only
+ *   case in which a call waits -- and check them: cu_seqlens with
+ *   muse_validate_cu_seqlens, and position_ids (where a RoPE table is read)
+ *   against [0, n_pos).  Without it, a malformed cu_seqlens or an
+ *   out-of-range position gives unspecified results but every memory access
+ *   stays inside the buffers implied by the host-visible sizes.
  */
 #ifndef MUSE_ATTN_H
 #define MUSE_ATTN_H
@@ -95,6 +104,23 @@ typedef enum {
  *                     rotates the projected Q/K); gains and rstd outputs must then
  *                     be NULL.  The fused entry points, which normalise the query
  *                     in their prologue, return UNSUPPORTED for it.  Zero: normalise.
+ * kv_split            split policy of the attention kernels for grids too small
+ *                     to fill the device (a tuning knob, not from the pages): the
+ *                     forward and the backward's dQ kernel cut a work item's key
+ *                     tiles, the backward's dK/dV kernel a key block's (query
+ *                     tile, head) steps, into parts run by separate workgroups
+ *                     and summed in part order.
+ *                       0  automatic (the default): split only grids with fewer
+ *                          work items than resident workgroup slots of the current
+ *                          device (two per CU; one for the D = 128 dK/dV kernel),
+ *                          into parts of at least 4 steps (at most 4 parts; 8 for
+ *                          dK/dV);
+ *                       1  never split;
+ *                       n >= 2  split every work item of two or more steps into
+ *                          min(n, 8) parts (a tuning and testing aid).
+ *                     Splitting reorders the sums (results move within rounding);
+ *                     a given policy, shape and device always give the same bits,
+ *                     fused and unfused alike.  Negative: INVALID_ARG.
  */
 typedef struct {
   int32_t head_dim;
@@ -110,6 +136,7 @@ typedef struct {
   float gain_center;
   int32_t bidirectional;
   int32_t skip_qk_norm;
+  int32_t kv_split;
 } muse_attn_params;
 
 /*
@@ -126,7 +153,8 @@ typedef struct {
  *       position_ids).  NULL means the implicit positions: the index inside the
  *       BSHD row, or inside the THD segment (restarting at 0).  Positions must
  *       lie in [0, n_pos) of the cos/sin table; out-of-range ids are clamped
- *       into it (memory stays safe, the result is unspecified).  Masking
+ *       into it (memory stays safe, the result is unspecified;
+ *       MUSE_DEBUG_VALIDATE=1 rejects them with INVALID_ARG).  Masking
  *       always uses the token's index inside its row/segment.
  * attention_mask: optional device uint8 [batch, seqlen] token validity for
  *       BSHD (model page, MuseSparkTextModel.forward attention_mask: nonzero =
@@ -257,20 +285,28 @@ muse_status muse_qk_norm_rope_table(const muse_attn_params *params, const muse_l
  * q_hat [N, Hq, D], k_hat [N, Hkv, D], v [N, Hkv, D]: bf16 in.
  * o     [N, Hq, D] bf16 out.  lse: optional fp32 [N, Hq] out (natural log).
  *
- * Small grids (fewer than two work items of 128 query columns per CU, e.g.
- * one GPU's share of a head-sharded layer) split each item's keys into parts
- * that run side by side and are combined in a fixed order (see
- * muse_attn_set_kv_split).  Those calls use a device buffer the library keeps
- * per (device, stream), allocated (and its counters zeroed) on the first call
- * of a shape that needs more than it holds; that call synchronises the stream
- * and must not be under graph capture (UNSUPPORTED).  A captured graph that
- * takes the split path uses its capturing stream's buffer: do not replay it
- * concurrently with other calls on that stream.
- * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}), DEVICE.
+ * Small grids split each work item's keys into parts (params->kv_split)
+ * whose partial results go through the workspace: workspace_bytes >=
+ * muse_attn_fwd_workspace_size(params, layout) (0 when the call does not
+ * split; then workspace may be NULL).  The partial slots need no initial
+ * contents; the call zeroes its arrival counters on the stream first.
+ * Errors: INVALID_ARG (also a missing, misaligned or too small workspace),
+ * UNSUPPORTED (D not in {64,128}), DEVICE.
  */
 muse_status muse_gqa_attn_fwd(const muse_attn_params *params, const muse_layout *layout,
                               const void *q_hat, const void *k_hat, const void *v, void *o,
-                              float *lse, void *stream);
+                              float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes the attention forward (muse_gqa_attn_fwd,
+ * muse_attn_fused_fwd, muse_attn_core_fwd) needs for params and layout on
+ * the current device: the KV-split partial slots and arrival counters, 0 when
+ * the split policy leaves the grid whole.
+ * Errors: as the parameter and layout checks of muse_gqa_attn_fwd; INVALID_ARG
+ * for a NULL bytes.
+ */
+muse_status muse_attn_fwd_workspace_size(const muse_attn_params *params, const muse_layout *layout,
+                                         size_t *bytes);
 
 /*
  * Parameter-free output RMSNorm times the sigmoid output gate (layers page,
@@ -299,13 +335,14 @@ muse_status muse_out_norm_gate(const muse_attn_params *params, const muse_layout
  * k_hat_out [N, Hkv, D] bf16 out: the normalised, rotated keys (what a KV cache
  *           keeps).  Required: the attention reads it back.
  * out       [N, Hq, D] bf16 out.   lse: optional fp32 [N, Hq] out.
+ * workspace, workspace_bytes: as muse_gqa_attn_fwd (muse_attn_fwd_workspace_size).
  * Errors: as the three calls above.
  */
 muse_status muse_attn_core_fwd(const muse_attn_params *params, const muse_layout *layout,
                                const void *q, const void *k, const void *v, const void *gate,
                                const float *q_gain, const float *k_gain, const float *cos,
                                const float *sin, int32_t n_pos, void *k_hat_out, void *out,
-                               float *lse, void *stream);
+                               float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The attention kernel of muse_attn_core_fwd on its own: the query norm/RoPE
@@ -315,13 +352,14 @@ muse_status muse_attn_core_fwd(const muse_attn_params *params, const muse_layout
  *
  * q, gate [N, Hq, D]; k_hat, v [N, Hkv, D]: bf16 in.  q_gain, cos, sin, n_pos
  * as in muse_qk_norm_rope (Q side).  out [N, Hq, D] bf16 out; lse optional
- * fp32 [N, Hq] out.
+ * fp32 [N, Hq] out.  workspace, workspace_bytes: as muse_gqa_attn_fwd.
  * Errors: as muse_gqa_attn_fwd, plus the table rules of muse_qk_norm_rope.
  */
 muse_status muse_attn_fused_fwd(const muse_attn_params *params, const muse_layout *layout,
                                 const void *q, const void *k_hat, const void *v, const void *gate,
                                 const float *q_gain, const float *cos, const float *sin,
-                                int32_t n_pos, void *out, float *lse, void *stream);
+                                int32_t n_pos, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * ---------------------------------------------------------------- backward
@@ -332,10 +370,9 @@ muse_status muse_attn_fused_fwd(const muse_attn_params *params, const muse_layou
  * the Q/K-dtype rotation (upcast_rope = 0), by their bf16 casts (the bf16
  * roundings of its products and sums differentiated as the identity).
  * Entry points that
- * need scratch memory take a caller-owned workspace (16-byte aligned, at
- * least the size the matching *_workspace_size call reports); its contents
- * are overwritten, and calls that share a workspace must not overlap in time.
- * Results are deterministic: no atomics, fixed reduction orders.
+ * need scratch memory take a caller-owned workspace (see the conventions).
+ * Results are deterministic: fixed reduction orders (a split's arrival
+ * counters only pick which part sums the others, in part order).
  */
 
 /*
@@ -367,12 +404,16 @@ muse_status muse_attn_bwd_delta(const muse_attn_params *params, const muse_layou
  * q_hat [N, Hq, D], k_hat, v [N, Hkv, D], d_o [N, Hq, D] bf16 in; lse (natural
  * log, from the forward) and delta fp32 [N, Hq] in; dq_hat [N, Hq, D], dk_hat,
  * dv [N, Hkv, D] bf16 out.  A padded key gets zero gradients.
+ * workspace: muse_gqa_attn_bwd_workspace_size bytes (the split's partial sums
+ * and arrival counters; 0 when params->kv_split leaves both kernels whole).
  * Errors: INVALID_ARG, UNSUPPORTED (D not in {64,128}), DEVICE.
  */
 muse_status muse_gqa_attn_bwd(const muse_attn_params *params, const muse_layout *layout,
                               const void *q_hat, const void *k_hat, const void *v, const void *d_o,
                               const float *lse, const float *delta, void *dq_hat, void *dk_hat,
-                              void *dv, void *stream);
+                              void *dv, void *workspace, size_t workspace_bytes, void *stream);
+muse_status muse_gqa_attn_bwd_workspace_size(const muse_attn_params *params,
+                                             const muse_layout *layout, size_t *bytes);
 
 /*
  * Backward of muse_qk_norm_rope.  For each row: g = the FP32 inverse rotation
@@ -429,25 +470,6 @@ muse_status muse_attn_core_bwd_workspace_size(const muse_attn_params *params,
  */
 muse_status muse_validate_cu_seqlens(const int32_t *cu_seqlens_host, int32_t num_segments,
                                      int32_t total_tokens, int32_t max_seqlen);
-
-/*
- * Split policy of the attention kernels for small grids (process-wide): the
- * forward (muse_gqa_attn_fwd, muse_attn_fused_fwd, muse_attn_core_fwd) and
- * the backward's dQ kernel split a work item's key tiles; the backward's
- * dK/dV kernel (muse_gqa_attn_bwd, muse_attn_core_bwd) splits a key block's
- * (query tile, head) steps.
- *   0  automatic (default): split only grids with fewer work items than
- *      resident workgroup slots (two per CU; one for the D = 128 dK/dV
- *      kernel), into parts of at least 4 steps (at most 4 parts; 8 for dK/dV);
- *   1  never split;
- *   n >= 2  split every work item with two or more steps into min(n, 8)
- *      parts (a tuning and testing aid).
- * Splitting reorders the sums (results move within rounding); a given policy
- * and shape always give the same bits, fused and unfused alike.  The backward
- * split uses the same per-(device, stream) buffer as the forward's.
- * Returns the previous policy, or -1 (nothing changed) when mode < 0.
- */
-int32_t muse_attn_set_kv_split(int32_t mode);
 
 /* Static name of a status code. */
 const char *muse_status_string(muse_status status);

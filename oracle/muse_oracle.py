@@ -67,6 +67,7 @@ __all__ = [
     "visible_mask",
     "attention",
     "attention_rows",
+    "attention_rows_grouped",
     "out_norm_gate",
     "Segments",
     "attn_core",
@@ -394,6 +395,46 @@ def attention_rows(q_hat_rows, k_hat, v, segments: Segments, rows, *, num_heads,
     return round_bf16(o), lse
 
 
+def attention_rows_grouped(q_hat_rows, k_hat, v, segments: Segments, rows, *, num_heads, window=0, scaling,
+                           causal=True, key_valid=None, block=64):
+    """attention_rows for many rows at once: the same masked softmax of each
+    selected (token, head) row over its segment's keys (layers page,
+    MuseSparkAttention; model page, _causal_mask), evaluated for up to
+    ``block`` rows of one (segment, KV head) together.  A block's keys are the
+    run of its segment that holds every key some row of the block sees (for
+    causal rows: from the earliest window start to the latest query); keys
+    outside a row's visible set get probability zero exactly, as in the plain
+    definition.  Returns (bf16(o) [len(rows), D], lse [len(rows)])."""
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    groups = num_heads // k_hat.shape[1]
+    o = np.zeros((len(rows), k_hat.shape[2]))
+    lse = np.zeros(len(rows))
+    by_unit = {}
+    for r, (t, h) in enumerate(rows):
+        s0, length = segments.locate(int(t))
+        by_unit.setdefault((s0, length, int(h) // groups), []).append(r)
+    for (s0, length, g), idx in by_unit.items():
+        idx.sort(key=lambda r: int(rows[r][0]))
+        kok_seg = None if key_valid is None else np.asarray(key_valid)[s0:s0 + length]
+        for b0 in range(0, len(idx), block):
+            sel = idx[b0:b0 + block]
+            qpos = np.array([int(rows[r][0]) - s0 for r in sel])
+            if causal:
+                lo = max(0, int(qpos.min()) - window + 1) if window and window > 0 else 0
+                hi = int(qpos.max()) + 1
+            else:
+                lo, hi = 0, length
+            qb = np.stack([np.asarray(q_hat_rows[r], dtype=np.float64) for r in sel])
+            kok = None if kok_seg is None else kok_seg[lo:hi]
+            # positions shifted by lo: visibility depends only on differences
+            ob, lb = _attend_block(qb, k_hat[s0 + lo:s0 + hi, g], v[s0 + lo:s0 + hi, g], qpos - lo, window,
+                                   scaling, causal, kok)
+            o[sel] = ob
+            lse[sel] = lb
+    return round_bf16(o), lse
+
+
 # --------------------------------------------------------------------------
 # Output norm and gate -- layers page, _output_norm_gate_core (parameter-free
 # output RMSNorm, sigmoid gate with the output's shape, gated output in the
@@ -438,7 +479,8 @@ def attn_core(q, k, v, gate, segments: Segments, *, theta, eps, out_eps, scaling
 
 def attn_core_rows(q_rows, k, v, gate_rows, segments: Segments, rows, *, num_heads, theta, eps,
                    out_eps, scaling, window=0, use_rope=True, q_gain=None, k_gain=None, gain_center=1.0,
-                   query_scale=1.0, position_ids=None, upcast_rope=True, causal=True, key_valid=None):
+                   query_scale=1.0, position_ids=None, upcast_rope=True, causal=True, key_valid=None,
+                   grouped=False):
     """The full forward for selected (token, head) rows only.
 
     ``q_rows``/``gate_rows`` [R, D] hold the query and gate values of the R
@@ -459,8 +501,9 @@ def attn_core_rows(q_rows, k, v, gate_rows, segments: Segments, rows, *, num_hea
                     use_rope, qc, qs, upcast_rope)
     k1, _ = rms_norm(k, eps, k_gain, gain_center)
     k_hat = rope_rotate(k1, kc[:, None, :], ks[:, None, :], upcast_rope) if use_rope else k1
-    o, lse = attention_rows(q_hat, k_hat, v, segments, rows, num_heads=num_heads,
-                            window=window, scaling=scaling, causal=causal, key_valid=key_valid)
+    attend = attention_rows_grouped if grouped else attention_rows
+    o, lse = attend(q_hat, k_hat, v, segments, rows, num_heads=num_heads, window=window, scaling=scaling,
+                    causal=causal, key_valid=key_valid)
     out, o_rstd = out_norm_gate(o, np.asarray(gate_rows, dtype=np.float64), out_eps)
     return dict(q_hat=q_hat, k_hat=k_hat, o=o, lse=lse, o_rstd=o_rstd, out=out)
 

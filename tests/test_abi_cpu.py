@@ -75,10 +75,11 @@ def _bshd(batch=1, seqlen=16):
     return m.c_layout(batch, seqlen, None, batch, 0, 0, None)
 
 
-def _attn(p, lay, q=FAKE, k=FAKE + (1 << 24), v=FAKE + (2 << 24), o=FAKE + (3 << 24), lse=None):
+def _attn(p, lay, q=FAKE, k=FAKE + (1 << 24), v=FAKE + (2 << 24), o=FAKE + (3 << 24), lse=None, ws=None,
+          wsb=0):
     return m.library().muse_gqa_attn_fwd(ctypes.byref(p) if p is not None else None,
                                          ctypes.byref(lay) if lay is not None else None,
-                                         q, k, v, o, lse, None)
+                                         q, k, v, o, lse, ws, wsb, None)
 
 
 def test_null_params_and_layout():
@@ -91,7 +92,7 @@ def test_null_params_and_layout():
     (dict(num_heads=6, num_key_value_heads=4), 1), (dict(scaling=0.0), 1),
     (dict(scaling=float("nan")), 1), (dict(qk_eps=-1.0), 1), (dict(out_eps=float("inf")), 1),
     (dict(query_scale=float("inf")), 1), (dict(gain_center=float("nan")), 1),
-    (dict(bidirectional=1, sliding_window=8), 1),
+    (dict(bidirectional=1, sliding_window=8), 1), (dict(kv_split=-1), 1),
     (dict(head_dim=96), 2), (dict(head_dim=256), 2),
 ])
 def test_bad_params(kw, status):
@@ -203,7 +204,7 @@ def test_skip_qk_norm_rules():
     # the fused core normalises the query in its prologue
     st = lib.muse_attn_fused_fwd(ctypes.byref(p), ctypes.byref(lay), FAKE, FAKE + (1 << 24),
                                  FAKE + (2 << 24), FAKE + (3 << 24), None, FAKE + (4 << 24),
-                                 FAKE + (5 << 24), 16, FAKE + (6 << 24), None, None)
+                                 FAKE + (5 << 24), 16, FAKE + (6 << 24), None, None, 0, None)
     assert st == 2
 
 
@@ -244,9 +245,83 @@ def test_backward_argument_rules():
     assert core(pp=_params(skip_qk_norm=1)) == 2
     # the attention backward needs every tensor
     st = lib.muse_gqa_attn_bwd(ctypes.byref(p), ctypes.byref(lay), A[0], A[1], A[2], A[3], A[4], None,
-                               A[6], A[7], A[8], None)
+                               A[6], A[7], A[8], None, 0, None)
     assert st == 1
     # and the Q/K backward takes a tensor's three buffers together
     st = lib.muse_qk_norm_rope_bwd(ctypes.byref(p), ctypes.byref(lay), A[0], None, None, None, A[4], A[5], 16,
                                    None, None, A[7], None, None, None, None, 0, None)
     assert st == 1
+
+
+def _size(fn, p, lay):
+    size = ctypes.c_size_t(12345)
+    assert fn(ctypes.byref(p), ctypes.byref(lay), ctypes.byref(size)) == 0
+    return size.value
+
+
+def test_split_workspace_rules():
+    """The KV split keeps its partial slots and counters in the caller's
+    workspace: a forced split (kv_split >= 2) needs one, sized by the query,
+    and a call without it, with too little, misaligned or overlapping an
+    input is rejected before any launch."""
+    lib = m.library()
+    lay = _bshd(1, 1000)                                   # 8 query blocks, up to 16 key tiles each
+    whole = _size(lib.muse_attn_fwd_workspace_size, _params(kv_split=1), lay)
+    assert whole == 0
+    p = _params(kv_split=3)
+    need = _size(lib.muse_attn_fwd_workspace_size, p, lay)
+    # counters (items x 4 waves) plus a slot per (item, part, wave) of 130 x 64 floats
+    items = 8 * 2
+    assert need >= items * 3 * 4 * (128 // 32 * 16 + 2) * 64 * 4 + items * 4 * 4
+    ws = FAKE + (8 << 24)
+    assert _attn(p, lay, ws=None, wsb=0) == 1
+    assert "workspace" in lib.muse_last_error().decode()
+    assert _attn(p, lay, ws=ws, wsb=need - 1) == 1
+    assert _attn(p, lay, ws=ws + 8, wsb=need) == 1
+    assert "aligned" in lib.muse_last_error().decode()
+    assert _attn(p, lay, ws=FAKE + (1 << 24) - 256, wsb=need) == 1   # overlaps k
+    assert "overlaps" in lib.muse_last_error().decode()
+    # the fused entry points take the same workspace
+    st = lib.muse_attn_fused_fwd(ctypes.byref(p), ctypes.byref(lay), FAKE, FAKE + (1 << 24), FAKE + (2 << 24),
+                                 FAKE + (3 << 24), None, FAKE + (4 << 24), FAKE + (5 << 24), 1000,
+                                 FAKE + (6 << 24), None, None, 0, None)
+    assert st == 1 and "workspace" in lib.muse_last_error().decode()
+    st = lib.muse_attn_core_fwd(ctypes.byref(p), ctypes.byref(lay), FAKE, FAKE + (1 << 24), FAKE + (2 << 24),
+                                FAKE + (3 << 24), None, None, FAKE + (4 << 24), FAKE + (5 << 24), 1000,
+                                FAKE + (7 << 24), FAKE + (6 << 24), None, ws, need - 16, None)
+    assert st == 1 and "workspace" in lib.muse_last_error().decode()
+
+
+def test_backward_split_workspace_rules():
+    lib = m.library()
+    lay = _bshd(1, 1000)
+    assert _size(lib.muse_gqa_attn_bwd_workspace_size, _params(kv_split=1), lay) == 0
+    p = _params(kv_split=4)
+    need = _size(lib.muse_gqa_attn_bwd_workspace_size, p, lay)
+    assert need > 0
+    A = [FAKE + (i << 24) for i in range(12)]
+
+    def bwd(ws, wsb):
+        return lib.muse_gqa_attn_bwd(ctypes.byref(p), ctypes.byref(lay), A[0], A[1], A[2], A[3], A[4], A[5],
+                                     A[6], A[7], A[8], ws, wsb, None)
+    assert bwd(None, 0) == 1
+    assert bwd(A[9], need - 1) == 1
+    assert "workspace" in lib.muse_last_error().decode()
+    # the core backward's workspace holds the split region besides its tensors
+    core_split = _size(lib.muse_attn_core_bwd_workspace_size, p, lay)
+    core_whole = _size(lib.muse_attn_core_bwd_workspace_size, _params(kv_split=1), lay)
+    assert core_split >= core_whole + need
+
+
+def test_sources_allocate_nothing():
+    """No allocation anywhere in the library's sources, and the only
+    synchronisation is the opt-in debug check's."""
+    csrc = os.path.join(ROOT, "decoder_attention_qk_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        text = re.sub(r"//[^\n]*", "", open(os.path.join(csrc, name)).read())
+        for call in ("hipMalloc", "hipFree", "hipHostMalloc", "hipMallocAsync", "hipExtMallocWithFlags",
+                     "malloc(", "hipHostRegister"):
+            assert call not in text, (name, call)
+        if name != "debug_check.cpp":
+            for call in ("hipStreamSynchronize", "hipDeviceSynchronize", "hipEventSynchronize", "hipMemcpy"):
+                assert call not in text, (name, call)

@@ -671,6 +671,49 @@ def test_core_rows_match_full_core():
     np.testing.assert_array_equal(part["k_hat"], full["k_hat"])
 
 
+@pytest.mark.parametrize("causal,window,valid", [(True, 0, False), (True, 1, False), (True, 3, False),
+                                                  (True, 7, True), (False, 0, False), (False, 0, True)])
+def test_grouped_rows_brute_force(causal, window, valid):
+    """The grouped row evaluation against pure-Python softmax on rows spread
+    over segments of mixed lengths (one of length 1), heads of several KV
+    groups, blocks of a few rows, with and without padded keys."""
+    rng = np.random.default_rng(31 + window + 2 * causal + 5 * valid)
+    lens = [13, 1, 22, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    n, hq, hkv, d = cu[-1], 6, 2, 5
+    q = _bf16(rng.standard_normal((n, hq, d)))
+    k = _bf16(rng.standard_normal((n, hkv, d)))
+    v = _bf16(rng.standard_normal((n, hkv, d)))
+    ok = rng.random(n) > 0.3 if valid else None
+    ro, rl = _brute_attention(q, k, v, list(zip(cu[:-1], lens)), window, 0.55, causal=causal, valid=ok)
+    rows = [(int(t), int(h)) for t in rng.permutation(n)[:30] for h in rng.choice(hq, 2, replace=False)]
+    qr = np.stack([q[t, h] for t, h in rows])
+    go, gl = O.attention_rows_grouped(qr, k, v, O.Segments.thd(cu), rows, num_heads=hq, window=window,
+                                      scaling=0.55, causal=causal, key_valid=ok, block=3)
+    for r, (t, h) in enumerate(rows):
+        np.testing.assert_array_equal(go[r], _bf16(ro[t, h]))
+        assert gl[r] == rl[t, h] or abs(gl[r] - rl[t, h]) <= 1e-13 * max(1.0, abs(rl[t, h]))
+
+
+def test_grouped_rows_match_per_row_evaluation_at_size():
+    # many rows of a longer sequence with a window: the grouped blocks span
+    # several windows
+    rng = np.random.default_rng(77)
+    n, hq, hkv, d = 700, 8, 2, 16
+    q = _bf16(rng.standard_normal((n, hq, d)))
+    k = _bf16(rng.standard_normal((n, hkv, d)))
+    v = _bf16(rng.standard_normal((n, hkv, d)))
+    seg = O.Segments.bshd(2, 350)
+    rows = [(int(t), int(rng.integers(hq))) for t in range(0, n, 3)]
+    qr = np.stack([q[t, h] for t, h in rows])
+    for window in (0, 40):
+        a, la = O.attention_rows(qr, k, v, seg, rows, num_heads=hq, window=window, scaling=0.25)
+        b, lb = O.attention_rows_grouped(qr, k, v, seg, rows, num_heads=hq, window=window, scaling=0.25)
+        assert np.max(np.abs(a - b)) <= 2.0 ** -8 * np.max(np.abs(a))   # fp64 summation order only
+        assert np.mean(a == b) > 0.999
+        np.testing.assert_allclose(la, lb, rtol=1e-12, atol=1e-12)
+
+
 def test_rope_rotations_compose():
     # R(a) R(b) = R(a + b): two rotations by the table rows of positions a and b
     # equal one rotation by the row of a + b, up to the FP32 table and the two

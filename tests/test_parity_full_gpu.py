@@ -1,7 +1,9 @@
 """Full-size workloads on the GPU, in the launch configuration the benchmark
-times (the fused core), checked against the oracle on sampled rows: every
+times (the fused core), checked against the oracle on sampled rows: one row
+of every attention work item (segment, block of query tokens, KV head), every
 segment's first/last rows, rows around each window edge and random rows over
-all heads.  The normalised keys (a full output) are checked everywhere."""
+all heads (the sequences past 32k: all but the work-item rows).  The
+normalised keys (a full output) are checked everywhere."""
 
 import numpy as np
 import pytest
@@ -55,13 +57,14 @@ def test_full_size_sampled_rows(name, layer):
                                            case.gate, case.q_gain, case.k_gain, case.cos, case.sin,
                                            want_lse=True)
     torch.cuda.synchronize()
-    rows = sample_rows(case.segs, w.num_heads, case.x["window"], n_random=192, seed=layer)
+    rows = sample_rows(case.segs, w.num_heads, case.x["window"], n_random=192, seed=layer,
+                       num_kv_heads=None if name in LONG else w.num_kv_heads)
     tok = np.array([t for t, _ in rows])
     hd = np.array([h for _, h in rows])
     kw = case.oracle_kw()
     ref = O.attn_core_rows(bits_f64(case.x["q"][tok, hd]), bits_f64(case.x["k"]),
                            bits_f64(case.x["v"]), bits_f64(case.x["gate"][tok, hd]), case.segs,
-                           rows, num_heads=w.num_heads, **kw)
+                           rows, num_heads=w.num_heads, grouped=True, **kw)
     ti, hi = torch.from_numpy(tok).cuda(), torch.from_numpy(hd).cuda()
     st = check_bf16(f64(out[ti, hi]), ref["out"], what=f"{name} L{layer} out rows")
     sk = check_bf16(f64(k_hat), ref["k_hat"], what=f"{name} L{layer} k_hat")
@@ -70,8 +73,9 @@ def test_full_size_sampled_rows(name, layer):
     q_hat, _, _, _ = m.muse_qk_norm_rope(case.params, case.layout, case.q, None, case.q_gain, None,
                                          case.cos, case.sin)
     torch.cuda.synchronize()
-    _, rl = O.attention_rows(f64(q_hat[ti, hi]), f64(k_hat), bits_f64(case.x["v"]), case.segs, rows,
-                             num_heads=w.num_heads, window=case.x["window"], scaling=case.scaling)
+    _, rl = O.attention_rows_grouped(f64(q_hat[ti, hi]), f64(k_hat), bits_f64(case.x["v"]), case.segs, rows,
+                                     num_heads=w.num_heads, window=case.x["window"], scaling=case.scaling)
     check_fp32(f64(lse[ti, hi]), rl, floor=1.0, what=f"{name} L{layer} lse rows")
     del q_hat
-    print(f"[full] {name} L{layer}: {len(rows)} rows, out max err {st['max_err']:.3g}", flush=True)
+    print(f"[full] {name} L{layer}: {len(rows)} rows, out row err {st['max_err']:.4f}, "
+          f"elem err {st['elem_err']:.4f}", flush=True)

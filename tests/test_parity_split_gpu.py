@@ -1,9 +1,12 @@
 """GPU parity of the attention forward's KV split (a work item's key tiles cut
 into parts run by separate workgroups and combined per wave in part order).
 Forced splits of small cases against the oracle, fused == unfused bitwise
-under the split, repeat runs bitwise equal (the arrival counters return to
-zero), every output row written, and the automatic split of a grid too small
-to fill the device."""
+under the split, repeat runs bitwise equal, every output row written, the
+automatic split of a grid too small to fill the device, the split policy as a
+per-call parameter, a caller workspace reused across shapes, and a split call
+captured in a HIP graph."""
+
+import dataclasses
 
 import numpy as np
 import pytest
@@ -36,13 +39,16 @@ def _gpu():
     m.library()
 
 
+def _with_split(case, mode):
+    """The case with the per-call split policy `mode` in its params."""
+    case.params = dataclasses.replace(case.params, kv_split=mode)
+    return case
+
+
 @pytest.fixture
 def split_mode():
-    """Sets a KV-split policy for one test and restores automatic afterwards."""
-    def set_mode(mode):
-        m.muse_attn_set_kv_split(mode)
-    yield set_mode
-    m.muse_attn_set_kv_split(0)
+    """split_mode(case, mode): sets the case's per-call KV-split policy."""
+    return _with_split
 
 
 def _sentinel_like(t):
@@ -62,7 +68,7 @@ def _q_k_hat(case, layout=None):
 def test_split_attention_stage(w, mode, split_mode):
     case = make_case(w)
     q_hat, k_hat = _q_k_hat(case)
-    split_mode(mode)
+    split_mode(case, mode)
     print(f"[split] {w.name} mode {mode}", flush=True)
     o = _sentinel_like(q_hat)
     o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, o=o, want_lse=True)
@@ -82,7 +88,7 @@ def test_split_attention_stage(w, mode, split_mode):
 @pytest.mark.parametrize("w", CASES, ids=IDS)
 def test_split_fused_core(w, mode, split_mode):
     case = make_case(w)
-    split_mode(mode)
+    split_mode(case, mode)
     print(f"[split fused] {w.name} mode {mode}", flush=True)
     out = _sentinel_like(case.q)
     out, k_hat_f, lse_f = m.muse_attn_core_fwd(case.params, case.layout, case.q, case.k, case.v, case.gate,
@@ -111,7 +117,7 @@ def test_split_padded_keys_and_empty_rows(split_mode):
     valid[1, 64:192] = 0        # two whole padded tiles inside the row
     lay = m.Layout.bshd(2, 640, attention_mask=torch.from_numpy(valid).cuda())
     q_hat, k_hat = _q_k_hat(case, lay)
-    split_mode(4)
+    split_mode(case, 4)
     o, lse = m.muse_gqa_attn_fwd(case.params, lay, q_hat, k_hat, case.v, want_lse=True)
     out, _, lse_f = m.muse_attn_core_fwd(case.params, lay, case.q, case.k, case.v, case.gate, case.q_gain,
                                          case.k_gain, case.cos, case.sin, want_lse=True)
@@ -134,7 +140,7 @@ def test_split_bidirectional(split_mode):
                          segment_lengths=(300, 900, 5), use_rope=False)
     case = make_case(w, bidirectional=True)
     q_hat, k_hat = _q_k_hat(case)
-    split_mode(3)
+    split_mode(case, 3)
     o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
     torch.cuda.synchronize()
     ro, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs, window=0,
@@ -151,9 +157,10 @@ def test_automatic_split_of_a_small_grid(split_mode):
                          theta=5.0e5)
     case = make_case(w)
     q_hat, k_hat = _q_k_hat(case)
-    split_mode(0)
+    assert m.muse_attn_fwd_workspace_size(case.params, case.layout) > 0     # automatic: splits
     o, lse = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
-    split_mode(1)
+    split_mode(case, 1)
+    assert m.muse_attn_fwd_workspace_size(case.params, case.layout) == 0
     o1, lse1 = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
     torch.cuda.synchronize()
     ro, rl = O.attention(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), case.segs, window=0,
@@ -166,14 +173,83 @@ def test_automatic_split_of_a_small_grid(split_mode):
     assert float((lse - lse1).abs().max()) < 1e-5 * max(1.0, float(lse1.abs().max()))
 
 
-def test_policy_setter_returns_previous():
-    prev = m.muse_attn_set_kv_split(1)
-    try:
-        assert m.muse_attn_set_kv_split(5) == 1
-        assert m.muse_attn_set_kv_split(-3) == -1
-        assert m.muse_attn_set_kv_split(0) == 5
-    finally:
-        m.muse_attn_set_kv_split(prev)
+def test_policy_is_per_call():
+    """Calls with different policies, interleaved on one stream, each give
+    their own policy's bits (no process-wide setting)."""
+    w = CASES[0]
+    case = make_case(w)
+    q_hat, k_hat = _q_k_hat(case)
+    p1 = dataclasses.replace(case.params, kv_split=1)
+    p3 = dataclasses.replace(case.params, kv_split=3)
+    a1, _ = m.muse_gqa_attn_fwd(p1, case.layout, q_hat, k_hat, case.v)
+    a3, _ = m.muse_gqa_attn_fwd(p3, case.layout, q_hat, k_hat, case.v)
+    b1, _ = m.muse_gqa_attn_fwd(p1, case.layout, q_hat, k_hat, case.v)
+    b3, _ = m.muse_gqa_attn_fwd(p3, case.layout, q_hat, k_hat, case.v)
+    torch.cuda.synchronize()
+    assert torch.equal(a1.view(torch.int16), b1.view(torch.int16))
+    assert torch.equal(a3.view(torch.int16), b3.view(torch.int16))
+    assert not torch.equal(a1.view(torch.int16), a3.view(torch.int16))
+
+
+def test_workspace_reused_across_shapes():
+    """One caller workspace, filled with garbage, then used by a small split
+    call whose slots cover where a larger call's counters sit, then by that
+    larger call: each result equals the same call on a fresh workspace (the
+    call zeroes its counters itself)."""
+    small = make_case(W.small_workload("split_ws_small_s300", num_heads=4, num_kv_heads=1, head_dim=128,
+                                       seqlen=300))
+    large = make_case(W.small_workload("split_ws_large_b3_s1000", num_heads=8, num_kv_heads=2, head_dim=128,
+                                       batch=3, seqlen=1000))
+    _with_split(small, 4)
+    _with_split(large, 3)
+    n_small = m.muse_attn_fwd_workspace_size(small.params, small.layout)
+    n_large = m.muse_attn_fwd_workspace_size(large.params, large.layout)
+    assert 0 < n_small < n_large
+    ws = torch.randint(-128, 127, (n_large,), dtype=torch.int8, device="cuda").view(torch.uint8)
+    outs = []
+    for case in (small, large, small, large):
+        q_hat, k_hat = _q_k_hat(case)
+        o_ws, l_ws = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True,
+                                         workspace=ws)
+        o_new, l_new = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
+        outs.append((o_ws, l_ws, o_new, l_new))
+    torch.cuda.synchronize()
+    for o_ws, l_ws, o_new, l_new in outs:
+        assert torch.equal(o_ws.view(torch.int16), o_new.view(torch.int16))
+        assert torch.equal(l_ws, l_new)
+
+
+def test_split_call_in_a_hip_graph():
+    """A split forward captured in a graph (its counter reset is a kernel, not
+    a memset node) and replayed several times, with eager work and
+    synchronisation between replays: every replay equals the eager call."""
+    w = CASES[1]
+    case = _with_split(make_case(w), 3)
+    q_hat, k_hat = _q_k_hat(case)
+    ws = torch.empty(m.muse_attn_fwd_workspace_size(case.params, case.layout), dtype=torch.uint8, device="cuda")
+    o_ref, lse_ref = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True,
+                                         workspace=ws)
+    o = torch.empty_like(o_ref)
+    lse = torch.empty_like(lse_ref)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, o=o, lse=lse, workspace=ws,
+                                stream=side)
+    torch.cuda.synchronize()
+    for i in range(4):
+        o.zero_()
+        lse.zero_()
+        junk, _ = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, workspace=ws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), i
+        assert torch.equal(lse, lse_ref), i
+    del g
 
 
 # ---------------------------------------------------------------- backward
@@ -197,7 +273,7 @@ def _bwd_inputs(case, layout=None):
 def test_split_attention_bwd(w, mode, split_mode):
     case = make_case(w)
     q_hat, k_hat, o, lse, d_o, delta = _bwd_inputs(case)
-    split_mode(mode)
+    split_mode(case, mode)
     print(f"[split bwd] {w.name} mode {mode}", flush=True)
     got = m.muse_gqa_attn_bwd(case.params, case.layout, q_hat, k_hat, case.v, d_o, lse, delta)
     again = m.muse_gqa_attn_bwd(case.params, case.layout, q_hat, k_hat, case.v, d_o, lse, delta)
@@ -218,7 +294,7 @@ def test_split_attention_bwd_padded_keys(split_mode):
     valid[1, 500:] = 0
     lay = m.Layout.bshd(2, 640, attention_mask=torch.from_numpy(valid).cuda())
     q_hat, k_hat, o, lse, d_o, delta = _bwd_inputs(case, lay)
-    split_mode(4)
+    split_mode(case, 4)
     dq, dk, dv = m.muse_gqa_attn_bwd(case.params, lay, q_hat, k_hat, case.v, d_o, lse, delta)
     torch.cuda.synchronize()
     rq, rk, rv = O.attention_bwd(f64(q_hat), f64(k_hat), bits_f64(case.x["v"]), f64(d_o), case.segs, window=0,
@@ -231,12 +307,12 @@ def test_split_attention_bwd_padded_keys(split_mode):
 
 
 def test_split_on_a_side_stream_matches_the_default_stream(split_mode):
-    """A torch side stream (non-blocking) gets its own split buffer, zeroed in
-    its own stream order: the first call on it equals the default stream's."""
+    """A call on a torch side stream (non-blocking) zeroes its counters in
+    its own stream order: it equals the default stream's call."""
     w = W.small_workload("split_side_stream_s1100", num_heads=8, num_kv_heads=2, head_dim=128, seqlen=1100)
     case = make_case(w)
     q_hat, k_hat = _q_k_hat(case)
-    split_mode(3)
+    split_mode(case, 3)
     o_ref, lse_ref = m.muse_gqa_attn_fwd(case.params, case.layout, q_hat, k_hat, case.v, want_lse=True)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
