@@ -21,7 +21,7 @@ __all__ = [
     "muse_gqa_attn_fwd", "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd",
     "muse_attn_bwd_delta", "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd",
     "muse_qk_norm_rope_bwd_workspace_size", "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size",
-    "muse_attn_fwd_workspace_size", "muse_gqa_attn_bwd_workspace_size",
+    "muse_attn_fwd_workspace_size", "muse_gqa_attn_bwd_workspace_size", "muse_qk_norm_rope_bwd_static",
     "muse_validate_cu_seqlens", "muse_status_string", "muse_version",
 ]
 
@@ -36,7 +36,7 @@ symbols = (
     "muse_gqa_attn_fwd", "muse_out_norm_gate", "muse_attn_core_fwd", "muse_attn_fused_fwd", "muse_out_norm_gate_bwd", "muse_attn_bwd_delta",
     "muse_gqa_attn_bwd", "muse_qk_norm_rope_bwd", "muse_qk_norm_rope_bwd_workspace_size",
     "muse_attn_core_bwd", "muse_attn_core_bwd_workspace_size", "muse_attn_fwd_workspace_size",
-    "muse_gqa_attn_bwd_workspace_size", "muse_validate_cu_seqlens",
+    "muse_gqa_attn_bwd_workspace_size", "muse_qk_norm_rope_bwd_static", "muse_validate_cu_seqlens",
     "muse_status_string", "muse_last_error", "muse_version",
 )
 
@@ -83,6 +83,7 @@ _SIGS = {
     "muse_qk_norm_rope_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
                               ctypes.c_size_t, _P],
     "muse_qk_norm_rope_bwd_workspace_size": [_P, _P, _P],
+    "muse_qk_norm_rope_bwd_static": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P],
     "muse_attn_core_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                            _P, _P, ctypes.c_size_t, _P],
     "muse_attn_core_bwd_workspace_size": [_P, _P, _P],
@@ -514,6 +515,31 @@ def muse_qk_norm_rope_bwd(params: AttnParams, layout: Layout, q, k, q_gain, k_ga
         _ptr(sin, "sin", "fp32"), n_pos, _ptr(dq_hat, "dq_hat", "bf16"), _ptr(dk_hat, "dk_hat", "bf16"),
         _ptr(dq, "dq", "bf16"), _ptr(dk, "dk", "bf16"), _ptr(dq_gain, "dq_gain", "fp32"),
         _ptr(dk_gain, "dk_gain", "fp32"), wp, wb, _stream(stream)))
+    return dq, dk, dq_gain, dk_gain
+
+
+def muse_qk_norm_rope_bwd_static(params: AttnParams, layout: Layout, q, k, q_gain, k_gain, cos, sin, dq_hat,
+                                 dk_hat, *, dq=None, dk=None, dq_gain=None, dk_gain=None, stream=None):
+    """muse_qk_norm_rope_bwd with the library's static scratch instead of a
+    workspace (the C call allocates nothing; outputs not passed in are
+    allocated here); returns (dq, dk, dq_gain, dk_gain)."""
+    import torch
+    if q is not None and dq is None:
+        dq = torch.empty_like(q)
+    if k is not None and dk is None:
+        dk = torch.empty_like(k)
+    if q_gain is not None and dq_gain is None:
+        dq_gain = torch.empty_like(q_gain)
+    if k_gain is not None and dk_gain is None:
+        dk_gain = torch.empty_like(k_gain)
+    n_pos = cos.shape[0] if cos is not None else 0
+    p, l = params.to_c(), layout.to_c()
+    _check(library().muse_qk_norm_rope_bwd_static(
+        ctypes.byref(p), ctypes.byref(l), _ptr(q, "q", "bf16"), _ptr(k, "k", "bf16"),
+        _ptr(q_gain, "q_gain", "fp32"), _ptr(k_gain, "k_gain", "fp32"), _ptr(cos, "cos", "fp32"),
+        _ptr(sin, "sin", "fp32"), n_pos, _ptr(dq_hat, "dq_hat", "bf16"), _ptr(dk_hat, "dk_hat", "bf16"),
+        _ptr(dq, "dq", "bf16"), _ptr(dk, "dk", "bf16"), _ptr(dq_gain, "dq_gain", "fp32"),
+        _ptr(dk_gain, "dk_gain", "fp32"), _stream(stream)))
     return dq, dk, dq_gain, dk_gain
 
 

@@ -795,11 +795,12 @@ extern "C" muse_status muse_qk_norm_rope_bwd_workspace_size(const muse_attn_para
   return MUSE_OK;
 }
 
-extern "C" muse_status muse_qk_norm_rope_bwd(const muse_attn_params *p, const muse_layout *l, const void *q,
+static muse_status qk_norm_rope_bwd_impl(const muse_attn_params *p, const muse_layout *l, const void *q,
                                              const void *k, const float *q_gain, const float *k_gain,
                                              const float *cos, const float *sin, int32_t n_pos, const void *dq_hat,
                                              const void *dk_hat, void *dq, void *dk, float *dq_gain, float *dk_gain,
-                                             void *workspace, size_t workspace_bytes, void *stream) {
+                                             void *workspace, size_t workspace_bytes, void *stream,
+                                             bool static_scratch) {
   muse_status s = check_params(p);
   if (s != MUSE_OK) return s;
   Geometry g;
@@ -821,6 +822,18 @@ extern "C" muse_status muse_qk_norm_rope_bwd(const muse_attn_params *p, const mu
   const int64_t qb = bf16_bytes(N, g.hq, g.d), kb = bf16_bytes(N, g.hkv, g.d);
   const int64_t tab = p->use_rope ? (int64_t)n_pos * (g.d / 2) * 4 : 0;
   const size_t need = (q_gain || k_gain) ? qk_bwd_partial_bytes(g, q_gain != nullptr, k_gain != nullptr) : 0;
+  if (static_scratch && need > 0) {
+    // the library-held scratch of this GPU (no allocation: a static device array)
+    float *ptr = nullptr;
+    size_t have = 0;
+    const hipError_t e = qk_norm_bwd_static_scratch(&ptr, &have);
+    if (e != hipSuccess) return device_status(e, "static scratch lookup");
+    if (need > have)
+      return set_error(MUSE_ERR_INVALID_ARG, "the gain partial sums need %zu bytes, more than the %zu bytes "
+                       "of static scratch; use muse_qk_norm_rope_bwd with a workspace", need, have);
+    workspace = ptr;
+    workspace_bytes = have;
+  }
   s = check_disjoint({{q, qb, "q"}, {k, kb, "k"}, {q_gain, g.d * 4, "q_gain"}, {k_gain, g.d * 4, "k_gain"},
                       {cos, tab, "cos"}, {sin, tab, "sin"}, {dq_hat, qb, "dq_hat"}, {dk_hat, kb, "dk_hat"},
                       layout_range(l, g, 0), layout_range(l, g, 1)},
@@ -862,6 +875,24 @@ extern "C" muse_status muse_qk_norm_rope_bwd(const muse_attn_params *p, const mu
   return device_status(launch_qk_norm_rope_bwd(g.d, a, (hipStream_t)stream), "qk_norm_rope_bwd launch");
 }
 
+
+extern "C" muse_status muse_qk_norm_rope_bwd(const muse_attn_params *p, const muse_layout *l, const void *q,
+                                             const void *k, const float *q_gain, const float *k_gain,
+                                             const float *cos, const float *sin, int32_t n_pos, const void *dq_hat,
+                                             const void *dk_hat, void *dq, void *dk, float *dq_gain, float *dk_gain,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+  return qk_norm_rope_bwd_impl(p, l, q, k, q_gain, k_gain, cos, sin, n_pos, dq_hat, dk_hat, dq, dk, dq_gain,
+                               dk_gain, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" muse_status muse_qk_norm_rope_bwd_static(const muse_attn_params *p, const muse_layout *l,
+                                                    const void *q, const void *k, const float *q_gain,
+                                                    const float *k_gain, const float *cos, const float *sin,
+                                                    int32_t n_pos, const void *dq_hat, const void *dk_hat, void *dq,
+                                                    void *dk, float *dq_gain, float *dk_gain, void *stream) {
+  return qk_norm_rope_bwd_impl(p, l, q, k, q_gain, k_gain, cos, sin, n_pos, dq_hat, dk_hat, dq, dk, dq_gain,
+                               dk_gain, nullptr, 0, stream, true);
+}
 
 extern "C" muse_status muse_attn_core_bwd_workspace_size(const muse_attn_params *p, const muse_layout *l,
                                                          size_t *bytes) {

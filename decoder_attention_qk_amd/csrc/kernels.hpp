@@ -175,6 +175,10 @@ hipError_t launch_out_norm_gate_bwd(int head_dim, const OutGateBwdArgs &a, hipSt
 // blocks the Q/K backward uses for q_rows / k_rows rows (the partial buffers' first dimension)
 void qk_norm_bwd_blocks(int head_dim, int64_t q_rows, int64_t k_rows, int32_t *q_blocks, int32_t *k_blocks);
 hipError_t launch_qk_norm_rope_bwd(int head_dim, const QkNormBwdArgs &a, hipStream_t stream);
+// The current device's copy of the library-held scratch of the Q/K backward's
+// allocation-free entry point: its address (from hipGetSymbolAddress, looked
+// up once per device) and size.
+hipError_t qk_norm_bwd_static_scratch(float **ptr, size_t *bytes);
 hipError_t launch_attn_bwd(int head_dim, const AttnBwdArgs &a, hipStream_t stream);
 int attn_bwd_keys_per_workgroup();
 int attn_columns_per_workgroup();  // (token, head) query columns one attention workgroup holds

@@ -17,6 +17,8 @@
 // bits.  Gain gradients are reduced deterministically: every block walks a
 // fixed set of rows, sums its lanes' partials through LDS in a fixed order,
 // and a second kernel adds the block partials of each column in block order.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -285,6 +287,35 @@ void qk_norm_bwd_blocks(int head_dim, int64_t q_rows, int64_t k_rows, int32_t *q
   };
   *q_blocks = nb(q_rows);
   *k_blocks = nb(k_rows);
+}
+
+// Scratch of muse_qk_norm_rope_bwd_static: the gain partial sums of both
+// tensors at the largest block count ([2][kMaxQkBlocks][128] floats, 2 MiB),
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): the launch takes the address hipGetSymbolAddress reports for the
+// current device.
+constexpr size_t kStaticScratchFloats = 2 * (size_t)kMaxQkBlocks * 128;
+static __device__ __align__(256) float scratch[kStaticScratchFloats];
+
+hipError_t qk_norm_bwd_static_scratch(float **ptr, size_t *bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float *>(p);
+  }
+  *ptr = addr[dev];
+  *bytes = kStaticScratchFloats * sizeof(float);
+  return hipSuccess;
 }
 
 hipError_t launch_qk_norm_rope_bwd(int head_dim, const QkNormBwdArgs &args, hipStream_t stream) {

@@ -440,6 +440,27 @@ muse_status muse_qk_norm_rope_bwd_workspace_size(const muse_attn_params *params,
                                                  const muse_layout *layout, size_t *bytes);
 
 /*
+ * muse_qk_norm_rope_bwd without a workspace, for callers that cannot
+ * allocate (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The gain-gradient partial sums go to scratch memory
+ * the library holds in device memory instead: one static array per GPU of
+ * 2 x 2048 x 128 floats (2 MiB), held from the first call on that GPU until
+ * the process ends.  Every shape muse_qk_norm_rope_bwd accepts fits it; a
+ * shape whose partial sums did not fit would get INVALID_ARG.  The call
+ * allocates nothing.  All calls on one GPU share its array: calls that
+ * overlap in time on one GPU (other streams, other threads, a graph replayed
+ * beside another call) race and give wrong gain gradients.  Nothing in the
+ * array needs to start at zero (each call overwrites the partial rows it
+ * reads).  Arguments, results and errors otherwise as muse_qk_norm_rope_bwd.
+ */
+muse_status muse_qk_norm_rope_bwd_static(const muse_attn_params *params, const muse_layout *layout,
+                                         const void *q, const void *k, const float *q_gain,
+                                         const float *k_gain, const float *cos, const float *sin,
+                                         int32_t n_pos, const void *dq_hat, const void *dk_hat,
+                                         void *dq, void *dk, float *dq_gain, float *dk_gain,
+                                         void *stream);
+
+/*
  * Backward of the whole core (muse_attn_core_fwd): gradients of q, k, v, the
  * gate logits and the two gains, from dout [N, Hq, D] bf16.
  * o: the forward's attention output before the output norm ([N, Hq, D] bf16,

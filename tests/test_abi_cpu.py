@@ -325,3 +325,19 @@ def test_sources_allocate_nothing():
         if name != "debug_check.cpp":
             for call in ("hipStreamSynchronize", "hipDeviceSynchronize", "hipEventSynchronize", "hipMemcpy"):
                 assert call not in text, (name, call)
+
+
+def test_static_qk_bwd_argument_rules():
+    """The allocation-free Q/K backward validates like the workspace one
+    (these calls fail before any device work)."""
+    lib = m.library()
+    p, lay = _params(), _bshd(1, 16)
+    A = [FAKE + (i << 24) for i in range(12)]
+
+    def call(q=A[0], dqh=A[1], dq=A[2], qg=None, dqg=None, pp=p):
+        return lib.muse_qk_norm_rope_bwd_static(ctypes.byref(pp), ctypes.byref(lay), q, None, qg, None, A[4],
+                                                A[5], 16, dqh, None, dq, None, dqg, None, None)
+    assert call(dq=None) == 1                              # a tensor without its gradient output
+    assert call(qg=A[6]) == 1                              # a gain without its gradient
+    assert call(pp=_params(head_dim=96)) == 2
+    assert call(pp=_params(kv_split=-2)) == 1
