@@ -14,6 +14,8 @@ and the CPU oracle's rate on a sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --summarize-pmc DIR [DIR ...]   # rocprofv3 counter summary (text)
+    python bench.py --summarize-trace DIR           # rocprofv3 kernel-trace table
+    python bench.py --workload W --traffic-record FETCH_DIR WRITE_DIR   # HBM traffic record
 """
 
 from __future__ import annotations
@@ -74,7 +76,12 @@ def parse(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (reference kernel for HBM counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
-                    help="print a text summary of rocprofv3 --pmc result directories and exit")
+                    help="print a text summary of rocprofv3 --pmc CSV result directories and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a table of a rocprofv3 --kernel-trace CSV result directory and exit")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the fused kernel's HBM-traffic record of --workload from two rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE CSV runs made with --calibrate-copy, and exit")
     return ap.parse_args(argv)
 
 
@@ -364,16 +371,25 @@ def measure_backward(b: Bench, warmup: int = 5, iters: int = 20) -> dict:
     }
 
 
-def measure_workload(name: str, kv_split: int, steps: int = 10, warmup: int = 5) -> dict:
+def measure_workload(name: str, kv_split: int, warm_s: float = 0.1, timed_s: float = 0.2) -> dict:
     """Sub-record of another configuration: its step, the fused kernel's
-    roofline fraction and the flushed Q/K norm+RoPE and output norm/gate stages."""
+    roofline fraction and the flushed Q/K norm+RoPE and output norm/gate stages.
+    Warmup and timed steps are counted to cover about warm_s and timed_s of
+    work (at least 5 and 10 steps), so short steps still run at settled clocks."""
     w = W.WORKLOADS[name]
     b = Bench(w, kv_split)
-    t = time_steps(b, steps, warmup)
+    b.step()
+    b.torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    b.step()
+    b.torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-6)
+    t = time_steps(b, max(10, int(timed_s / one)), max(5, int(warm_s / one)))
     rec = kernel_record(b, t)
     flop_step = sum(t["flop_layers"])
     st = measure_stages(b, which=("qk_norm_rope", "out_norm_gate"))
-    out = {"step_ms": round(t["step_s"] * 1e3, 4), "TFLOPs_step": round(flop_step / t["step_s"] / 1e12, 3),
+    out = {"steps": len(t["attn_s"]), "step_ms": round(t["step_s"] * 1e3, 4),
+           "TFLOPs_step": round(flop_step / t["step_s"] / 1e12, 3),
            "fused_kernel": rec, "qk_norm_rope_flushed": st["qk_norm_rope"],
            "out_norm_gate_flushed": st["out_norm_gate"]}
     b.free()
@@ -451,53 +467,127 @@ def cpu_baseline(w: W.Workload, budget_s: float = 20.0) -> dict:
                       f"{cores} cores, elementwise numpy single-threaded"}
 
 
+def _csv_rows(d: str, suffix: str) -> list[dict]:
+    """Rows of every rocprofv3 CSV file under d whose name ends in suffix."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _short_kernel(name: str) -> str:
+    return name.replace("muse::(anonymous namespace)::", "").replace("(anonymous namespace)::", "") \
+        .replace("muse::", "").split("(")[0].replace("void ", "").strip()
+
+
+def _counter_table(d: str) -> dict:
+    """{dispatch id: (kernel, {counter: value summed over instances})} of a
+    rocprofv3 --pmc CSV directory."""
+    import collections
+    per = collections.OrderedDict()
+    for r in _csv_rows(d, "counter_collection.csv"):
+        did = int(r["Dispatch_Id"])
+        name, vals = per.setdefault(did, (_short_kernel(r["Kernel_Name"]), collections.defaultdict(float)))
+        vals[r["Counter_Name"]] += float(r["Counter_Value"])
+    return per
+
+
+def summarize_trace(d: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace CSV directory: per kernel
+    and grid, the number of dispatches and their mean, min and max duration."""
+    import collections
+    groups = collections.OrderedDict()
+    for r in _csv_rows(d, "kernel_trace.csv"):
+        grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
+        key = (_short_kernel(r["Kernel_Name"]), grid)
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | grid (threads) | calls | mean us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (name, grid), us in groups.items():
+        lines.append(f"| {name} | {grid} | {len(us)} | {np.mean(us):.2f} | {min(us):.2f} | {max(us):.2f} |")
+    return "\n".join(lines)
+
+
 def summarize_pmc(dirs: list[str]) -> str:
-    """Text summary of rocprofv3 --pmc result databases: per kernel, the mean
+    """Text summary of rocprofv3 --pmc CSV directories: per kernel, the mean
     of each counter per dispatch and the ratios the attention kernel's
     analysis uses."""
     import collections
-    import glob
-    import sqlite3
     lines = []
     for d in dirs:
-        for db in sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True)):
-            con = sqlite3.connect(db)
-            rows = con.execute("select dispatch_id, kernel_name, counter_name, sum(value), avg(duration) "
-                               "from counters_collection group by dispatch_id, counter_name").fetchall()
-            per = collections.defaultdict(lambda: collections.defaultdict(float))
-            n = collections.Counter()
-            seen = set()
-            for did, kname, cname, val, dur in rows:
-                kname = kname.replace("(anonymous namespace)::", "").split("(")[0]
-                per[kname][cname] += val
-                if did not in seen:
-                    seen.add(did)
-                    n[kname] += 1
-                    per[kname]["duration_ns"] += dur
-            lines.append(f"## {os.path.relpath(db, ROOT) if db.startswith(ROOT) else db}")
-            for kname in sorted(per, key=lambda k: -per[k]["duration_ns"]):
-                c = {k: v / n[kname] for k, v in per[kname].items()}
-                lines.append(f"- `{kname}`: {n[kname]} dispatches; per dispatch: "
-                             + ", ".join(f"{k} {v:.6g}" for k, v in sorted(c.items())))
-                mf = c.get("SQ_INSTS_MFMA", 0.0)
-                if mf:
-                    r = []
-                    if "SQ_INSTS_VALU" in c:
-                        r.append(f"non-MFMA VALU per MFMA {(c['SQ_INSTS_VALU'] - mf) / mf:.3f}")
-                    for k in ("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
-                        if k in c:
-                            r.append(f"{k} per MFMA {c[k] / mf:.3f}")
-                    lines.append("  - " + "; ".join(r))
-                if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and c.get("SQ_VALU_MFMA_COEXEC_CYCLES") is not None:
-                    lines.append(f"  - VALU co-executed with MFMA in "
-                                 f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.3f} of MFMA-busy cycles")
+        per = _counter_table(d)
+        agg = collections.OrderedDict()
+        for name, vals in per.values():
+            n, tot = agg.setdefault(name, [0, collections.defaultdict(float)])
+            agg[name][0] += 1
+            for k, v in vals.items():
+                tot[k] += v
+        lines.append(f"## {os.path.basename(os.path.normpath(d))}")
+        for name, (n, tot) in agg.items():
+            c = {k: v / n for k, v in tot.items()}
+            lines.append(f"- `{name}`: {n} dispatches; per dispatch: "
+                         + ", ".join(f"{k} {v:.6g}" for k, v in sorted(c.items())))
+            mf = c.get("SQ_INSTS_MFMA", 0.0)
+            r = []
+            if mf:
+                if "SQ_INSTS_VALU" in c:
+                    r.append(f"non-MFMA VALU per MFMA {(c['SQ_INSTS_VALU'] - mf) / mf:.3f}")
+                for k in ("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+                    if k in c:
+                        r.append(f"{k} per MFMA {c[k] / mf:.3f}")
+            if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+                r.append(f"VALU co-issued with MFMA in {c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}"
+                         " of MFMA-busy cycles")
+            if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and c.get("SQ_BUSY_CU_CYCLES"):
+                r.append(f"MFMA busy per SIMD-cycle of a busy CU (SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES)) "
+                         f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * c['SQ_BUSY_CU_CYCLES']):.3f}")
+            if c.get("SQ_WAVE_CYCLES") and c.get("SQ_BUSY_CU_CYCLES"):
+                r.append(f"waves resident per busy CU (4 SQ_WAVE_CYCLES / SQ_BUSY_CU_CYCLES; wave cycles count "
+                         f"in units of 4) {4 * c['SQ_WAVE_CYCLES'] / c['SQ_BUSY_CU_CYCLES']:.2f}")
+            if r:
+                lines.append("  - " + "; ".join(r))
     return "\n".join(lines)
+
+
+def traffic_record(workload: str, fetch_dir: str, write_dir: str) -> dict:
+    """HBM bytes per launch of the fused attention kernel from two rocprofv3
+    --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
+    what the same counter reads for the 256 MiB device copy of
+    --calibrate-copy (the largest copy dispatch of the run)."""
+    copy_bytes = 256 * 1024 * 1024
+    w = W.WORKLOADS[workload]
+    out = {"workload": workload, "kernel": f"attn_fwd_kernel<{w.head_dim}, true, false>",
+           "kernel_source_digest": kernel_source_digest()}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _counter_table(d)
+        copies = [v[counter] for name, v in per.values() if "copy" in name.lower() and counter in v]
+        fused = [v[counter] for name, v in per.values() if name.startswith("attn_fwd_kernel") and "true" in name
+                 and counter in v]
+        if not copies or not fused:
+            raise SystemExit(f"{d}: no copy or fused-attention dispatch with {counter}")
+        scale = copy_bytes / (max(copies) * 1024.0)
+        key = "fetch" if counter == "FETCH_SIZE" else "write"
+        out[f"{key}_bytes_per_launch"] = int(round(np.mean(fused) * 1024.0 * scale))
+        out[f"{key}_scale"] = round(scale, 4)
+    qb = w.tokens * w.num_heads * w.head_dim * 2
+    kb = w.tokens * w.num_kv_heads * w.head_dim * 2
+    out["algorithmic_read_bytes"] = 2 * qb + 2 * kb
+    out["algorithmic_write_bytes"] = qb
+    return out
 
 
 def main(argv=None):
     args = parse(argv)
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.traffic_record:
+        print(json.dumps(traffic_record(args.workload, *args.traffic_record), indent=1))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
