@@ -525,6 +525,12 @@ def summarize_pmc(dirs: list[str]) -> str:
             for k, v in vals.items():
                 tot[k] += v
         lines.append(f"## {os.path.basename(os.path.normpath(d))}")
+        # HBM counters calibrated on the 256 MiB copy of --calibrate-copy, when present
+        scale = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            copies = [v[counter] for name, v in per.values() if "copy" in name.lower() and counter in v]
+            if copies and max(copies) > 0:
+                scale[counter] = 256 * 1024 * 1024 / (max(copies) * 1024.0)
         for name, (n, tot) in agg.items():
             c = {k: v / n for k, v in tot.items()}
             lines.append(f"- `{name}`: {n} dispatches; per dispatch: "
@@ -540,6 +546,9 @@ def summarize_pmc(dirs: list[str]) -> str:
             if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
                 r.append(f"VALU co-issued with MFMA in {c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}"
                          " of MFMA-busy cycles")
+            for counter, sc in scale.items():
+                if counter in c:
+                    r.append(f"{counter} x {sc:.4f} = {c[counter] * 1024.0 * sc / 1e9:.4f} GB per dispatch")
             if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and c.get("SQ_BUSY_CU_CYCLES"):
                 r.append(f"MFMA busy per SIMD-cycle of a busy CU (SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES)) "
                          f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * c['SQ_BUSY_CU_CYCLES']):.3f}")

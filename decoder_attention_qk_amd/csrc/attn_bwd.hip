@@ -20,7 +20,9 @@
 // dK/dV kernel -- keys stationary: a workgroup owns 128 keys of one KV head,
 //   32 per wave, held as B fragments (K and V) in registers; Q and dO tiles
 //   of 64 tokens of one query head stream through LDS together with their
-//   LSE and delta rows, for every head of the group.  Per 32-query half a
+//   LSE and delta rows, the group's heads of one token tile in turn, the
+//   token tiles in an order shared by neighbouring key blocks (so blocks
+//   resident together on an XCD read each tile from one L2 fill).  Per 32-query half a
 //   wave forms S = Q K^T and dP = dO V^T (lane l owns key column l % 32),
 //   then dV^T += dO^T P and dK^T += Q^T dS with P and dS in the B-operand
 //   layout and dO^T, Q^T read transposed from LDS.
@@ -160,7 +162,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) 
   auto vbuf = [&](int buf) __attribute__((always_inline)) { return (lds_char *)(buf ? lds_v1 : lds_v0); };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform, so the per-wave work tests below are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31;
   const int g = lane >> 5;
@@ -362,7 +365,8 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
   };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform, so the per-wave work tests below are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31;
   const int g = lane >> 5;
@@ -413,8 +417,31 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
   const int qlo = bidir ? 0 : kb0;
   const int qhi = bidir || W <= 0 ? L - 1 : min(L - 1, min(kb0 + COLS - 1, L - 1) + W - 1);
   const int qt_lo = qlo / BN;
-  const int nqt = qhi / BN - qt_lo + 1;
+  const int qt_hi = qhi / BN;
+  const int nqt = qt_hi - qt_lo + 1;
   const int ntiles = nqt * a.group;
+  // Visiting order of the query tiles.  Workgroups of neighbouring key blocks
+  // run side by side on one XCD; walking their tiles in a common order makes
+  // them read the same tile at about the same time, so one L2 fill serves
+  // them all.  Without a window every block's tiles end at the segment's
+  // last tile: walk down from there.  With a window every block's tiles form
+  // a run of the same length R (fewer at the segment's end), which holds one
+  // multiple of R: start the walk there, go up and wrap round.  The G heads
+  // of a tile are consecutive steps (their rows are adjacent in memory).
+  const bool windowed = !bidir && W > 0 && W < L;
+  int rot = 0;
+  if (windowed) {
+    const int R = (COLS - 2 + W) / BN + 1;
+    const int s = (qt_lo + R - 1) / R * R;
+    rot = s <= qt_hi ? s - qt_lo : 0;
+  }
+  auto step_tile = [&](int it, int &h) __attribute__((always_inline)) {
+    const int ti = it / a.group;
+    h = kvh * a.group + (it - ti * a.group);
+    if (!windowed) return qt_hi - ti;
+    const int x = rot + ti;
+    return qt_lo + (x >= nqt ? x - nqt : x);
+  };
   // split: this part takes steps [it0, it1) (the last launched part takes any remainder)
   const int span = a.dkv_parts > 1 ? a.dkv_span : ntiles;
   const int nparts = min((ntiles + span - 1) / span, a.dkv_parts);
@@ -435,8 +462,8 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
   ad.init(lane);
 
   auto issue_dma = [&](int it, int buf) {
-    const int h = kvh * a.group + it / nqt;
-    const int t0 = (qt_lo + it % nqt) * BN;
+    int h;
+    const int t0 = step_tile(it, h) * BN;
     const int rows = min(L - t0, BN);
     const int64_t r0 = (int64_t)(s0 + t0) * a.hq + h;
     const int valid_bytes = ((rows - 1) * (int)q_stride + D) * 2;
@@ -464,7 +491,8 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
   for (int dt = 0; dt < DT; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
 
   auto compute = [&](int it, int BUF) __attribute__((always_inline)) {
-    const int t0 = (qt_lo + it % nqt) * BN;
+    int h;
+    const int t0 = step_tile(it, h) * BN;
     const bool none_visible = !wave_active || (!bidir && (t0 + BN - 1 < kw0 || (W > 0 && t0 > kw1 + W - 1)));
     if (none_visible) return;
     const bool all_visible = t0 + BN <= L && (bidir || (t0 >= kw1 && (W <= 0 || t0 + BN - 1 <= kw0 + W - 1)));

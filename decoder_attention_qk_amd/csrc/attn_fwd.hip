@@ -85,7 +85,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
   auto vbuf = [&](int buf) __attribute__((always_inline)) { return (lds_char *)(buf ? lds_v1 : lds_v0); };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform, so the per-wave tile tests below are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31;
   const int g = lane >> 5;
