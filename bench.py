@@ -528,7 +528,7 @@ def summarize_pmc(dirs: list[str]) -> str:
         # HBM counters calibrated on the 256 MiB copy of --calibrate-copy, when present
         scale = {}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            copies = [v[counter] for name, v in per.values() if "copy" in name.lower() and counter in v]
+            copies = [v[counter] for name, v in per.values() if name.startswith("__amd_rocclr_copyBuffer") and counter in v]
             if copies and max(copies) > 0:
                 scale[counter] = 256 * 1024 * 1024 / (max(copies) * 1024.0)
         for name, (n, tot) in agg.items():
@@ -571,7 +571,7 @@ def traffic_record(workload: str, fetch_dir: str, write_dir: str) -> dict:
            "kernel_source_digest": kernel_source_digest()}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _counter_table(d)
-        copies = [v[counter] for name, v in per.values() if "copy" in name.lower() and counter in v]
+        copies = [v[counter] for name, v in per.values() if name.startswith("__amd_rocclr_copyBuffer") and counter in v]
         fused = [v[counter] for name, v in per.values() if name.startswith("attn_fwd_kernel") and "true" in name
                  and counter in v]
         if not copies or not fused:
@@ -584,6 +584,25 @@ def traffic_record(workload: str, fetch_dir: str, write_dir: str) -> dict:
     kb = w.tokens * w.num_kv_heads * w.head_dim * 2
     out["algorithmic_read_bytes"] = 2 * qb + 2 * kb
     out["algorithmic_write_bytes"] = qb
+    # the attention backward's two kernels, when the runs included it: each
+    # reads q-hat, dO, k-hat, v, LSE and delta once; dQ writes dq-hat, dK/dV
+    # writes dk-hat and dv
+    rows = w.tokens * w.num_heads * 4
+    bwd = {}
+    for kname, wbytes in (("attn_bwd_dq_kernel", qb), ("attn_bwd_dkdv_kernel", 2 * kb)):
+        rec = {"algorithmic_read_bytes": 2 * qb + 2 * kb + 2 * rows, "algorithmic_write_bytes": wbytes}
+        for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            per = _counter_table(d)
+            vals = [v[counter] for name, v in per.values() if name.startswith(kname) and counter in v]
+            if not vals:
+                break
+            key = "fetch" if counter == "FETCH_SIZE" else "write"
+            rec[f"{key}_bytes_per_launch"] = int(round(np.mean(vals) * 1024.0 * out[f"{key}_scale"]))
+        else:
+            rec["fetched_over_algorithmic"] = round(rec["fetch_bytes_per_launch"] / rec["algorithmic_read_bytes"], 3)
+            bwd[kname] = rec
+    if bwd:
+        out["backward"] = bwd
     return out
 
 
