@@ -216,6 +216,44 @@ def time_steps(b: Bench, steps: int, warmup: int) -> dict:
     return dict(step_s=wall / steps, attn_s=attn, kpass_s=kpass, flop_layers=flop_layers)
 
 
+NOMINAL_CLOCK_MHZ = 2400.0     # the clock the 2.5 PFLOP/s dense bf16 peak is quoted at
+
+
+def clock_under_load(b: Bench, seconds: float = 0.6):
+    """Median shader clock (MHz) while the step repeats, read by polling
+    `rocm-smi --showclocks` from a child process; None where the tool is
+    missing or reports nothing.  Runs after the timed steps, so the timed
+    region carries no polling."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("rocm-smi")
+    if exe is None:
+        return None
+    vals, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            m = re.search(r'"sclk clock speed:":\s*"\((\d+)Mhz\)"', r.stdout)
+            if m:
+                vals.append(int(m.group(1)))
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        b.step()
+        b.torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    return float(np.median(vals)) if vals else None
+
+
 def kernel_record(b: Bench, t: dict) -> dict:
     """The fused attention kernel's roofline record: algorithmic flop per
     launch averaged over the step's launches / the average launch duration."""
@@ -673,6 +711,12 @@ def main(argv=None):
         "k_norm_rope": rec["k_norm_rope"],
         "fused_bytes_per_layer": 3 * qb + 2 * kb,
     }
+    # for information: the same fraction against the peak scaled to the shader
+    # clock measured under the step's load
+    clk = clock_under_load(b)
+    line["roofline"]["clock_mhz_under_load"] = clk
+    line["roofline"]["frac_at_clock"] = (
+        round(rec["achieved"] / (PEAK_BF16_TFLOPS * clk / NOMINAL_CLOCK_MHZ), 4) if clk else None)
     if not args.no_stages:
         line["stages_flushed"] = measure_stages(b)
     if not args.no_backward:
