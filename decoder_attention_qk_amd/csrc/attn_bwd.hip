@@ -27,11 +27,16 @@
 //   then dV^T += dO^T P and dK^T += Q^T dS with P and dS in the B-operand
 //   layout and dO^T, Q^T read transposed from LDS.
 //
+// At D = 128 (no part split) dK/dV runs as attn_bwd_dkdv_rs_kernel below: the
+// same steps split between two waves per SIMD, one forming S, P and dV, the
+// other dP, dS and dK, with P handed over through LDS.
+//
 // Tiles are read both row-wise and transposed, so their 16-byte chunks use
 // the swizzle that keeps both patterns free of bank conflicts (Tile::swz_kv).
 // Masked scores get P = 0 explicitly (a query whose every key is padding has
 // lse = -inf).  Tiles no wave of the workgroup can see are never loaded.
 #include <cmath>
+#include <type_traits>
 
 #include "attn_common.hpp"
 #include "kernels.hpp"
@@ -562,6 +567,315 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
   store_cols<D>(a.dv + krow, dvacc, 1.0f, g, kpad);
 }
 
+// ===========================================================================
+// dK/dV at D = 128 with each SIMD's work split by role.  The one-wave-per-SIMD
+// kernel above leaves a SIMD's MFMA pipe idle whenever its only wave runs
+// VALU work or waits; here a workgroup of eight waves owns the same 128 keys
+// and waves c and c + 4 (the same SIMD) share key group c: wave c (A) forms
+// S = Q K^T, P = exp(S - LSE) and dV^T += dO^T P, wave c + 4 (B) forms
+// dP = dO V^T, dS = P (dP - delta) and dK^T += Q^T dS.  Each holds only its own
+// operand (K or V) and accumulator (dV or dK), so two waves fit a SIMD.  P
+// travels from A to B through LDS as fp16 (P <= 1, so the rounding is 2^-11
+// relative, below dS's own bf16 rounding).  Phases: one per (query tile,
+// head) step; in phase u wave A works on step u and wave B on step u - 1,
+// and a workgroup barrier ends the phase.  Q/dO tiles with their LSE and
+// delta rows sit in three LDS stages: in phase u, A reads step u's stage, B
+// step u - 1's, and the B waves' DMA fills step u + 1's.  Steps visit the
+// tiles in the order of the kernel above; a part split is not taken here.
+namespace rs {
+constexpr int D = 128;
+constexpr int NC = 4;                  // key groups (A/B wave pairs) per workgroup
+constexpr int NWAVES = 2 * NC;
+constexpr int KS = D / 16;
+constexpr int DT = D / 32;
+constexpr int NSTAGE = 3;
+using T = Tile<D>;
+constexpr int RB = T::ROW_BYTES;
+constexpr int DMA_PER_WAVE = T::TILE_BYTES / 1024 / NC;   // KiB of one tile per B wave
+constexpr int PHALF = 2 * 64 * 16;     // fp16 P of one 32-query half: [chunk 0/1][lane] of 16 bytes
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <int J>
+using ic = std::integral_constant<int, J>;
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
+}
+__device__ __forceinline__ void unpack_f16x2(uint32_t w, float &a, float &b) {
+  const f16x2 h = __builtin_bit_cast(f16x2, w);
+  a = (float)h[0];
+  b = (float)h[1];
+}
+// Workgroup barrier over LDS traffic only (the DMA of a stage is waited for
+// explicitly by the waves that issue it, before the barrier that precedes
+// its first reader).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+}  // namespace rs
+
+template <bool PAD>
+__global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(AttnBwdArgs a) {
+  using namespace rs;
+  // one array per stage, addressed with compile-time stage numbers, so the
+  // DMA into one stage never aliases (and never delays) reads of another
+  __shared__ __attribute__((aligned(16))) char lds_q0[T::TILE_BYTES], lds_q1[T::TILE_BYTES], lds_q2[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_o0[T::TILE_BYTES], lds_o1[T::TILE_BYTES], lds_o2[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float lds_l0[BN], lds_l1[BN], lds_l2[BN];
+  __shared__ __attribute__((aligned(16))) float lds_d0[BN], lds_d1[BN], lds_d2[BN];
+  __shared__ __attribute__((aligned(16))) char lds_p[NC][2][2 * PHALF];
+  auto qst = [&](auto S) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value % NSTAGE;
+    return (lds_char *)(st == 0 ? lds_q0 : st == 1 ? lds_q1 : lds_q2);
+  };
+  auto ost = [&](auto S) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value % NSTAGE;
+    return (lds_char *)(st == 0 ? lds_o0 : st == 1 ? lds_o1 : lds_o2);
+  };
+  auto lst = [&](auto S) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value % NSTAGE;
+    return (__attribute__((address_space(3))) float *)(st == 0 ? lds_l0 : st == 1 ? lds_l1 : lds_l2);
+  };
+  auto dst_ = [&](auto S) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value % NSTAGE;
+    return (__attribute__((address_space(3))) float *)(st == 0 ? lds_d0 : st == 1 ? lds_d1 : lds_d2);
+  };
+
+  const int tid = threadIdx.x;
+  // wave-uniform, so the role and per-step tests below are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = wave & (NC - 1);
+  const bool role_a = wave < NC;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+
+  // work item: as the one-wave kernel (no part split)
+  const int per_seg = a.k_blocks * a.hkv;
+  const int b = blockIdx.x;
+  const int seg = b / per_seg;
+  int rest = b % per_seg;
+  const int kb = rest / a.hkv;
+  const int kvh = rest % a.hkv;
+  int s0, L;
+  segment_bounds(a.lay, seg, s0, L);
+  const int kb0 = kb * (32 * NC);
+  if (kb0 >= L) return;
+  const int kw0 = kb0 + c * 32;
+  const int kw1 = min(kw0 + 31, L - 1);
+  const bool wave_active = kw0 < L;
+  const int key = kw0 + n;
+  const bool kin = key < L;
+  const int64_t krow = ((int64_t)(s0 + (kin ? key : 0)) * a.hkv + kvh) * D;
+
+  const int W = a.window;
+  const bool bidir = a.bidirectional != 0;
+  const float c2 = a.scale_log2;
+  const int mask_base = bidir ? 0 : key;
+  const int lim_c = W > 0 ? min(W, L - key) : L - key;
+  const uint32_t mask_lim = bidir ? (uint32_t)L : (uint32_t)max(lim_c, 0);
+  const int qlo = bidir ? 0 : kb0;
+  const int qhi = bidir || W <= 0 ? L - 1 : min(L - 1, min(kb0 + 32 * NC - 1, L - 1) + W - 1);
+  const int qt_lo = qlo / BN;
+  const int qt_hi = qhi / BN;
+  const int nqt = qt_hi - qt_lo + 1;
+  const int nsteps = nqt * a.group;
+  // the step order of the one-wave kernel (shared by neighbouring key blocks)
+  const bool windowed = !bidir && W > 0 && W < L;
+  int rot = 0;
+  if (windowed) {
+    const int R = (32 * NC - 2 + W) / BN + 1;
+    const int s_ = (qt_lo + R - 1) / R * R;
+    rot = s_ <= qt_hi ? s_ - qt_lo : 0;
+  }
+  auto step_tile = [&](int it, int &h) __attribute__((always_inline)) {
+    const int ti = it / a.group;
+    h = kvh * a.group + (it - ti * a.group);
+    if (!windowed) return qt_hi - ti;
+    const int x = rot + ti;
+    return qt_lo + (x >= nqt ? x - nqt : x);
+  };
+  // this key group's view of the query tile starting at t0
+  auto visibility = [&](int t0, bool &all_visible) __attribute__((always_inline)) {
+    const bool none = !wave_active || (!bidir && (t0 + BN - 1 < kw0 || (W > 0 && t0 > kw1 + W - 1)));
+    all_visible = !none && t0 + BN <= L && (bidir || (t0 >= kw1 && (W <= 0 || t0 + BN - 1 <= kw0 + W - 1)));
+    return !none;
+  };
+
+  TileAddr<D> ad;
+  ad.init(lane);
+  lds_char *pbase = (lds_char *)lds_p[c][0];
+
+  if (role_a) {
+    // ============ wave A: S, P, dV ============
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 rk = *reinterpret_cast<const uint4 *>(a.k + krow + ks * 16 + g * 8);
+      kf[ks] = __builtin_bit_cast(bf16x8, kin ? rk : make_uint4(0, 0, 0, 0));
+    }
+    f32x16 dvacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dvacc[dt] = f32x16{};
+    vmem_wait_all();
+    lds_barrier();   // the first step's stage has landed
+    auto phase = [&](int u, auto J) __attribute__((always_inline)) {
+      if (u < nsteps) {
+        int h;
+        const int t0 = step_tile(u, h) * BN;
+        bool all_visible;
+        if (visibility(t0, all_visible)) {
+          const lds_char *Qt = qst(J);
+          const lds_char *Ot = ost(J);
+          const __attribute__((address_space(3))) float *Lt = lst(J);
+          lds_char *slot = pbase + (u & 1) * (2 * PHALF);
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const f32x16 sv = rows_times<D>(Qt, ad, half * 32 * RB, kf);
+            float p[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(Lt + half * 32 + 8 * j + 4 * g);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                p[4 * j + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * j + e], c2, -(l4[e] * kLog2e)));
+            }
+            if (!all_visible) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int qp = t0 + half * 32 + (i >> 2) * 8 + 4 * g + (i & 3);
+                p[i] = (uint32_t)(qp - mask_base) < mask_lim ? p[i] : 0.0f;
+              }
+            }
+            u32x4 h0, h1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              h0[i] = pack_f16x2(p[2 * i], p[2 * i + 1]);
+              h1[i] = pack_f16x2(p[8 + 2 * i], p[8 + 2 * i + 1]);
+            }
+            *(__attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + lane * 16) = h0;
+            *(__attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + 1024 + lane * 16) = h1;
+            bf16x8 p0, p1;
+            pack16(p, p0, p1);
+            tr_times<D>(Ot, ad, half * 32, p0, p1, dvacc);
+          }
+        }
+      }
+      lds_barrier();
+    };
+    for (int r = 0;; r += 3) {
+      phase(r, ic<0>{}); if (r == nsteps) break;
+      phase(r + 1, ic<1>{}); if (r + 1 == nsteps) break;
+      phase(r + 2, ic<2>{}); if (r + 2 == nsteps) break;
+    }
+    if (!wave_active || !kin) return;
+    bool kpad = false;
+    if constexpr (PAD) kpad = a.key_valid[s0 + key] == 0;
+    // a padded key is seen by no query: its gradients are zero
+    store_cols<D>(a.dv + krow, dvacc, 1.0f, g, kpad);
+    return;
+  }
+
+  // ============ wave B: DMA; dP, dS, dK ============
+  bf16x8 vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint4 rv = *reinterpret_cast<const uint4 *>(a.v + krow + ks * 16 + g * 8);
+    vf[ks] = __builtin_bit_cast(bf16x8, kin ? rv : make_uint4(0, 0, 0, 0));
+  }
+  const int64_t q_stride = (int64_t)a.hq * D;
+  int off[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int slot = (c * DMA_PER_WAVE + i) * 64 + lane;
+    const int row = slot / T::CHUNKS;
+    const int pch = slot % T::CHUNKS;
+    off[i] = (row * (int)q_stride + (pch ^ T::swz_kv(row)) * 8) * 2;
+  }
+  // the step's Q and dO tiles, and (waves 4, 5) its LSE and delta rows; rows
+  // past the segment read as 0
+  auto issue_dma = [&](int it, auto S) __attribute__((always_inline)) {
+    int h;
+    const int t0 = step_tile(it, h) * BN;
+    const int rows = min(L - t0, BN);
+    const int64_t r0 = (int64_t)(s0 + t0) * a.hq + h;
+    const int valid_bytes = ((rows - 1) * (int)q_stride + D) * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + r0 * D, valid_bytes);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(a.d_o + r0 * D, valid_bytes);
+    lds_char *qdst = qst(S) + c * DMA_PER_WAVE * 1024;
+    lds_char *odst = ost(S) + c * DMA_PER_WAVE * 1024;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      dma16(qr, off[i], qdst + i * 1024);
+      dma16(orr, off[i], odst + i * 1024);
+    }
+    if (c < 2) {
+      const int fbytes = ((rows - 1) * a.hq + 1) * 4;
+      const __amdgpu_buffer_rsrc_t fr = make_rsrc((c ? a.delta : a.lse) + r0, fbytes);
+      dma4(fr, lane * a.hq * 4, (lds_char *)(c ? dst_(S) : lst(S)));
+    }
+  };
+  f32x16 dkacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dkacc[dt] = f32x16{};
+
+  if (nsteps > 0) issue_dma(0, ic<0>{});
+  vmem_wait_all();
+  lds_barrier();
+  auto bphase = [&](int u, auto J) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;   // u % NSTAGE
+    // step u + 1 into the stage step u - 2 left (A read it in phase u - 2,
+    // B in phase u - 1)
+    if (u + 1 < nsteps) issue_dma(u + 1, ic<j + 1>{});
+    if (u >= 1) {
+      int h;
+      const int t0 = step_tile(u - 1, h) * BN;
+      bool all_visible;
+      if (visibility(t0, all_visible)) {
+        const lds_char *Qt = qst(ic<j + 2>{});   // stage of step u - 1
+        const lds_char *Ot = ost(ic<j + 2>{});
+        const __attribute__((address_space(3))) float *Dl = dst_(ic<j + 2>{});
+        const lds_char *slot = pbase + ((u - 1) & 1) * (2 * PHALF);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const f32x16 dp = rows_times<D>(Ot, ad, half * 32 * RB, vf);
+          const u32x4 h0 = *(const __attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + lane * 16);
+          const u32x4 h1 = *(const __attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + 1024 + lane * 16);
+          float p[16], ds[16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            unpack_f16x2(h0[i], p[2 * i], p[2 * i + 1]);
+            unpack_f16x2(h1[i], p[8 + 2 * i], p[8 + 2 * i + 1]);
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(Dl + half * 32 + 8 * jj + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ds[4 * jj + e] = p[4 * jj + e] * (dp[4 * jj + e] - d4[e]);
+          }
+          bf16x8 d0, d1;
+          pack16(ds, d0, d1);
+          tr_times<D>(Qt, ad, half * 32, d0, d1, dkacc);
+        }
+      }
+    }
+    vmem_wait_all();   // step u + 1 has landed before the phase that reads it
+    lds_barrier();
+  };
+  for (int r = 0;; r += 3) {
+    bphase(r, ic<0>{}); if (r == nsteps) break;
+    bphase(r + 1, ic<1>{}); if (r + 1 == nsteps) break;
+    bphase(r + 2, ic<2>{}); if (r + 2 == nsteps) break;
+  }
+  if (!wave_active || !kin) return;
+  bool kpad = false;
+  if constexpr (PAD) kpad = a.key_valid[s0 + key] == 0;
+  store_cols<D>(a.dk + krow, dkacc, a.scaling, g, kpad);
+}
+
 template <int D, bool PAD>
 hipError_t launch_d(const AttnBwdArgs &a, hipStream_t stream) {
   const int64_t nseg = a.lay.num_segments;
@@ -571,8 +885,13 @@ hipError_t launch_d(const AttnBwdArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, PAD>), dim3((unsigned)dq_blocks), dim3(64 * NW), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (kv_blocks > 0)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, PAD>), dim3((unsigned)kv_blocks), dim3(64 * NW), 0, stream, a);
+  if (kv_blocks > 0) {
+    if (D == 128 && a.dkv_parts == 1)
+      hipLaunchKernelGGL((attn_bwd_dkdv_rs_kernel<PAD>), dim3((unsigned)kv_blocks), dim3(64 * rs::NWAVES), 0, stream,
+                         a);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, PAD>), dim3((unsigned)kv_blocks), dim3(64 * NW), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
