@@ -732,10 +732,9 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
           const lds_char *Ot = ost(J);
           const __attribute__((address_space(3))) float *Lt = lst(J);
           lds_char *slot = pbase + (u & 1) * (2 * PHALF);
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const f32x16 sv = rows_times<D>(Qt, ad, half * 32 * RB, kf);
-            float p[16];
+          // P of one half from its scores (exp, then the mask after it: a
+          // query with no visible key has LSE = -inf)
+          auto probs = [&](const f32x16 &sv, int half, float (&p)[16]) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(Lt + half * 32 + 8 * j + 4 * g);
@@ -743,13 +742,15 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
               for (int e = 0; e < 4; ++e)
                 p[4 * j + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * j + e], c2, -(l4[e] * kLog2e)));
             }
-            if (!all_visible) {
+          };
+          auto mask_p = [&](float (&p)[16], int half) __attribute__((always_inline)) {
 #pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int qp = t0 + half * 32 + (i >> 2) * 8 + 4 * g + (i & 3);
-                p[i] = (uint32_t)(qp - mask_base) < mask_lim ? p[i] : 0.0f;
-              }
+            for (int i = 0; i < 16; ++i) {
+              const int qp = t0 + half * 32 + (i >> 2) * 8 + 4 * g + (i & 3);
+              p[i] = (uint32_t)(qp - mask_base) < mask_lim ? p[i] : 0.0f;
             }
+          };
+          auto hand_over = [&](const float (&p)[16], int half, bf16x8 &b0, bf16x8 &b1) __attribute__((always_inline)) {
             u32x4 h0, h1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -758,10 +759,22 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
             }
             *(__attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + lane * 16) = h0;
             *(__attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + 1024 + lane * 16) = h1;
-            bf16x8 p0, p1;
-            pack16(p, p0, p1);
-            tr_times<D>(Ot, ad, half * 32, p0, p1, dvacc);
-          }
+            pack16(p, b0, b1);
+          };
+          // the second half's S chain beside the first half's exp, the first
+          // half's dV MFMAs beside the second half's exp
+          const f32x16 s0 = rows_times<D>(Qt, ad, 0, kf);
+          const f32x16 s1 = rows_times<D>(Qt, ad, 32 * RB, kf);
+          float pa[16], pb[16];
+          probs(s0, 0, pa);
+          if (!all_visible) mask_p(pa, 0);
+          bf16x8 a0, a1, b0, b1;
+          hand_over(pa, 0, a0, a1);
+          tr_times<D>(Ot, ad, 0, a0, a1, dvacc);
+          probs(s1, 1, pb);
+          if (!all_visible) mask_p(pb, 1);
+          hand_over(pb, 1, b0, b1);
+          tr_times<D>(Ot, ad, 32, b0, b1, dvacc);
         }
       }
       lds_barrier();
@@ -839,9 +852,7 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
         const lds_char *Ot = ost(ic<j + 2>{});
         const __attribute__((address_space(3))) float *Dl = dst_(ic<j + 2>{});
         const lds_char *slot = pbase + ((u - 1) & 1) * (2 * PHALF);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const f32x16 dp = rows_times<D>(Ot, ad, half * 32 * RB, vf);
+        auto dscores = [&](const f32x16 &dp, int half, bf16x8 &d0, bf16x8 &d1) __attribute__((always_inline)) {
           const u32x4 h0 = *(const __attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + lane * 16);
           const u32x4 h1 = *(const __attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + 1024 + lane * 16);
           float p[16], ds[16];
@@ -856,10 +867,15 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
 #pragma unroll
             for (int e = 0; e < 4; ++e) ds[4 * jj + e] = p[4 * jj + e] * (dp[4 * jj + e] - d4[e]);
           }
-          bf16x8 d0, d1;
           pack16(ds, d0, d1);
-          tr_times<D>(Qt, ad, half * 32, d0, d1, dkacc);
-        }
+        };
+        const f32x16 dp0 = rows_times<D>(Ot, ad, 0, vf);
+        const f32x16 dp1 = rows_times<D>(Ot, ad, 32 * RB, vf);
+        bf16x8 a0, a1, b0, b1;
+        dscores(dp0, 0, a0, a1);
+        tr_times<D>(Qt, ad, 0, a0, a1, dkacc);
+        dscores(dp1, 1, b0, b1);
+        tr_times<D>(Qt, ad, 32, b0, b1, dkacc);
       }
     }
     vmem_wait_all();   // step u + 1 has landed before the phase that reads it
