@@ -627,7 +627,7 @@ def traffic_record(workload: str, fetch_dir: str, write_dir: str) -> dict:
     # writes dk-hat and dv
     rows = w.tokens * w.num_heads * 4
     bwd = {}
-    for kname, wbytes in (("attn_bwd_dq_kernel", qb), ("attn_bwd_dkdv_kernel", 2 * kb)):
+    for kname, wbytes in (("attn_bwd_dq_kernel", qb), ("attn_bwd_dkdv", 2 * kb)):
         rec = {"algorithmic_read_bytes": 2 * qb + 2 * kb + 2 * rows, "algorithmic_write_bytes": wbytes}
         for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
             per = _counter_table(d)
