@@ -328,7 +328,8 @@ BwdSplitNeed bwd_split_need(const AttnBwdArgs &a, const Geometry &g, int policy)
   const size_t acc_bytes = (size_t)32 * g.d * sizeof(float);   // one D x 32 fp32 accumulator per wave
   n.slot_bytes = std::max(n.q.parts > 1 ? (size_t)items_q * n.q.parts * nw * acc_bytes : 0,
                           n.kv.parts > 1 ? (size_t)items_k * n.kv.parts * nw * 2 * acc_bytes : 0);
-  n.counters = std::max(n.q.parts > 1 ? items_q : 0, n.kv.parts > 1 ? items_k : 0) * nw;
+  // at D = 128 the two roles of a dK/dV key group arrive on counters of their own
+  n.counters = std::max(n.q.parts > 1 ? items_q : 0, n.kv.parts > 1 ? items_k * (g.d == 128 ? 2 : 1) : 0) * nw;
   return n;
 }
 

@@ -27,7 +27,7 @@
 //   then dV^T += dO^T P and dK^T += Q^T dS with P and dS in the B-operand
 //   layout and dO^T, Q^T read transposed from LDS.
 //
-// At D = 128 (no part split) dK/dV runs as attn_bwd_dkdv_rs_kernel below: the
+// At D = 128 dK/dV runs as attn_bwd_dkdv_rs_kernel below: the
 // same steps split between two waves per SIMD, one forming S, P and dV, the
 // other dP, dS and dK, with P handed over through LDS.
 //
@@ -347,9 +347,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) 
 }
 
 // ===========================================================================
-// D = 128 holds 2 x 64 accumulator registers, 2 x 32 for the K/V fragments
-// and the per-half scores: more than the 256 registers of two waves per SIMD,
-// so that instantiation runs one wave per SIMD (accumulators in AGPRs).
+// One wave holds both accumulators and both fragment sets: at D = 64 two
+// waves fit a SIMD; D = 128 (2 x 64 accumulator and 2 x 32 fragment registers)
+// runs as the role-split kernel below instead.
 template <int D, bool PAD>
 __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   using T = Tile<D>;
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_kerne
 // and a workgroup barrier ends the phase.  Q/dO tiles with their LSE and
 // delta rows sit in three LDS stages: in phase u, A reads step u's stage, B
 // step u - 1's, and the B waves' DMA fills step u + 1's.  Steps visit the
-// tiles in the order of the kernel above; a part split is not taken here.
+// tiles in the order of the kernel above, parts of a split item included.
 namespace rs {
 constexpr int D = 128;
 constexpr int NC = 4;                  // key groups (A/B wave pairs) per workgroup
@@ -617,7 +617,9 @@ __device__ __forceinline__ void lds_barrier() {
 }
 }  // namespace rs
 
-template <bool PAD>
+// SPLIT: the launch cuts key blocks into parts (a separate instantiation, so
+// the unsplit kernel carries none of the part bookkeeping)
+template <bool PAD, bool SPLIT>
 __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(AttnBwdArgs a) {
   using namespace rs;
   // one array per stage, addressed with compile-time stage numbers, so the
@@ -653,12 +655,16 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  // work item: as the one-wave kernel (no part split)
-  const int per_seg = a.k_blocks * a.hkv;
+  // work item: as the one-wave kernel (segment-major, key blocks ascending,
+  // then part, then kv head)
+  const int dkv_parts = SPLIT ? a.dkv_parts : 1;
+  const int per_seg = a.k_blocks * dkv_parts * a.hkv;
   const int b = blockIdx.x;
   const int seg = b / per_seg;
   int rest = b % per_seg;
-  const int kb = rest / a.hkv;
+  const int kb = rest / (dkv_parts * a.hkv);
+  rest %= dkv_parts * a.hkv;
+  const int part = rest / a.hkv;
   const int kvh = rest % a.hkv;
   int s0, L;
   segment_bounds(a.lay, seg, s0, L);
@@ -682,7 +688,14 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
   const int qt_lo = qlo / BN;
   const int qt_hi = qhi / BN;
   const int nqt = qt_hi - qt_lo + 1;
-  const int nsteps = nqt * a.group;
+  const int ntiles = nqt * a.group;
+  // split: this part takes steps [it0, it0 + nsteps) (the last launched part
+  // takes any remainder); uniform per workgroup
+  const int span = SPLIT ? a.dkv_span : ntiles;
+  const int nparts = SPLIT ? min((ntiles + span - 1) / span, dkv_parts) : 1;
+  if (part >= nparts) return;
+  const int it0 = part * span;
+  const int nsteps = (part == nparts - 1 ? ntiles : it0 + span) - it0;
   // the step order of the one-wave kernel (shared by neighbouring key blocks)
   const bool windowed = !bidir && W > 0 && W < L;
   int rot = 0;
@@ -691,13 +704,22 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
     const int s_ = (qt_lo + R - 1) / R * R;
     rot = s_ <= qt_hi ? s_ - qt_lo : 0;
   }
-  auto step_tile = [&](int it, int &h) __attribute__((always_inline)) {
+  // the query tile of this part's step u (and its head h)
+  auto step_tile = [&](int u, int &h) __attribute__((always_inline)) {
+    const int it = it0 + u;
     const int ti = it / a.group;
     h = kvh * a.group + (it - ti * a.group);
     if (!windowed) return qt_hi - ti;
     const int x = rot + ti;
     return qt_lo + (x >= nqt ? x - nqt : x);
   };
+  // the part's accumulator slots and arrival counters: per (item, key group)
+  // the one-wave kernel's slot of [dK | dV], B summing the dK half and A the
+  // dV half, each with its own counter (B's, then A's after all of B's)
+  constexpr int HALF_SLOT = DT * 16 * 64;
+  const int64_t item = ((int64_t)seg * a.k_blocks + kb) * a.hkv + kvh;
+  const int64_t n_items = (int64_t)a.lay.num_segments * a.k_blocks * a.hkv;
+  float *slot0 = a.part_acc + (item * dkv_parts * NC + c) * (2 * HALF_SLOT);
   // this key group's view of the query tile starting at t0
   auto visibility = [&](int t0, bool &all_visible) __attribute__((always_inline)) {
     const bool none = !wave_active || (!bidir && (t0 + BN - 1 < kw0 || (W > 0 && t0 > kw1 + W - 1)));
@@ -717,7 +739,8 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
       const uint4 rk = *reinterpret_cast<const uint4 *>(a.k + krow + ks * 16 + g * 8);
       kf[ks] = __builtin_bit_cast(bf16x8, kin ? rk : make_uint4(0, 0, 0, 0));
     }
-    f32x16 dvacc[DT];
+    f32x16 dvv[1][DT];
+    f32x16 (&dvacc)[DT] = dvv[0];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dvacc[dt] = f32x16{};
     vmem_wait_all();
@@ -784,7 +807,13 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
       phase(r + 1, ic<1>{}); if (r + 1 == nsteps) break;
       phase(r + 2, ic<2>{}); if (r + 2 == nsteps) break;
     }
-    if (!wave_active || !kin) return;
+    if (!wave_active) return;
+    if constexpr (SPLIT) {
+      if (!split_sum(dvv, slot0 + HALF_SLOT, (int64_t)NC * 2 * HALF_SLOT, part, nparts,
+                     a.part_cnt + n_items * NC + item * NC + c))
+        return;
+    }
+    if (!kin) return;
     bool kpad = false;
     if constexpr (PAD) kpad = a.key_valid[s0 + key] == 0;
     // a padded key is seen by no query: its gradients are zero
@@ -831,7 +860,8 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
       dma4(fr, lane * a.hq * 4, (lds_char *)(c ? dst_(S) : lst(S)));
     }
   };
-  f32x16 dkacc[DT];
+  f32x16 dkv1[1][DT];
+  f32x16 (&dkacc)[DT] = dkv1[0];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dkacc[dt] = f32x16{};
 
@@ -886,7 +916,11 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
     bphase(r + 1, ic<1>{}); if (r + 1 == nsteps) break;
     bphase(r + 2, ic<2>{}); if (r + 2 == nsteps) break;
   }
-  if (!wave_active || !kin) return;
+  if (!wave_active) return;
+  if constexpr (SPLIT) {
+    if (!split_sum(dkv1, slot0, (int64_t)NC * 2 * HALF_SLOT, part, nparts, a.part_cnt + item * NC + c)) return;
+  }
+  if (!kin) return;
   bool kpad = false;
   if constexpr (PAD) kpad = a.key_valid[s0 + key] == 0;
   store_cols<D>(a.dk + krow, dkacc, a.scaling, g, kpad);
@@ -902,10 +936,14 @@ hipError_t launch_d(const AttnBwdArgs &a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (kv_blocks > 0) {
-    if (D == 128 && a.dkv_parts == 1)
-      hipLaunchKernelGGL((attn_bwd_dkdv_rs_kernel<PAD>), dim3((unsigned)kv_blocks), dim3(64 * rs::NWAVES), 0, stream,
-                         a);
-    else
+    if constexpr (D == 128) {
+      if (a.dkv_parts > 1)
+        hipLaunchKernelGGL((attn_bwd_dkdv_rs_kernel<PAD, true>), dim3((unsigned)kv_blocks), dim3(64 * rs::NWAVES), 0,
+                           stream, a);
+      else
+        hipLaunchKernelGGL((attn_bwd_dkdv_rs_kernel<PAD, false>), dim3((unsigned)kv_blocks), dim3(64 * rs::NWAVES), 0,
+                           stream, a);
+    } else
       hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, PAD>), dim3((unsigned)kv_blocks), dim3(64 * NW), 0, stream, a);
   }
   return hipGetLastError();
