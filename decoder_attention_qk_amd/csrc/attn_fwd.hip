@@ -314,19 +314,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
 
     // The tile is processed as two 32-key halves; the per-column reference
     // makes a per-half softmax exact (order below).
-    // All K fragments of a half are read before its MFMA chain starts, so
-    // the LDS latency is paid once per half rather than once per k-step.
-    auto qk = [&](int half) __attribute__((always_inline)) {
-      bf16x8 kf[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks] + half * 32 * RB);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc, 0, 0, 0);
-      return acc;
-    };
     auto mask = [&](f32x16 &sv, int half) __attribute__((always_inline)) {
       // this lane's keys of the half as bits at compile-time positions
       // (8 (i/4) + i%4) of one 32-bit word; visibility is one unsigned range
@@ -406,10 +393,36 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     // share one basic block and the wave interleaves them.
     const bool masked = __builtin_amdgcn_readfirstlane((int)(!all_visible || padded)) != 0;
     bf16x8 pa0, pa1, pb0, pb1;
-    f32x16 s0v = qk(0);
+    // QK^T of the first half: its K fragments are all read before the chain
+    // (the LDS latency is paid once), and the second half's fragments are
+    // read one per MFMA of it, so they have landed when the second chain
+    // starts.
+    bf16x8 k0f[KS], k1f[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      k0f[ks] = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks]);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s0v = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s0v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f[ks], qf[ks], s0v, 0, 0, 0);
+      k1f[ks] = *(const __attribute__((address_space(3))) bf16x8 *)(Kt + ka[ks] + 32 * RB);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
     if (masked) mask(s0v, 0);
-    f32x16 s1v = qk(1);
+    f32x16 s1v = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s1v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f[ks], qf[ks], s1v, 0, 0, 0);
     half_step(s0v, pa0, pa1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // one MFMA of the second chain
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);   // five VALU ops of the softmax
+    }
     if (masked) mask(s1v, 1);
     pv(0, pa0, pa1);
     half_step(s1v, pb0, pb1);
