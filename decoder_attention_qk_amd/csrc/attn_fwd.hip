@@ -343,21 +343,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       p1 = __builtin_bit_cast(bf16x8, hi);
       return tsum;
     };
-    auto pv = [&](int half, const bf16x8 &p0, const bf16x8 &p1) __attribute__((always_inline)) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int r0 = (half * 32 + 16 * kk) * RB;
-          const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0));
-          const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0 + 8 * RB));
-          const bf16x8 vf = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, kk ? p1 : p0, oacc[dt], 0, 0, 0);
-        }
-      }
-    };
 
     // One half: probabilities against the current reference; the half is
     // kept when every lane's partial sum is at most kSumLimit (so no
@@ -424,9 +409,34 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);   // five VALU ops of the softmax
     }
     if (masked) mask(s1v, 1);
-    pv(0, pa0, pa1);
+    // PV of the first half, with the second half's V fragments read beside
+    // it (two transposed reads per MFMA), so the last chain starts at once
+    bf16x8 v1f[2][DT];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int r0 = (16 * kk) * RB;
+        const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0));
+        const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0 + 8 * RB));
+        const bf16x8 vf = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, kk ? pa1 : pa0, oacc[dt], 0, 0, 0);
+        const int r1 = (32 + 16 * kk) * RB;
+        const bf16x4 wlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r1));
+        const bf16x4 whi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r1 + 8 * RB));
+        v1f[kk][dt] = __builtin_shufflevector(wlo, whi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
     half_step(s1v, pb0, pb1);
-    pv(1, pb0, pb1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1f[kk][dt], kk ? pb1 : pb0, oacc[dt], 0, 0, 0);
   };
 
   const int lo = W > 0 && !bidir ? max(0, q0 - W + 1) : 0;
