@@ -220,28 +220,37 @@ NOMINAL_CLOCK_MHZ = 2400.0     # the clock the 2.5 PFLOP/s dense bf16 peak is qu
 
 
 def clock_under_load(b: Bench, seconds: float = 0.6):
-    """Median shader clock (MHz) while the step repeats, read by polling
-    `rocm-smi --showclocks` from a child process; None where the tool is
-    missing or reports nothing.  Runs after the timed steps, so the timed
-    region carries no polling."""
+    """Median shader clock (MHz) while the step repeats, read from the
+    driver's sysfs clock table (the line marked as current in
+    pp_dpm_sclk, the value rocm-smi reports) by a thread of this process;
+    None where the table is missing.  Runs after the timed steps, so the
+    timed region carries no polling."""
+    import glob
     import re
-    import shutil
-    import subprocess
     import threading
-    exe = shutil.which("rocm-smi")
-    if exe is None:
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not paths:
         return None
+
+    def current(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*Mhz", line)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
     vals, stop = [], threading.Event()
 
     def poll():
         while not stop.is_set():
-            try:
-                r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=10)
-            except (OSError, subprocess.SubprocessError):
-                return
-            m = re.search(r'"sclk clock speed:":\s*"\((\d+)Mhz\)"', r.stdout)
-            if m:
-                vals.append(int(m.group(1)))
+            v = current(paths[0])
+            if v:
+                vals.append(v)
+            stop.wait(0.02)
 
     th = threading.Thread(target=poll, daemon=True)
     th.start()
@@ -250,7 +259,7 @@ def clock_under_load(b: Bench, seconds: float = 0.6):
         b.step()
         b.torch.cuda.synchronize()
     stop.set()
-    th.join(timeout=15)
+    th.join(timeout=5)
     return float(np.median(vals)) if vals else None
 
 

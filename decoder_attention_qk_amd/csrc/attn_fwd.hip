@@ -399,13 +399,26 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
     if (masked) mask(s0v, 0);
+    // the first 16 keys' V fragments of the first half are read beside the
+    // second QK^T chain
+    bf16x8 v0f[DT];
     f32x16 s1v = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s1v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f[ks], qf[ks], s1v, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      s1v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f[ks], qf[ks], s1v, 0, 0, 0);
+      if (ks < DT) {
+        const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[ks]));
+        const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[ks] + 8 * RB));
+        v0f[ks] = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
     half_step(s0v, pa0, pa1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // one MFMA of the second chain
+      if (ks < DT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);   // two transposed V reads
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);   // five VALU ops of the softmax
     }
     if (masked) mask(s1v, 1);
@@ -416,12 +429,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(AttnArgs a) {
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int r0 = (16 * kk) * RB;
-        const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0));
-        const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0 + 8 * RB));
-        const bf16x8 vf = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 vf;
+        if (kk == 0) {
+          vf = v0f[dt];
+        } else {
+          const int r0 = (16 * kk) * RB;
+          const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0));
+          const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4 *)(Vt + va[dt] + r0 + 8 * RB));
+          vf = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, kk ? pa1 : pa0, oacc[dt], 0, 0, 0);
         const int r1 = (32 + 16 * kk) * RB;
         const bf16x4 wlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
