@@ -219,18 +219,36 @@ def time_steps(b: Bench, steps: int, warmup: int) -> dict:
 NOMINAL_CLOCK_MHZ = 2400.0     # the clock the 2.5 PFLOP/s dense bf16 peak is quoted at
 
 
-def clock_under_load(b: Bench, seconds: float = 0.6):
-    """Median shader clock (MHz) while the step repeats, read from the
-    driver's sysfs clock table (the line marked as current in
-    pp_dpm_sclk, the value rocm-smi reports) by a thread of this process;
-    None where the table is missing.  Runs after the timed steps, so the
-    timed region carries no polling."""
+def sclk_table_path(torch, dev):
+    """The sysfs shader-clock table of the device in use: found by its PCI
+    address; else the only such table on the host; else None (several
+    tables and no address to tell them apart)."""
     import glob
+    try:
+        pr = torch.cuda.get_device_properties(dev)
+        addr = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+        path = f"/sys/bus/pci/devices/{addr}/pp_dpm_sclk"
+        if os.path.exists(path):
+            return path
+    except (AttributeError, RuntimeError, TypeError, ValueError):
+        pass
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    return paths[0] if len(paths) == 1 else None
+
+
+def clock_under_load(b: Bench, seconds: float = 0.6):
+    """Median shader clock (MHz) of the device in use while the step repeats,
+    read from the driver's sysfs clock table (the line marked as current in
+    pp_dpm_sclk, the value rocm-smi reports) by a thread of this process;
+    None where the table is missing or cannot be told apart from other
+    devices'.  Runs after the timed steps, so the timed region carries no
+    polling."""
     import re
     import threading
-    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
-    if not paths:
+    path = sclk_table_path(b.torch, b.dev)
+    if path is None:
         return None
+    paths = [path]
 
     def current(path):
         try:

@@ -1,6 +1,6 @@
 """Host-side logic of bench.py (no GPU): the one-GPU guard, the causal-
 adjusted FLOP count against a brute-force count of visible pairs, and the
-traffic record's source digest."""
+traffic record's source digest, and which sysfs clock table is read."""
 
 import json
 import os
@@ -52,3 +52,35 @@ def test_traffic_record_is_ignored_when_the_kernel_sources_change(tmp_path, monk
     assert bench.measured_traffic("x", 1) == 120
     monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 16)
     assert bench.measured_traffic("x", 1) is None
+
+
+class _Props:
+    pci_domain_id, pci_bus_id, pci_device_id = 0, 0x1c, 0
+
+
+def _fake_torch(props):
+    class _Cuda:
+        @staticmethod
+        def get_device_properties(dev):
+            if props is None:
+                raise RuntimeError("no device")
+            return props
+
+    class _Torch:
+        cuda = _Cuda
+    return _Torch
+
+
+def test_clock_table_is_the_device_s_own(monkeypatch):
+    """The clock table is found by the device's PCI address; without one, only
+    a single table on the host is taken (several would be ambiguous)."""
+    own = "/sys/bus/pci/devices/0000:1c:00.0/pp_dpm_sclk"
+    monkeypatch.setattr(bench.os.path, "exists", lambda p: p == own)
+    assert bench.sclk_table_path(_fake_torch(_Props), 0) == own
+    import glob
+    monkeypatch.setattr(bench.os.path, "exists", lambda p: False)
+    monkeypatch.setattr(glob, "glob", lambda pat: ["/sys/class/drm/card1/device/pp_dpm_sclk",
+                                                   "/sys/class/drm/card0/device/pp_dpm_sclk"])
+    assert bench.sclk_table_path(_fake_torch(None), 0) is None
+    monkeypatch.setattr(glob, "glob", lambda pat: ["/sys/class/drm/card0/device/pp_dpm_sclk"])
+    assert bench.sclk_table_path(_fake_torch(None), 0) == "/sys/class/drm/card0/device/pp_dpm_sclk"
