@@ -28,8 +28,9 @@
 //   layout and dO^T, Q^T read transposed from LDS.
 //
 // At D = 128 dK/dV runs as attn_bwd_dkdv_rs_kernel below: the
-// same steps split between two waves per SIMD, one forming S, P and dV, the
-// other dP, dS and dK, with P handed over through LDS.
+// same steps split between two waves per SIMD, one forming S, P and dV (and
+// issuing the tile DMA), the other dP, dS and dK, with P handed over through
+// LDS.
 //
 // Tiles are read both row-wise and transposed, so their 16-byte chunks use
 // the swizzle that keeps both patterns free of bank conflicts (Tile::swz_kv).
@@ -731,8 +732,40 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
   ad.init(lane);
   lds_char *pbase = (lds_char *)lds_p[c][0];
 
+  const int64_t q_stride = (int64_t)a.hq * D;
+  int off[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int slot = (c * DMA_PER_WAVE + i) * 64 + lane;
+    const int row = slot / T::CHUNKS;
+    const int pch = slot % T::CHUNKS;
+    off[i] = (row * (int)q_stride + (pch ^ T::swz_kv(row)) * 8) * 2;
+  }
+  // the step's Q and dO tiles, and (waves 0, 1) its LSE and delta rows; rows
+  // past the segment read as 0
+  auto issue_dma = [&](int it, auto S) __attribute__((always_inline)) {
+    int h;
+    const int t0 = step_tile(it, h) * BN;
+    const int rows = min(L - t0, BN);
+    const int64_t r0 = (int64_t)(s0 + t0) * a.hq + h;
+    const int valid_bytes = ((rows - 1) * (int)q_stride + D) * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + r0 * D, valid_bytes);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(a.d_o + r0 * D, valid_bytes);
+    lds_char *qdst = qst(S) + c * DMA_PER_WAVE * 1024;
+    lds_char *odst = ost(S) + c * DMA_PER_WAVE * 1024;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      dma16(qr, off[i], qdst + i * 1024);
+      dma16(orr, off[i], odst + i * 1024);
+    }
+    if (c < 2) {
+      const int fbytes = ((rows - 1) * a.hq + 1) * 4;
+      const __amdgpu_buffer_rsrc_t fr = make_rsrc((c ? a.delta : a.lse) + r0, fbytes);
+      dma4(fr, lane * a.hq * 4, (lds_char *)(c ? dst_(S) : lst(S)));
+    }
+  };
   if (role_a) {
-    // ============ wave A: S, P, dV ============
+    // ============ wave A: DMA; S, P, dV ============
     bf16x8 kf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -743,9 +776,14 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
     f32x16 (&dvacc)[DT] = dvv[0];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dvacc[dt] = f32x16{};
+    if (nsteps > 0) issue_dma(0, ic<0>{});
     vmem_wait_all();
     lds_barrier();   // the first step's stage has landed
     auto phase = [&](int u, auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;   // u % NSTAGE
+      // step u + 1 into the stage step u - 2 left (A read it in phase u - 2,
+      // B in phase u - 1).  A issues the DMA: B's phase is the longer one
+      if (u + 1 < nsteps) issue_dma(u + 1, ic<j + 1>{});
       if (u < nsteps) {
         int h;
         const int t0 = step_tile(u, h) * BN;
@@ -800,6 +838,7 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
           tr_times<D>(Ot, ad, 32, b0, b1, dvacc);
         }
       }
+      vmem_wait_all();   // step u + 1 has landed before the phase that reads it
       lds_barrier();
     };
     for (int r = 0;; r += 3) {
@@ -821,58 +860,22 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
     return;
   }
 
-  // ============ wave B: DMA; dP, dS, dK ============
+  // ============ wave B: dP, dS, dK ============
   bf16x8 vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const uint4 rv = *reinterpret_cast<const uint4 *>(a.v + krow + ks * 16 + g * 8);
     vf[ks] = __builtin_bit_cast(bf16x8, kin ? rv : make_uint4(0, 0, 0, 0));
   }
-  const int64_t q_stride = (int64_t)a.hq * D;
-  int off[DMA_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int slot = (c * DMA_PER_WAVE + i) * 64 + lane;
-    const int row = slot / T::CHUNKS;
-    const int pch = slot % T::CHUNKS;
-    off[i] = (row * (int)q_stride + (pch ^ T::swz_kv(row)) * 8) * 2;
-  }
-  // the step's Q and dO tiles, and (waves 4, 5) its LSE and delta rows; rows
-  // past the segment read as 0
-  auto issue_dma = [&](int it, auto S) __attribute__((always_inline)) {
-    int h;
-    const int t0 = step_tile(it, h) * BN;
-    const int rows = min(L - t0, BN);
-    const int64_t r0 = (int64_t)(s0 + t0) * a.hq + h;
-    const int valid_bytes = ((rows - 1) * (int)q_stride + D) * 2;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + r0 * D, valid_bytes);
-    const __amdgpu_buffer_rsrc_t orr = make_rsrc(a.d_o + r0 * D, valid_bytes);
-    lds_char *qdst = qst(S) + c * DMA_PER_WAVE * 1024;
-    lds_char *odst = ost(S) + c * DMA_PER_WAVE * 1024;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      dma16(qr, off[i], qdst + i * 1024);
-      dma16(orr, off[i], odst + i * 1024);
-    }
-    if (c < 2) {
-      const int fbytes = ((rows - 1) * a.hq + 1) * 4;
-      const __amdgpu_buffer_rsrc_t fr = make_rsrc((c ? a.delta : a.lse) + r0, fbytes);
-      dma4(fr, lane * a.hq * 4, (lds_char *)(c ? dst_(S) : lst(S)));
-    }
-  };
   f32x16 dkv1[1][DT];
   f32x16 (&dkacc)[DT] = dkv1[0];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dkacc[dt] = f32x16{};
 
-  if (nsteps > 0) issue_dma(0, ic<0>{});
   vmem_wait_all();
   lds_barrier();
   auto bphase = [&](int u, auto J) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;   // u % NSTAGE
-    // step u + 1 into the stage step u - 2 left (A read it in phase u - 2,
-    // B in phase u - 1)
-    if (u + 1 < nsteps) issue_dma(u + 1, ic<j + 1>{});
     if (u >= 1) {
       int h;
       const int t0 = step_tile(u - 1, h) * BN;
@@ -908,7 +911,6 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
         tr_times<D>(Qt, ad, 32, b0, b1, dkacc);
       }
     }
-    vmem_wait_all();   // step u + 1 has landed before the phase that reads it
     lds_barrier();
   };
   for (int r = 0;; r += 3) {
