@@ -602,11 +602,6 @@ using ic = std::integral_constant<int, J>;
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
 }
-__device__ __forceinline__ void unpack_f16x2(uint32_t w, float &a, float &b) {
-  const f16x2 h = __builtin_bit_cast(f16x2, w);
-  a = (float)h[0];
-  b = (float)h[1];
-}
 // Workgroup barrier over LDS traffic only (the DMA of a stage is waited for
 // explicitly by the waves that issue it, before the barrier that precedes
 // its first reader).
@@ -888,17 +883,27 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
         auto dscores = [&](const f32x16 &dp, int half, bf16x8 &d0, bf16x8 &d1) __attribute__((always_inline)) {
           const u32x4 h0 = *(const __attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + lane * 16);
           const u32x4 h1 = *(const __attribute__((address_space(3))) u32x4 *)(slot + half * PHALF + 1024 + lane * 16);
-          float p[16], ds[16];
+          // dS = P (dP - delta) as fma(P, dP - delta, +0), so the fp16 P
+          // enters a mixed-precision fma as it is (v_fma_mix_f32: no
+          // conversion); the result equals the product except that an exact
+          // -0 becomes +0
+          _Float16 ph[16];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            unpack_f16x2(h0[i], p[2 * i], p[2 * i + 1]);
-            unpack_f16x2(h1[i], p[8 + 2 * i], p[8 + 2 * i + 1]);
+            const f16x2 lo = __builtin_bit_cast(f16x2, (uint32_t)h0[i]);
+            const f16x2 hi = __builtin_bit_cast(f16x2, (uint32_t)h1[i]);
+            ph[2 * i] = lo[0];
+            ph[2 * i + 1] = lo[1];
+            ph[8 + 2 * i] = hi[0];
+            ph[8 + 2 * i + 1] = hi[1];
           }
+          float ds[16];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(Dl + half * 32 + 8 * jj + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ds[4 * jj + e] = p[4 * jj + e] * (dp[4 * jj + e] - d4[e]);
+            for (int e = 0; e < 4; ++e)
+              ds[4 * jj + e] = __builtin_fmaf((float)ph[4 * jj + e], dp[4 * jj + e] - d4[e], 0.0f);
           }
           pack16(ds, d0, d1);
         };
