@@ -775,10 +775,10 @@ __global__ __launch_bounds__(64 * rs::NWAVES, 1) void attn_bwd_dkdv_rs_kernel(At
     vmem_wait_all();
     lds_barrier();   // the first step's stage has landed
     auto phase = [&](int u, auto J) __attribute__((always_inline)) {
-      constexpr int j = decltype(J)::value;   // u % NSTAGE
+      constexpr int js = decltype(J)::value;   // u % NSTAGE
       // step u + 1 into the stage step u - 2 left (A read it in phase u - 2,
       // B in phase u - 1).  A issues the DMA: B's phase is the longer one
-      if (u + 1 < nsteps) issue_dma(u + 1, ic<j + 1>{});
+      if (u + 1 < nsteps) issue_dma(u + 1, ic<js + 1>{});
       if (u < nsteps) {
         int h;
         const int t0 = step_tile(u, h) * BN;
