@@ -236,6 +236,17 @@ def sclk_table_path(torch, dev):
     return paths[0] if len(paths) == 1 else None
 
 
+def current_sclk_mhz(text: str):
+    """The current shader clock (MHz) in the text of a pp_dpm_sclk table: the
+    level line marked with '*' (e.g. "1: 1844Mhz *"); None if no line is."""
+    import re
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+            return int(m.group(1)) if m else None
+    return None
+
+
 def clock_under_load(b: Bench, seconds: float = 0.6):
     """Median shader clock (MHz) of the device in use while the step repeats,
     read from the driver's sysfs clock table (the line marked as current in
@@ -243,29 +254,23 @@ def clock_under_load(b: Bench, seconds: float = 0.6):
     None where the table is missing or cannot be told apart from other
     devices'.  Runs after the timed steps, so the timed region carries no
     polling."""
-    import re
     import threading
     path = sclk_table_path(b.torch, b.dev)
     if path is None:
         return None
-    paths = [path]
 
-    def current(path):
+    def current():
         try:
             with open(path) as f:
-                for line in f:
-                    if line.rstrip().endswith("*"):
-                        m = re.search(r"(\d+)\s*Mhz", line)
-                        return int(m.group(1)) if m else None
+                return current_sclk_mhz(f.read())
         except OSError:
             return None
-        return None
 
     vals, stop = [], threading.Event()
 
     def poll():
         while not stop.is_set():
-            v = current(paths[0])
+            v = current()
             if v:
                 vals.append(v)
             stop.wait(0.02)

@@ -84,3 +84,11 @@ def test_clock_table_is_the_device_s_own(monkeypatch):
     assert bench.sclk_table_path(_fake_torch(None), 0) is None
     monkeypatch.setattr(glob, "glob", lambda pat: ["/sys/class/drm/card0/device/pp_dpm_sclk"])
     assert bench.sclk_table_path(_fake_torch(None), 0) == "/sys/class/drm/card0/device/pp_dpm_sclk"
+
+
+def test_current_clock_is_the_marked_level():
+    table = "0: 500Mhz \n1: 1200Mhz \n2: 1844Mhz *\n3: 2400Mhz \n"
+    assert bench.current_sclk_mhz(table) == 1844
+    assert bench.current_sclk_mhz("0: 500Mhz *\n1: 2400Mhz\n") == 500
+    assert bench.current_sclk_mhz("0: 500Mhz\n1: 2400Mhz\n") is None
+    assert bench.current_sclk_mhz("") is None
